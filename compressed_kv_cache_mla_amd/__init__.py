@@ -1,0 +1,151 @@
+"""MI355X (gfx950) MLA decode over the compressed latent KV cache.
+
+A thin ctypes binding over libmla.so (the C ABI in include/mla.h): it only
+marshals arguments -- torch tensors' device pointers, sizes and the current
+HIP stream.  Every step of the path (cache append, query absorption, split-KV
+decode, combine, W^UV epilogue) runs in the library's HIP kernels.
+
+Importing this package does not touch the GPU.  Loading fails loudly if
+libmla.so has not been built (python -m compressed_kv_cache_mla_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
+MLA_BF16, MLA_FP32 = 0, 1
+FLAG_BAD_SEQ_LEN, FLAG_BAD_PAGE, FLAG_BAD_POSITION, FLAG_BAD_SEQ_ID = 1, 2, 4, 8
+
+EXPORTED = ("mla_cache_append", "mla_decode_workspace_size", "mla_decode", "mla_read_error_flags",
+            "mla_last_error", "mla_device_cu_count")
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"mla status {status}: {msg}")
+        self.status = status
+
+
+class mla_dims(ctypes.Structure):
+    _fields_ = [("n_h", ctypes.c_int32), ("d_h", ctypes.c_int32), ("d_c", ctypes.c_int32),
+                ("d_hR", ctypes.c_int32), ("d_model", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Dims:
+    """MLA sizes in the pages' notation (DeepSeek-V2: n_h = 128, d_h = 128,
+    d_c = 512, d_h^R = 64, d_model = 5120)."""
+    n_h: int = 128
+    d_h: int = 128
+    d_c: int = 512
+    d_hR: int = 64
+    d_model: int = 5120
+    page_size: int = 64
+    rope_base: float = 10000.0
+    dtype: torch.dtype = torch.bfloat16
+    softmax_scale: float | None = None
+
+    @property
+    def scale(self) -> float:
+        return self.softmax_scale if self.softmax_scale is not None else 1.0 / (self.d_h + self.d_hR) ** 0.5
+
+    def c(self) -> mla_dims:
+        if self.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("dtype must be torch.bfloat16 or torch.float32")
+        return mla_dims(self.n_h, self.d_h, self.d_c, self.d_hR, self.d_model, self.page_size, self.scale,
+                        self.rope_base, MLA_BF16 if self.dtype == torch.bfloat16 else MLA_FP32)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with python -m compressed_kv_cache_mla_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        pdims = ctypes.POINTER(mla_dims)
+        L.mla_cache_append.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, i64, i32, vp, vp]
+        L.mla_cache_append.restype = ctypes.c_int
+        L.mla_decode_workspace_size.argtypes = [pdims, i32, i32]
+        L.mla_decode_workspace_size.restype = sz
+        L.mla_decode.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32, vp, vp, vp, vp, sz,
+                                 i32, vp]
+        L.mla_decode.restype = ctypes.c_int
+        L.mla_read_error_flags.argtypes = [vp, ctypes.POINTER(i32), vp]
+        L.mla_read_error_flags.restype = ctypes.c_int
+        L.mla_last_error.argtypes = []
+        L.mla_last_error.restype = ctypes.c_char_p
+        L.mla_device_cu_count.argtypes = []
+        L.mla_device_cu_count.restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != MLA_OK:
+        raise MlaError(status, lib().mla_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def cu_count() -> int:
+    return int(lib().mla_device_cu_count())
+
+
+def cache_append(dims: Dims, h_t, W_DKV, W_KR, pos, page_table, c_KV, k_R, row_stride: int, num_pages: int,
+                 seq_id=None, err_flag=None, stream=None):
+    """mla_cache_append: write c^KV = W^DKV h_t and k^R = RoPE(W^KR h_t) of T
+    token rows into the paged pool (see include/mla.h)."""
+    T = h_t.shape[0]
+    num_seqs, max_pages = page_table.shape
+    d = dims.c()
+    _check(lib().mla_cache_append(ctypes.byref(d), T, _ptr(h_t), _ptr(W_DKV), _ptr(W_KR), _ptr(seq_id), _ptr(pos),
+                                  _ptr(page_table), num_seqs, max_pages, _ptr(c_KV), _ptr(k_R), row_stride,
+                                  num_pages, _ptr(err_flag), _stream(stream)))
+
+
+def decode_workspace_size(dims: Dims, B: int, n_splits: int = 0) -> int:
+    d = dims.c()
+    return int(lib().mla_decode_workspace_size(ctypes.byref(d), B, n_splits))
+
+
+def decode(dims: Dims, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride: int, num_pages: int, page_table,
+           seq_lens, out, lse=None, workspace=None, n_splits: int = 0, stream=None):
+    """mla_decode: one query per sequence against its cached latent rows;
+    writes out [B, n_h, d_h] (fp32) and optionally lse [B, n_h]."""
+    B = q_C.shape[0]
+    max_pages = page_table.shape[1]
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_size(dims, B, n_splits), dtype=torch.uint8, device=q_C.device)
+    d = dims.c()
+    _check(lib().mla_decode(ctypes.byref(d), B, _ptr(q_C), _ptr(q_R), _ptr(pos_q), _ptr(W_UK), _ptr(W_UV),
+                            _ptr(c_KV), _ptr(k_R), row_stride, num_pages, _ptr(page_table), max_pages,
+                            _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), n_splits,
+                            _stream(stream)))
+    return workspace
+
+
+def read_error_flags(workspace_or_flag, stream=None) -> int:
+    """Device error flags (FLAG_* bits) of a decode workspace or append flag word; clears them."""
+    v = ctypes.c_int32(0)
+    _check(lib().mla_read_error_flags(_ptr(workspace_or_flag), ctypes.byref(v), _stream(stream)))
+    return int(v.value)

@@ -1,0 +1,121 @@
+// Shared device/host definitions of the gfx950 MLA kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+namespace mla {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// Fixed MLA widths the kernels are built for (DeepSeek-V2).
+constexpr int D_C = 512;          // latent c^KV
+constexpr int D_R = 64;           // decoupled RoPE key k^R
+constexpr int D_K = D_C + D_R;    // 576: one cached row
+constexpr int D_H = 128;          // per-head q^C / v width
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// Row index of token t of sequence b in the paged pool; out-of-range page ids
+// are clamped into the pool and reported through *flags.
+__device__ __forceinline__ int64_t pool_row(const int32_t* __restrict__ page_table, int32_t max_pages,
+                                            int32_t num_pages, int32_t page_size, int32_t b, int32_t t,
+                                            int32_t* flags) {
+  int32_t pg = page_table[(int64_t)b * max_pages + t / page_size];
+  if (pg < 0 || pg >= num_pages) {
+    if (flags) atomicOr(flags, MLA_FLAG_BAD_PAGE);
+    pg = pg < 0 ? 0 : num_pages - 1;
+  }
+  return (int64_t)pg * page_size + t % page_size;
+}
+
+// RoPE angle of pair k at position pos: pos * base^(-2k/d), in fp64.
+__device__ __forceinline__ void rope_cos_sin(int32_t pos, int k, int d, float base, float* c, float* s) {
+  double theta = pow((double)base, -2.0 * (double)k / (double)d);
+  double a = (double)pos * theta;
+  double sn, cs;
+  sincos(a, &sn, &cs);
+  *c = (float)cs;
+  *s = (float)sn;
+}
+
+// Decode workspace layout (bytes, each part 256-aligned).
+struct DecodeWs {
+  size_t flags, prefix, qabs, part_ml, part_o, total;
+  int32_t n_slots;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline DecodeWs decode_ws_layout(int32_t B, int32_t n_h, int32_t n_splits, int elt) {
+  DecodeWs w;
+  w.n_slots = n_splits + B;
+  size_t off = 0;
+  w.flags = off;   off += 256;
+  w.prefix = off;  off += align256((size_t)(B + 1) * 4);
+  w.qabs = off;    off += align256((size_t)B * n_h * D_K * elt);
+  w.part_ml = off; off += align256((size_t)w.n_slots * n_h * 2 * 4);
+  w.part_o = off;  off += align256((size_t)w.n_slots * n_h * D_C * 4);
+  w.total = off;
+  return w;
+}
+
+// Work partition: the batch's N cached tokens, laid end to end, are cut into
+// n_splits near-equal ranges [P_w, P_w+1), P_w = floor(w*N/n_splits).  Range w
+// and sequence b overlap in at most one segment, whose partial result lives in
+// slot w + b (distinct for every overlapping pair, and contiguous in w for a
+// fixed b).
+__device__ __forceinline__ int64_t split_begin(int64_t w, int64_t N, int64_t G) { return (w * N) / G; }
+// Split holding global token x (0 <= x < N).
+__device__ __forceinline__ int64_t split_of(int64_t x, int64_t N, int64_t G) {
+  return ((x + 1) * G + N - 1) / N - 1;
+}
+// Last b in [0, B) with prefix[b] <= x.
+__device__ __forceinline__ int32_t seq_of(const int32_t* __restrict__ prefix, int32_t B, int64_t x) {
+  int32_t lo = 0, hi = B - 1;
+  while (lo < hi) {
+    int32_t mid = (lo + hi + 1) >> 1;
+    if ((int64_t)prefix[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace mla
+
+// Launchers (host side), one per kernel family.
+namespace mla {
+hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void* W_DKV, const void* W_KR,
+                         const int32_t* seq_id, const int32_t* pos, const int32_t* page_table,
+                         int32_t num_seqs, int32_t max_pages, void* c_KV, void* k_R, int64_t row_stride,
+                         int32_t num_pages, int32_t* err_flag, hipStream_t s);
+hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_tokens, int32_t* prefix, int32_t* flags,
+                       hipStream_t s);
+hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
+                         const void* W_UK, void* qabs, hipStream_t s);
+hipError_t launch_decode_simple(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
+                                const void* k_R, int64_t row_stride, int32_t num_pages,
+                                const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
+                                int32_t n_splits, float* part_ml, float* part_o, int32_t* flags,
+                                hipStream_t s);
+hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
+                              const void* k_R, int64_t row_stride, int32_t num_pages,
+                              const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
+                              int32_t n_splits, float* part_ml, float* part_o, int32_t* flags,
+                              hipStream_t s);
+hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, int32_t n_splits,
+                          const float* part_ml, const float* part_o, const void* W_UV, float* out,
+                          float* lse, hipStream_t s);
+}  // namespace mla

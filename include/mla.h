@@ -1,0 +1,165 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) Multi-head Latent Attention decode
+ * library (libmla.so).
+ *
+ * What is computed (DeepSeek-V2 MLA, notation of the pages):
+ *   "DeepSeek-V2：在“大力出奇迹”的AI军备竞赛中，四两拨千斤" (liang.world), ch.2
+ *   "侠客甲——MLA": §2 low-rank joint KV compression (c_t^KV = W^DKV h_t,
+ *   k_t^C = W^UK c_t^KV, v_t^C = W^UV c_t^KV; W^UK and W^UV absorbed into the
+ *   query and output sides), §3 decoupled RoPE (q_{t,i} = [q^C_{t,i}; q^R_{t,i}],
+ *   k_{t,i} = [k^C_{t,i}; k^R_t], one k^R shared by all heads); and
+ *   "DeepSeek 系列模型技术深度解读" (tuntang.top), MLA section, "RoPE 的兼容性处理"
+ *   (k^R_t = RoPE(W^KR h_t)).  Each cached token stores only c^KV (d_c) and k^R
+ *   (d_h^R): "Must also cache k_rope" -- pptc.cn DeepSeek note, §6 pitfall 2.
+ *
+ * Conventions fixed here where the pages are silent:
+ *   - RoPE rotates adjacent pairs (x[2k], x[2k+1]) by pos * rope_base^(-2k/d_hR);
+ *     angles are formed in fp64, the rotation is done in fp32.
+ *   - Scores are (q^C . k^C + q^R . k^R) * softmax_scale (normally
+ *     1/sqrt(d_h + d_hR)); softmax over every cached token of the sequence.
+ *   - Weights are [out, in] row-major: W^DKV [d_c, d_model], W^KR [d_hR, d_model],
+ *     W^UK and W^UV [n_h*d_h, d_c]; head i owns rows i*d_h .. i*d_h+d_h-1.
+ *   - The output is each head's o_i = W^UV_i O~_i (fp32); W_O is not applied.
+ *
+ * Latent cache (paged pool, owned by the caller):
+ *   A pool row r holds one token: c^KV at c_KV + r*row_stride (d_c elements)
+ *   and k^R at k_R + r*row_stride (d_hR elements, already rotated).  The
+ *   interleaved layout k_R = c_KV + d_c, row_stride = d_c + d_hR (576) is the
+ *   default; separate pools sharing one stride also work.  Token t of sequence
+ *   b lives in row page_table[b*max_pages + t/page_size]*page_size + t%page_size.
+ *   Rows are 16-byte aligned (row_stride * element size % 16 == 0).
+ *
+ * Element type: dims.dtype selects bf16 (MLA_BF16: h, weights, q, cache in
+ * bf16; fp32 accumulation) or fp32 (MLA_FP32: everything fp32).  Outputs of
+ * mla_decode are fp32 in both cases.
+ *
+ * Ownership and ordering: every pointer is caller-owned device memory (HBM)
+ * unless stated.  Calls enqueue kernels on `stream` (a hipStream_t, or NULL
+ * for the default stream) and return after the launch; results are ready when
+ * the stream reaches that point.  The library allocates no device memory: the
+ * decode scratch is the caller's workspace.  Calls are reentrant; the only
+ * state is the thread-local message behind mla_last_error().
+ *
+ * Errors: host-side checks (null or misaligned pointers, unsupported dims,
+ * bad sizes, small workspace) return a status without launching anything.
+ * Values that live on the device (positions, sequence lengths, page ids) are
+ * checked by the kernels: an out-of-range value is clamped so that no access
+ * leaves its buffer, and a flag is raised in the workspace (decode) or in the
+ * optional err_flag word (append), readable with mla_read_error_flags().
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, bad size or count */
+  MLA_ERR_UNSUPPORTED = 2,  /* dims the kernels are not built for */
+  MLA_ERR_WORKSPACE = 3,    /* workspace smaller than mla_decode_workspace_size() */
+  MLA_ERR_HIP = 4           /* a HIP runtime / launch error */
+} mla_status;
+
+typedef enum mla_dtype { MLA_BF16 = 0, MLA_FP32 = 1 } mla_dtype;
+
+/* Device-side error flags (bit mask) raised by the kernels. */
+enum {
+  MLA_FLAG_BAD_SEQ_LEN = 1,   /* seq_len < 1 or > max_pages*page_size (clamped) */
+  MLA_FLAG_BAD_PAGE = 2,      /* page id outside [0, num_pages) (clamped) */
+  MLA_FLAG_BAD_POSITION = 4,  /* append position outside [0, max_pages*page_size) (row skipped) */
+  MLA_FLAG_BAD_SEQ_ID = 8     /* append sequence id outside [0, num_seqs) (row skipped) */
+};
+
+typedef struct mla_dims {
+  int32_t n_h;        /* attention heads (DeepSeek-V2: 128) */
+  int32_t d_h;        /* per-head q^C / k^C / v^C width (must be 128) */
+  int32_t d_c;        /* latent width of c^KV (must be 512) */
+  int32_t d_hR;       /* decoupled RoPE width of q^R / k^R (must be 64) */
+  int32_t d_model;    /* width of h_t (multiple of 64) */
+  int32_t page_size;  /* tokens per cache page (>= 1) */
+  float softmax_scale;
+  float rope_base;
+  int32_t dtype;      /* mla_dtype */
+} mla_dims;
+
+/*
+ * mla_cache_append -- write T new tokens into the latent cache.
+ * For each token row t: c^KV = W^DKV h_t and k^R = RoPE(W^KR h_t, pos[t])
+ * (liang.world ch.2 §2 eq. for c_t^KV; tuntang.top MLA section, k_t formula),
+ * rounded to the cache type and stored at position pos[t] of sequence
+ * seq_id[t] (the row of page_table), per the paging rule above.
+ *   h_t        [T, d_model]          dtype        device
+ *   W_DKV      [d_c, d_model]        dtype        device
+ *   W_KR       [d_hR, d_model]       dtype        device
+ *   seq_id     [T] int32 or NULL     device       NULL means seq_id[t] = t
+ *   pos        [T] int32             device       0 <= pos < max_pages*page_size
+ *   page_table [num_seqs, max_pages] int32 device entries in [0, num_pages)
+ *   c_KV, k_R  pool base pointers, row_stride elements per row, num_pages pages
+ *   err_flag   int32 device word or NULL; bad ids / positions set MLA_FLAG_* bits
+ * Rows with a bad seq_id / position are skipped; page ids are clamped.
+ */
+mla_status mla_cache_append(const mla_dims* dims, int32_t T, const void* h_t, const void* W_DKV,
+                            const void* W_KR, const int32_t* seq_id, const int32_t* pos,
+                            const int32_t* page_table, int32_t num_seqs, int32_t max_pages,
+                            void* c_KV, void* k_R, int64_t row_stride, int32_t num_pages,
+                            int32_t* err_flag, void* stream);
+
+/*
+ * mla_decode_workspace_size -- bytes of device workspace mla_decode needs for
+ * batch B with n_splits work partitions (0 = the library's default, one per
+ * compute unit).  Returns 0 for invalid dims.
+ */
+size_t mla_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t n_splits);
+
+/*
+ * mla_decode -- one decode query per sequence against its cached tokens.
+ * (liang.world ch.2 §1 per-head softmax attention over earlier tokens; §2
+ * absorption of W^UK into the query side, q~_i = W^UK_i^T q^C_i, and of W^UV
+ * into the output side; §3 score = q^C.k^C + q^R.k^R.)
+ * Steps, all in this library's kernels: plan (split the batch's tokens into
+ * n_splits near-equal ranges), absorb (q~ and RoPE(q^R) at pos_q), split-KV
+ * flash decode over the paged latent (all heads share each staged tile),
+ * cross-split log-sum-exp combine, and the W^UV epilogue.
+ *   q_C        [B, n_h, d_h]   dtype   device
+ *   q_R        [B, n_h, d_hR]  dtype   device, NOT yet rotated
+ *   pos_q      [B] int32       device  query positions (normally seq_lens[b]-1)
+ *   W_UK, W_UV [n_h*d_h, d_c]  dtype   device
+ *   c_KV, k_R, row_stride, num_pages   the pool, as for mla_cache_append
+ *   page_table [B, max_pages]  int32   device
+ *   seq_lens   [B] int32       device  cached tokens per sequence (>= 1; the
+ *                                      query's own token is among them)
+ *   out        [B, n_h, d_h]   fp32    device
+ *   lse        [B, n_h] fp32 or NULL   natural-log softmax normaliser per head
+ *   workspace  ws_bytes >= mla_decode_workspace_size(dims, B, n_splits),
+ *              256-byte aligned device memory; it also holds the error flags.
+ * Results are deterministic for fixed inputs and n_splits (no float atomics).
+ */
+mla_status mla_decode(const mla_dims* dims, int32_t B, const void* q_C, const void* q_R,
+                      const int32_t* pos_q, const void* W_UK, const void* W_UV,
+                      const void* c_KV, const void* k_R, int64_t row_stride, int32_t num_pages,
+                      const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                      float* out, float* lse, void* workspace, size_t ws_bytes, int32_t n_splits,
+                      void* stream);
+
+/*
+ * mla_read_error_flags -- wait for `stream`, then copy the device error flags
+ * of a decode workspace (or an append err_flag word) to *flags and clear them.
+ */
+mla_status mla_read_error_flags(void* workspace_or_flag, int32_t* flags, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* mla_last_error(void);
+
+/* Number of compute units of the current device (default n_splits). */
+int32_t mla_device_cu_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

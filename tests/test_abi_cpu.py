@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI that run without a GPU: the library loads,
+exports every function include/mla.h declares, and rejects bad arguments
+with the documented status before launching anything; plus the work-split
+arithmetic the kernels share (slot = split + sequence)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_kv_cache_mla_amd as mla
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert set(names) >= {"mla_cache_append", "mla_decode", "mla_decode_workspace_size"}
+    L = mla.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(mla.EXPORTED) == set(names)
+
+
+def _dims(**kw):
+    d = dict(n_h=128, d_h=128, d_c=512, d_hR=64, d_model=5120, page_size=64, softmax_scale=192 ** -0.5,
+             rope_base=10000.0, dtype=mla.MLA_BF16)
+    d.update(kw)
+    return mla.mla_dims(**{k: d[k] for k, _ in mla.mla_dims._fields_})
+
+
+def _decode(dims, ws_bytes=1 << 30, ptr=16, B=2, n_splits=8, stride=576):
+    L = mla.lib()
+    p = ctypes.c_void_p(ptr * 4096) if ptr else None
+    return L.mla_decode(ctypes.byref(dims) if dims is not None else None, B, p, p, p, p, p, p, p, stride, 10, p, 4,
+                        p, p, None, ctypes.c_void_p(1 << 20), ws_bytes, n_splits, None)
+
+
+def test_decode_rejects_bad_arguments_before_launching():
+    L = mla.lib()
+    assert _decode(None) == mla.MLA_ERR_INVALID_ARG
+    assert b"dims" in L.mla_last_error()
+    assert _decode(_dims(d_c=256)) == mla.MLA_ERR_UNSUPPORTED
+    assert _decode(_dims(d_hR=32)) == mla.MLA_ERR_UNSUPPORTED
+    assert _decode(_dims(d_h=64)) == mla.MLA_ERR_UNSUPPORTED
+    assert _decode(_dims(d_model=100)) == mla.MLA_ERR_UNSUPPORTED
+    assert _decode(_dims(page_size=0)) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(_dims(dtype=7)) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(_dims(), B=0) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(_dims(), ptr=0) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(_dims(), stride=500) == mla.MLA_ERR_INVALID_ARG     # < 512
+    assert _decode(_dims(), stride=580) == mla.MLA_ERR_INVALID_ARG     # 1160 B rows: not 16-byte multiples
+    assert _decode(_dims(), ws_bytes=100) == mla.MLA_ERR_WORKSPACE
+    assert b"workspace" in L.mla_last_error()
+
+
+def test_decode_rejects_misaligned_pointers():
+    L = mla.lib()
+    p = ctypes.c_void_p(4096 + 8)
+    d = _dims()
+    st = L.mla_decode(ctypes.byref(d), 2, p, p, p, p, p, p, p, 576, 10, p, 4, p, p, None, ctypes.c_void_p(1 << 20),
+                      1 << 30, 8, None)
+    assert st == mla.MLA_ERR_INVALID_ARG
+
+
+def test_append_rejects_bad_arguments():
+    L = mla.lib()
+    d = _dims()
+    p = ctypes.c_void_p(1 << 16)
+    args = [2, p, p, p, None, p, p, 2, 4, p, p, 576, 10, None, None]
+    assert L.mla_cache_append(ctypes.byref(d), -1, *args[1:]) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_cache_append(ctypes.byref(d), 0, *args[1:]) == mla.MLA_OK   # nothing to do
+    bad = list(args)
+    bad[1] = None
+    assert L.mla_cache_append(ctypes.byref(d), *bad) == mla.MLA_ERR_INVALID_ARG
+    bad = list(args)
+    bad[0] = 5           # seq_id NULL with T > num_seqs
+    assert L.mla_cache_append(ctypes.byref(d), *bad) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_cache_append(ctypes.byref(_dims(d_c=128)), *args) == mla.MLA_ERR_UNSUPPORTED
+
+
+def test_workspace_size_grows_with_batch_and_splits():
+    L = mla.lib()
+    d = _dims()
+    a = L.mla_decode_workspace_size(ctypes.byref(d), 64, 256)
+    b = L.mla_decode_workspace_size(ctypes.byref(d), 128, 256)
+    c = L.mla_decode_workspace_size(ctypes.byref(d), 64, 512)
+    assert 0 < a < b and a < c
+    # partials (G + B slots) of n_h x (512 + 2) fp32 dominate
+    assert a >= (256 + 64) * 128 * 514 * 4
+    assert L.mla_decode_workspace_size(ctypes.byref(_dims(d_c=1)), 64, 256) == 0
+
+
+# ---- the split arithmetic the decode and combine kernels share
+def _split_begin(w, N, G):
+    return (w * N) // G
+
+
+def _split_of(x, N, G):
+    return ((x + 1) * G + N - 1) // N - 1
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_split_slots_are_unique_and_contiguous(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    n = rng.integers(0, 300, size=B)
+    G = int(rng.integers(1, 300))
+    prefix = np.r_[0, np.cumsum(n)]
+    N = int(prefix[-1])
+    if N == 0:
+        return
+    for x in range(0, N, max(1, N // 50)):
+        w = _split_of(x, N, G)
+        assert _split_begin(w, N, G) <= x < _split_begin(w + 1, N, G)
+    seen = set()
+    for b in range(B):
+        if n[b] == 0:
+            continue
+        w0, w1 = _split_of(prefix[b], N, G), _split_of(prefix[b + 1] - 1, N, G)
+        ws = [w for w in range(G) if max(prefix[b], _split_begin(w, N, G)) < min(prefix[b + 1],
+                                                                                  _split_begin(w + 1, N, G))]
+        assert ws == list(range(w0, w1 + 1))
+        for w in ws:
+            assert w + b not in seen
+            seen.add(w + b)
+    assert max(seen) < G + B

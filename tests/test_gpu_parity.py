@@ -1,0 +1,173 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerance: max|gpu - oracle| / max|oracle| <= 1e-2 for bf16 and <= 1e-5 for
+fp32, on the decode output and on the cache rows the append kernel writes.
+Full-size configurations are checked on sampled sequences (the oracle runs
+them one by one); small variants cover several tiles, ragged tails, paging,
+split counts and the degenerate cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from cases import gpu_cache_rows, oracle_cache, oracle_decode, projected_queries, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 1e-2, torch.float32: 1e-5}
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _check_decode(wl, seqs, mode="absorbed", heads=None, q=None):
+    wl.decode()
+    torch.cuda.synchronize()
+    out = wl.out.cpu().numpy()
+    lse = wl.lse.cpu().numpy()
+    tol = TOL[wl.cfg.dtype]
+    worst = 0.0
+    for b in seqs:
+        ref, ref_lse = oracle_decode(wl, b, mode, heads, q=None if q is None else (q[0][b], q[1][b]))
+        got = out[b] if heads is None else out[b][list(heads)]
+        got_lse = lse[b] if heads is None else lse[b][list(heads)]
+        e = rel_err(got, ref)
+        worst = max(worst, e)
+        assert e <= tol, f"{wl.cfg.name} seq {b} ({mode}): rel err {e:.3e} > {tol}"
+        assert np.max(np.abs(got_lse - ref_lse)) <= 50 * tol * max(1.0, np.max(np.abs(ref_lse)))
+    return worst
+
+
+def _check_append(wl, seqs, tokens_per_seq=None):
+    tol = TOL[wl.cfg.dtype]
+    for b in seqs:
+        d = wl.oracle_inputs(b)
+        n = d["n"]
+        toks = np.arange(n) if tokens_per_seq is None else np.unique(np.r_[0, n - 1, tokens_per_seq(n)])
+        c, kR = oracle_cache(wl, d)
+        ref = np.concatenate([c, kR], axis=1)[toks]
+        got = gpu_cache_rows(wl, b, toks)
+        e = rel_err(got, ref)
+        assert e <= tol, f"{wl.cfg.name} append seq {b}: rel err {e:.3e} > {tol}"
+
+
+def test_tiny_fp32_end_to_end():
+    cfg = W.CONFIGS["tiny_fp32"]
+    _say(f"case {cfg.name}")
+    wl = W.Workload(cfg)
+    qC, qR = projected_queries(wl)
+    wl.set_queries(qC, qR)
+    q = (qC.double().numpy(), qR.double().numpy())
+    _check_append(wl, [0])
+    for n_splits in (1, 3, 256):
+        wl2 = W.Workload(cfg, n_splits=n_splits) if n_splits != wl.n_splits else wl
+        wl2.set_queries(qC, qR)
+        _check_decode(wl2, [0], "reconstruct", q=q)
+        _check_decode(wl2, [0], "absorbed", q=q)
+
+
+@pytest.mark.parametrize("n_h", [32, 64, 128])
+def test_bf16_small_ragged_paged(n_h):
+    cfg = W.scaled(W.CONFIGS["b64_ragged"], name=f"small_ragged_h{n_h}", n_h=n_h, d_model=512, B=5,
+                   lens=(0, 400), seed=77 + n_h)
+    _say(f"case {cfg.name}")
+    for n_splits in (1, 5, 64):
+        wl = W.Workload(cfg, n_splits=n_splits)
+        _check_decode(wl, range(cfg.B))
+    _check_append(wl, [0, 4])
+    _check_decode(wl, [1], "reconstruct", heads=[0, n_h - 1])
+
+
+def test_bf16_edge_lengths():
+    # n = 1 (query token only), lengths around the 48-row tile and 64-token page
+    lens = [0, 1, 46, 47, 48, 63, 64, 95, 96, 97, 127, 128]
+    cfg = W.scaled(W.CONFIGS["b32_l4096"], name="edge_lengths", d_model=256, B=len(lens), lens=0, seed=91)
+    _say(f"case {cfg.name}")
+    cfg.context_lengths = lambda: np.array(lens)  # noqa: E731
+    for n_splits in (1, 13, 256):
+        wl = W.Workload(cfg, n_splits=n_splits)
+        _check_decode(wl, range(cfg.B))
+
+
+def test_bf16_page_permutation_is_bitwise_invariant():
+    base = W.scaled(W.CONFIGS["b64_ragged"], name="perm", d_model=256, B=6, lens=(100, 900), seed=5)
+    _say("case page permutation")
+    outs = []
+    for perm in (False, True):
+        wl = W.Workload(W.scaled(base, permute_pages=perm), n_splits=37)
+        wl.decode()
+        torch.cuda.synchronize()
+        outs.append((wl.out.clone(), wl.lse.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_bf16_deterministic_and_split_invariant():
+    cfg = W.scaled(W.CONFIGS["b64_ragged"], name="splits", d_model=256, B=4, lens=(500, 3000), seed=6)
+    _say("case determinism / splits")
+    res = {}
+    for n_splits in (1, 2, 8, 256):
+        wl = W.Workload(cfg, n_splits=n_splits)
+        wl.decode()
+        a = wl.out.clone()
+        wl.decode()
+        torch.cuda.synchronize()
+        assert torch.equal(a, wl.out), "same inputs and splits must give bitwise-equal results"
+        res[n_splits] = a.double().cpu().numpy()
+    for k, v in res.items():
+        assert rel_err(v, res[1]) < 2e-3, f"splits {k} vs 1"
+
+
+def test_b32_l4096_full():
+    cfg = W.CONFIGS["b32_l4096"]
+    _say(f"case {cfg.name}")
+    wl = W.Workload(cfg)
+    _check_decode(wl, [0, cfg.B - 1])
+    _check_decode(wl, [0], "reconstruct", heads=[0, 77, 127])
+    _check_append(wl, [0, cfg.B - 1], tokens_per_seq=lambda n: np.arange(0, n, 97))
+
+
+def test_b64_ragged_paged_full():
+    cfg = W.CONFIGS["b64_ragged"]
+    _say(f"case {cfg.name}")
+    wl = W.Workload(cfg)
+    longest = int(np.argmax(wl.n))
+    _check_decode(wl, sorted({0, cfg.B - 1, longest}))
+
+
+def test_b4_l131072_full():
+    cfg = W.CONFIGS["b4_l131072"]
+    _say(f"case {cfg.name}")
+    wl = W.Workload(cfg)
+    _check_decode(wl, [0, 3])
+
+
+@pytest.mark.parametrize("layer", [0, 59])
+def test_l60_b128_l8192_sampled_layers(layer):
+    cfg = W.CONFIGS["l60_b128_l8192"]
+    _say(f"case {cfg.name} layer {layer}")
+    wl = W.Workload(cfg, layer=layer)
+    _check_decode(wl, [0, cfg.B - 1])
+    _check_append(wl, [0], tokens_per_seq=lambda n: np.array([n - 1]))
+
+
+def test_bad_device_values_are_flagged_not_faulting():
+    import compressed_kv_cache_mla_amd as mla
+    cfg = W.scaled(W.CONFIGS["b64_ragged"], name="flags", d_model=256, B=3, lens=(10, 200), seed=8)
+    _say("case device error flags")
+    wl = W.Workload(cfg, n_splits=8)
+    wl.decode()
+    assert mla.read_error_flags(wl.workspace) == 0
+    good = wl.seq_lens.clone()
+    wl.seq_lens[1] = 0
+    wl.decode()
+    assert mla.read_error_flags(wl.workspace) & mla.FLAG_BAD_SEQ_LEN
+    torch.cuda.synchronize()
+    assert torch.all(wl.out[1] == 0) and torch.all(torch.isinf(wl.lse[1]))
+    wl.seq_lens.copy_(good)
+    wl.page_table[0, 0] = wl.num_pages + 5
+    wl.decode()
+    assert mla.read_error_flags(wl.workspace) & mla.FLAG_BAD_PAGE
+    torch.cuda.synchronize()
+    assert torch.isfinite(wl.out).all()

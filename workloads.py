@@ -1,0 +1,231 @@
+"""Synthetic MLA decode workloads shared by the GPU tests and bench.py.
+
+Each workload fixes the shapes of one benchmark configuration (DeepSeek-V2
+attention dims: n_h = 128, d_h = 128, d_c = 512, d_h^R = 64, d_model = 5120),
+builds its inputs on the device from the seeded generator (seeded_inputs), and
+can regenerate, on the CPU and without reading anything back from the GPU,
+the fp64 inputs the oracle needs for any one sequence.
+
+Conventions (the same as the library's and the oracle's):
+* sequence b holds n_b cached tokens at positions 0 .. n_b-1; the decode query
+  is the last of them (position n_b - 1), appended just before decoding;
+* the pool is [num_pages, page_size, 576]: c^KV in columns 0..511, k^R in
+  512..575; sequence b owns ceil(n_b / page_size) pages, assigned either in
+  order or through a seeded random permutation of the whole pool;
+* cache rows come either from the append kernel applied to seeded token
+  states h ~ N(0, 1) ("append" mode) or straight from the generator as
+  N(0, 1) latents ("direct" mode, used where building the context through
+  append would take long, e.g. 60 layers x 128 x 8192 tokens);
+* weights ~ N(0, 1/fan_in); q^C, q^R ~ N(0, 1) (the distribution of W^UQ h and
+  W^QR h under those weights).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import seeded_inputs as si
+
+D_C, D_R, D_H = 512, 64, 128
+D_K = D_C + D_R
+
+
+@dataclass
+class Config:
+    name: str
+    n_h: int
+    d_model: int
+    B: int
+    lens: object            # int (uniform prior context L) or (lo, hi) ragged range of L
+    dtype: torch.dtype = torch.bfloat16
+    page_size: int = 64
+    permute_pages: bool = False
+    cache_mode: str = "append"   # "append" | "direct"
+    layers: int = 1
+    seed: int = 1234
+    query: str = "synthetic"     # "synthetic" | "projected" (q from W^UQ, W^QR; tests only)
+
+    def context_lengths(self) -> np.ndarray:
+        """Prior context L_b per sequence (the decode token comes on top)."""
+        if isinstance(self.lens, (tuple, list)):
+            lo, hi = self.lens
+            return si.uniform_ints(self.seed, self.name + "/lens", self.B, lo, hi)
+        return np.full(self.B, int(self.lens), dtype=np.int64)
+
+
+# The benchmark configurations (DeepSeek-V2 MLA decode shapes).
+CONFIGS = {
+    "tiny_fp32": Config("tiny_fp32", n_h=16, d_model=1024, B=1, lens=256, dtype=torch.float32,
+                        cache_mode="append", seed=1235, query="projected"),
+    "b32_l4096": Config("b32_l4096", n_h=128, d_model=5120, B=32, lens=4096, seed=1236),
+    "b64_ragged": Config("b64_ragged", n_h=128, d_model=5120, B=64, lens=(1024, 16384), permute_pages=True,
+                         seed=1237),
+    "b4_l131072": Config("b4_l131072", n_h=128, d_model=5120, B=4, lens=131072, seed=1238),
+    "l60_b128_l8192": Config("l60_b128_l8192", n_h=128, d_model=5120, B=128, lens=8192, layers=60,
+                             cache_mode="direct", seed=1239),
+    "b64_l8192": Config("b64_l8192", n_h=128, d_model=5120, B=64, lens=8192, seed=1240),
+}
+
+
+def scaled(cfg: Config, **kw) -> Config:
+    """A copy of cfg with some fields replaced (smaller test variants)."""
+    d = dict(cfg.__dict__)
+    d.update(kw)
+    return Config(**d)
+
+
+def _key(cfg: Config, name: str, layer: int = 0) -> int:
+    return si.stream_key(cfg.seed, name, layer)
+
+
+class Workload:
+    """Device tensors of one configuration (one layer at a time)."""
+
+    def __init__(self, cfg: Config, device="cuda", layer: int = 0, n_splits: int = 0):
+        import compressed_kv_cache_mla_amd as mla
+        self.mla = mla
+        self.cfg = cfg
+        self.layer = layer
+        self.device = torch.device(device)
+        self.dims = mla.Dims(n_h=cfg.n_h, d_model=cfg.d_model, page_size=cfg.page_size, dtype=cfg.dtype)
+        self.n_splits = n_splits
+        L = cfg.context_lengths()
+        self.n = (L + 1).astype(np.int64)                      # cached tokens incl. the decode token
+        self.prefix = np.concatenate([[0], np.cumsum(self.n)]).astype(np.int64)
+        ps = cfg.page_size
+        self.pages_per_seq = (self.n + ps - 1) // ps
+        self.max_pages = int(self.pages_per_seq.max())
+        self.num_pages = int(self.pages_per_seq.sum())
+        order = si.permutation(cfg.seed, cfg.name + "/pages", self.num_pages) if cfg.permute_pages \
+            else np.arange(self.num_pages)
+        pt = np.zeros((cfg.B, self.max_pages), dtype=np.int32)
+        off = 0
+        for b in range(cfg.B):
+            k = int(self.pages_per_seq[b])
+            pt[b, :k] = order[off:off + k]
+            off += k
+        self.page_table_np = pt
+        dev = self.device
+        self.page_table = torch.from_numpy(pt).to(dev)
+        self.seq_lens = torch.from_numpy(self.n.astype(np.int32)).to(dev)
+        self.pos_q = torch.from_numpy((self.n - 1).astype(np.int32)).to(dev)
+        self.pool = torch.empty((self.num_pages * ps, D_K), dtype=cfg.dtype, device=dev)
+        self.c_KV = self.pool[:, :D_C]
+        self.k_R = self.pool[:, D_C:]
+        self.row_stride = D_K
+        self.out = torch.empty((cfg.B, cfg.n_h, D_H), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((cfg.B, cfg.n_h), dtype=torch.float32, device=dev)
+        self._build_weights()
+        self._build_queries()
+        self._build_cache()
+        self.workspace = torch.empty(mla.decode_workspace_size(self.dims, cfg.B, n_splits), dtype=torch.uint8,
+                                     device=dev)
+
+    # ---------------------------------------------------------------- inputs
+    def _w(self, name, rows, cols, fan_in, device=None):
+        return si.normal(_key(self.cfg, name, self.layer), (rows, cols), 1.0 / math.sqrt(fan_in), self.cfg.dtype,
+                         device or self.device)
+
+    def _build_weights(self):
+        c, dm, nh = self.cfg, self.cfg.d_model, self.cfg.n_h
+        self.W_DKV = self._w("W_DKV", D_C, dm, dm)
+        self.W_KR = self._w("W_KR", D_R, dm, dm)
+        self.W_UK = self._w("W_UK", nh * D_H, D_C, D_C)
+        self.W_UV = self._w("W_UV", nh * D_H, D_C, D_C)
+
+    def _build_queries(self):
+        c = self.cfg
+        if c.query == "synthetic":
+            self.q_C = si.normal(_key(c, "q_C", self.layer), (c.B, c.n_h, D_H), 1.0, c.dtype, self.device)
+            self.q_R = si.normal(_key(c, "q_R", self.layer), (c.B, c.n_h, D_R), 1.0, c.dtype, self.device)
+        else:   # filled in by the caller (set_queries)
+            self.q_C = torch.zeros((c.B, c.n_h, D_H), dtype=c.dtype, device=self.device)
+            self.q_R = torch.zeros((c.B, c.n_h, D_R), dtype=c.dtype, device=self.device)
+
+    def set_queries(self, q_C: torch.Tensor, q_R: torch.Tensor):
+        self.q_C.copy_(q_C.to(self.device, self.cfg.dtype))
+        self.q_R.copy_(q_R.to(self.device, self.cfg.dtype))
+
+    def token_rows(self):
+        """(seq_id, pos) of every cached token, in global token order."""
+        B = self.cfg.B
+        seq = np.repeat(np.arange(B), self.n)
+        pos = np.arange(int(self.prefix[-1])) - np.repeat(self.prefix[:-1], self.n)
+        return seq.astype(np.int32), pos.astype(np.int32)
+
+    def h_rows(self, rows, device=None):
+        """Token states h for global token ids ``rows`` (append mode)."""
+        return si.normal_rows(_key(self.cfg, "h", self.layer), rows, self.cfg.d_model, 1.0, self.cfg.dtype,
+                              device or self.device)
+
+    def latent_rows(self, rows, device=None):
+        """Direct-mode cache rows [c^KV ; k^R] for global token ids ``rows``."""
+        return si.normal_rows(_key(self.cfg, "latent", self.layer), rows, D_K, 1.0, self.cfg.dtype,
+                              device or self.device)
+
+    def pool_rows(self, seq: np.ndarray, pos: np.ndarray) -> np.ndarray:
+        ps = self.cfg.page_size
+        return self.page_table_np[seq, pos // ps].astype(np.int64) * ps + pos % ps
+
+    def _build_cache(self, chunk: int = 65536):
+        seq, pos = self.token_rows()
+        N = seq.size
+        if self.cfg.cache_mode == "direct":
+            # all tokens but each sequence's last come straight from the generator;
+            # the last (decode) token is appended through the library
+            last = self.prefix[1:] - 1
+            mask = np.ones(N, dtype=bool)
+            mask[last] = False
+            ids = np.nonzero(mask)[0]
+            for i in range(0, ids.size, chunk):
+                g = ids[i:i + chunk]
+                rows = torch.from_numpy(self.pool_rows(seq[g], pos[g])).to(self.device)
+                self.pool[rows] = self.latent_rows(torch.from_numpy(g).to(self.device))
+            self.append_tokens(last)
+        else:
+            self.append_tokens(np.arange(N))
+
+    def append_tokens(self, ids: np.ndarray, chunk: int = 65536):
+        """Run the append kernel for global token ids ``ids``."""
+        seq, pos = self.token_rows()
+        for i in range(0, ids.size, chunk):
+            g = ids[i:i + chunk]
+            h = self.h_rows(torch.from_numpy(g).to(self.device))
+            self.mla.cache_append(self.dims, h, self.W_DKV, self.W_KR,
+                                  torch.from_numpy(pos[g]).to(self.device), self.page_table, self.c_KV, self.k_R,
+                                  self.row_stride, self.num_pages,
+                                  seq_id=torch.from_numpy(seq[g]).to(self.device))
+
+    # ---------------------------------------------------------------- run
+    def decode(self, stream=None):
+        self.mla.decode(self.dims, self.q_C, self.q_R, self.pos_q, self.W_UK, self.W_UV, self.c_KV, self.k_R,
+                        self.row_stride, self.num_pages, self.page_table, self.seq_lens, self.out, self.lse,
+                        self.workspace, self.n_splits, stream)
+
+    # ---------------------------------------------------------------- oracle side (CPU, generator only)
+    def oracle_inputs(self, b: int) -> dict:
+        """fp64 numpy inputs of sequence b, regenerated on the CPU."""
+        c = self.cfg
+        g0, g1 = int(self.prefix[b]), int(self.prefix[b + 1])
+        f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+        cpu = torch.device("cpu")
+        W = {k: f64(self._w(k, *shape, device=cpu)) for k, shape in
+             {"W_UK": (c.n_h * D_H, D_C, D_C), "W_UV": (c.n_h * D_H, D_C, D_C)}.items()}
+        d = dict(W_UK=W["W_UK"], W_UV=W["W_UV"], n=g1 - g0, pos_q=g1 - g0 - 1)
+        if c.cache_mode == "direct":
+            lat = f64(self.latent_rows(range(g0, g1 - 1), device=cpu))
+            d["prior_c"], d["prior_kR"] = lat[:, :D_C], lat[:, D_C:]
+            d["h_new"] = f64(self.h_rows(range(g1 - 1, g1), device=cpu))
+        else:
+            d["h"] = f64(self.h_rows(range(g0, g1), device=cpu))
+        d["W_DKV"] = f64(self._w("W_DKV", D_C, c.d_model, c.d_model, device=cpu))
+        d["W_KR"] = f64(self._w("W_KR", D_R, c.d_model, c.d_model, device=cpu))
+        if c.query == "synthetic":
+            d["q_C"] = f64(si.normal_rows(_key(c, "q_C", self.layer), range(b * c.n_h, (b + 1) * c.n_h), D_H, 1.0,
+                                          c.dtype, cpu))
+            d["q_R"] = f64(si.normal_rows(_key(c, "q_R", self.layer), range(b * c.n_h, (b + 1) * c.n_h), D_R, 1.0,
+                                          c.dtype, cpu))
+        return d
