@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA decode hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input: the
+append of each sequence's newest token (W^DKV down-projection + RoPE'd k^R
+into the paged latent cache) followed by mla_decode (plan, absorb, split-KV
+attention over the latent cache, combine, W^UV epilogue).  Inputs are
+resident in HBM before timing starts.  To keep the 256 MB Infinity Cache from
+serving repeated reads, steps rotate over several independent copies of the
+workload (own weights, queries and cache) whose total size exceeds it.
+
+Prints one JSON line.  `value` is decode tokens/s (B sequences per step);
+`roofline` is computed for the split-KV attention kernel from its algorithmic
+bytes and its HIP-event duration measured in the timed region; `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode tokens/s + latent-cache GB/s (% of HBM/MFMA roofline), 1 GPU"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+COUNTERS = os.path.join(ROOT, "profiles", "decode_attention_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "compressed_kv_cache_mla_amd", "csrc", "decode_mfma.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic(wl):
+    """Algorithmic bytes and flops of one step and of one launch of the
+    split-KV attention kernel."""
+    c = wl.cfg
+    N = int(wl.prefix[-1])
+    B, nh, dm = c.B, c.n_h, c.d_model
+    s = 2 if c.dtype.itemsize == 2 else 4
+    cache = N * 576 * s
+    attn_bytes = cache + B * nh * 576 * s + B * nh * (512 * 4 + 8)       # rows + q~ in, O~ + (m, l) out
+    attn_flops = N * nh * (2 * 576 + 2 * 512)
+    step_bytes = (cache + 2 * nh * 128 * 512 * s          # W^UK, W^UV
+                  + 576 * dm * s + B * dm * s + B * 576 * s  # W^DKV|W^KR, h, new rows
+                  + B * nh * (128 + 64) * s + B * nh * (128 + 1) * 4)   # q^C, q^R in; out, lse
+    step_flops = attn_flops + B * 4 * nh * 128 * 512 + B * 2 * dm * 576
+    return dict(N=N, cache=cache, attn_bytes=attn_bytes, attn_flops=attn_flops, step_bytes=step_bytes,
+                step_flops=step_flops)
+
+
+def cpu_baseline(wl, seconds: float):
+    """The fp64 oracle (absorbed form) doing the same per-sequence work as a
+    step -- append the newest token, then decode -- on a bounded sample."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    sample = [0, 1]
+    prepared = []
+    for b in sample:
+        d = wl.oracle_inputs(b)
+        n = d["n"]
+        if "h" in d:
+            c, kR = oracle.down_project(d["h"][:n - 1], d["W_DKV"], d["W_KR"], np.arange(n - 1), wl.dims.rope_base)
+            h_new = d["h"][n - 1:]
+        else:
+            c, kR, h_new = d["prior_c"], d["prior_kR"], d["h_new"]
+        prepared.append((d, c, kR, h_new))
+    done, t0 = 0, time.perf_counter()
+    while True:
+        for d, c, kR, h_new in prepared:
+            n = d["n"]
+            c1, k1 = oracle.down_project(h_new, d["W_DKV"], d["W_KR"], np.array([n - 1]), wl.dims.rope_base)
+            oracle.attend_absorbed(d["q_C"], d["q_R"], n - 1, np.concatenate([c, c1]), np.concatenate([kR, k1]),
+                                   d["W_UK"], d["W_UV"], wl.dims.rope_base, wl.dims.scale)
+            done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    n0 = int(wl.n[0])
+    return {"value": done / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 absorbed-form oracle, append + decode of sequences {sample} ({n0} cached tokens, "
+                      f"n_h={wl.cfg.n_h}) repeated {done} times in {el:.1f} s; 1 decode token per sequence"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b32_l4096")
+    ap.add_argument("--copies", type=int, default=0, help="workload copies to rotate over (0 = enough to exceed "
+                                                         "the 256 MB Infinity Cache twice)")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--impl", type=int, default=0, help="0 = MFMA attention kernel, 1 = VALU reference kernel")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not part of it "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+
+    cfg = W.CONFIGS[args.workload]
+    if cfg.layers > 1:
+        cfg = W.scaled(cfg, layers=1)
+    t_build = time.perf_counter()
+    first = W.Workload(cfg, layer=0, n_splits=args.splits)
+    alg = algorithmic(first)
+    per_copy = alg["step_bytes"] + first.workspace.numel()
+    copies = args.copies or max(2, math.ceil(2 * 256e6 / per_copy))
+    wls = [first] + [W.Workload(cfg, layer=i, n_splits=args.splits) for i in range(1, copies)]
+    torch.cuda.synchronize()
+    print(f"# built {copies} copies of {cfg.name} in {time.perf_counter() - t_build:.1f} s "
+          f"({per_copy / 1e6:.0f} MB each)", file=sys.stderr, flush=True)
+
+    def step(i, evs=None):
+        wl = wls[i % copies]
+        wl.append_step()
+        if evs is None:
+            wl.decode(impl=args.impl)
+        else:
+            wl.decode(ev_start=evs[0], ev_stop=evs[1], impl=args.impl)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in kev:        # create the HIP events before the timed region
+        a.record()
+        b.record()
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, kev[i])
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_start.elapsed_time(t_stop)
+    kern_ms = [a.elapsed_time(b) for a, b in kev]
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    ms_per_step = total_ms / args.steps
+    B = cfg.B
+    value = B / (ms_per_step * 1e-3)
+
+    achieved = alg["attn_bytes"] / (kern_avg * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS):
+        cnt = json.load(open(COUNTERS))
+        rec = cnt.get("workloads", {}).get(cfg.name)
+        if rec and cnt.get("kernel_source_sha256_16") == kernel_source_hash() and args.impl == 0:
+            traffic = rec["hbm_bytes_per_launch"]
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if cfg.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "context_tokens_per_seq": int(cfg.lens) if not isinstance(
+            cfg.lens, (tuple, list)) else list(cfg.lens), "cached_tokens": alg["N"], "n_h": cfg.n_h, "d_h": 128,
+                   "d_c": 512, "d_hR": 64, "d_model": cfg.d_model, "page_size": cfg.page_size,
+                   "copies_rotated": copies, "n_splits": args.splits or first.mla.cu_count()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "split-KV attention (decode_mfma_kernel)" if args.impl == 0 else "decode_simple_kernel",
+                     "kernel_us": round(kern_avg * 1e3, 2),
+                     "mfma_tflops": round(alg["attn_flops"] / (kern_avg * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(alg["attn_flops"] / (kern_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "latent_cache_GBps": round(alg["cache"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_GBps": round(alg["step_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(alg["step_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,8 +23,8 @@ MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP
 MLA_BF16, MLA_FP32 = 0, 1
 FLAG_BAD_SEQ_LEN, FLAG_BAD_PAGE, FLAG_BAD_POSITION, FLAG_BAD_SEQ_ID = 1, 2, 4, 8
 
-EXPORTED = ("mla_cache_append", "mla_decode_workspace_size", "mla_decode", "mla_read_error_flags",
-            "mla_last_error", "mla_device_cu_count")
+EXPORTED = ("mla_cache_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_ex",
+            "mla_read_error_flags", "mla_last_error", "mla_device_cu_count")
 
 
 class MlaError(RuntimeError):
@@ -37,6 +37,10 @@ class mla_dims(ctypes.Structure):
     _fields_ = [("n_h", ctypes.c_int32), ("d_h", ctypes.c_int32), ("d_c", ctypes.c_int32),
                 ("d_hR", ctypes.c_int32), ("d_model", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class mla_decode_opts(ctypes.Structure):
+    _fields_ = [("ev_start", ctypes.c_void_p), ("ev_stop", ctypes.c_void_p), ("impl", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -83,6 +87,9 @@ def lib() -> ctypes.CDLL:
         L.mla_decode.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32, vp, vp, vp, vp, sz,
                                  i32, vp]
         L.mla_decode.restype = ctypes.c_int
+        L.mla_decode_ex.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32, vp, vp, vp, vp, sz,
+                                    i32, ctypes.POINTER(mla_decode_opts), vp]
+        L.mla_decode_ex.restype = ctypes.c_int
         L.mla_read_error_flags.argtypes = [vp, ctypes.POINTER(i32), vp]
         L.mla_read_error_flags.restype = ctypes.c_int
         L.mla_last_error.argtypes = []
@@ -128,19 +135,34 @@ def decode_workspace_size(dims: Dims, B: int, n_splits: int = 0) -> int:
     return int(lib().mla_decode_workspace_size(ctypes.byref(d), B, n_splits))
 
 
+def _event_handle(ev):
+    if ev is None:
+        return None
+    if not ev.cuda_event:      # torch creates the HIP event on its first record
+        ev.record()
+    return ctypes.c_void_p(ev.cuda_event)
+
+
 def decode(dims: Dims, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride: int, num_pages: int, page_table,
-           seq_lens, out, lse=None, workspace=None, n_splits: int = 0, stream=None):
-    """mla_decode: one query per sequence against its cached latent rows;
-    writes out [B, n_h, d_h] (fp32) and optionally lse [B, n_h]."""
+           seq_lens, out, lse=None, workspace=None, n_splits: int = 0, stream=None, ev_start=None, ev_stop=None,
+           impl: int = 0):
+    """mla_decode (mla_decode_ex when events or impl are given): one query per
+    sequence against its cached latent rows; writes out [B, n_h, d_h] (fp32)
+    and optionally lse [B, n_h].  ev_start / ev_stop (torch.cuda.Event) are
+    recorded around the split-KV attention kernel."""
     B = q_C.shape[0]
     max_pages = page_table.shape[1]
     if workspace is None:
         workspace = torch.empty(decode_workspace_size(dims, B, n_splits), dtype=torch.uint8, device=q_C.device)
     d = dims.c()
-    _check(lib().mla_decode(ctypes.byref(d), B, _ptr(q_C), _ptr(q_R), _ptr(pos_q), _ptr(W_UK), _ptr(W_UV),
-                            _ptr(c_KV), _ptr(k_R), row_stride, num_pages, _ptr(page_table), max_pages,
-                            _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), n_splits,
-                            _stream(stream)))
+    args = (ctypes.byref(d), B, _ptr(q_C), _ptr(q_R), _ptr(pos_q), _ptr(W_UK), _ptr(W_UV), _ptr(c_KV), _ptr(k_R),
+            row_stride, num_pages, _ptr(page_table), max_pages, _ptr(seq_lens), _ptr(out), _ptr(lse),
+            _ptr(workspace), workspace.numel(), n_splits)
+    if ev_start is None and ev_stop is None and impl == 0:
+        _check(lib().mla_decode(*args, _stream(stream)))
+    else:
+        o = mla_decode_opts(_event_handle(ev_start), _event_handle(ev_stop), impl)
+        _check(lib().mla_decode_ex(*args, ctypes.byref(o), _stream(stream)))
     return workspace
 
 

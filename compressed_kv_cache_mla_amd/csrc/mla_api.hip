@@ -108,6 +108,15 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, const void* q_C, const vo
                       const void* W_UK, const void* W_UV, const void* c_KV, const void* k_R, int64_t row_stride,
                       int32_t num_pages, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
                       float* out, float* lse, void* workspace, size_t ws_bytes, int32_t n_splits, void* stream) {
+  return mla_decode_ex(dims, B, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride, num_pages, page_table, max_pages,
+                       seq_lens, out, lse, workspace, ws_bytes, n_splits, nullptr, stream);
+}
+
+mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
+                         const void* W_UK, const void* W_UV, const void* c_KV, const void* k_R, int64_t row_stride,
+                         int32_t num_pages, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                         float* out, float* lse, void* workspace, size_t ws_bytes, int32_t n_splits,
+                         const mla_decode_opts* opts, void* stream) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
@@ -139,8 +148,11 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, const void* q_C, const vo
 
   hipError_t e = mla::launch_plan(seq_lens, B, max_tokens, prefix, flags, s);
   if (e == hipSuccess) e = mla::launch_absorb(*dims, B, q_C, q_R, pos_q, W_UK, qabs, s);
+  if (opts && opts->impl != 0 && opts->impl != 1) return fail(MLA_ERR_INVALID_ARG, "opts->impl=%d", opts->impl);
+  if (e == hipSuccess && opts && opts->ev_start) e = hipEventRecord((hipEvent_t)opts->ev_start, s);
   if (e == hipSuccess) {
-    const bool mfma = dims->dtype == MLA_BF16 && (dims->n_h == 32 || dims->n_h == 64 || dims->n_h == 128);
+    const bool mfma = dims->dtype == MLA_BF16 && (dims->n_h == 32 || dims->n_h == 64 || dims->n_h == 128) &&
+                      !(opts && opts->impl == 1);
     if (mfma)
       e = mla::launch_decode_mfma(*dims, B, qabs, c_KV, k_R, row_stride, num_pages, page_table, max_pages, prefix,
                                   n_splits, part_ml, part_o, flags, s);
@@ -148,6 +160,7 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, const void* q_C, const vo
       e = mla::launch_decode_simple(*dims, B, qabs, c_KV, k_R, row_stride, num_pages, page_table, max_pages,
                                     prefix, n_splits, part_ml, part_o, flags, s);
   }
+  if (e == hipSuccess && opts && opts->ev_stop) e = hipEventRecord((hipEvent_t)opts->ev_stop, s);
   if (e == hipSuccess) e = mla::launch_combine(*dims, B, prefix, n_splits, part_ml, part_o, W_UV, out, lse, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();

@@ -147,6 +147,27 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, const void* q_C, const vo
                       void* stream);
 
 /*
+ * mla_decode_ex -- mla_decode with options.  opts may be NULL (then it is
+ * mla_decode).  ev_start / ev_stop are hipEvent_t handles (or NULL) recorded
+ * on `stream` right before and right after the split-KV attention kernel, so
+ * a caller can time that kernel alone.  impl selects the attention kernel:
+ * 0 = default (bf16 MFMA kernel when dtype is bf16 and n_h is 32, 64 or 128;
+ * otherwise the VALU kernel), 1 = always the VALU kernel (reference path).
+ */
+typedef struct mla_decode_opts {
+  void* ev_start;
+  void* ev_stop;
+  int32_t impl;
+} mla_decode_opts;
+
+mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const void* q_R,
+                         const int32_t* pos_q, const void* W_UK, const void* W_UV,
+                         const void* c_KV, const void* k_R, int64_t row_stride, int32_t num_pages,
+                         const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                         float* out, float* lse, void* workspace, size_t ws_bytes, int32_t n_splits,
+                         const mla_decode_opts* opts, void* stream);
+
+/*
  * mla_read_error_flags -- wait for `stream`, then copy the device error flags
  * of a decode workspace (or an append err_flag word) to *flags and clear them.
  */

@@ -200,10 +200,20 @@ class Workload:
                                   seq_id=torch.from_numpy(seq[g]).to(self.device))
 
     # ---------------------------------------------------------------- run
-    def decode(self, stream=None):
+    def decode(self, stream=None, ev_start=None, ev_stop=None, impl=0):
         self.mla.decode(self.dims, self.q_C, self.q_R, self.pos_q, self.W_UK, self.W_UV, self.c_KV, self.k_R,
                         self.row_stride, self.num_pages, self.page_table, self.seq_lens, self.out, self.lse,
-                        self.workspace, self.n_splits, stream)
+                        self.workspace, self.n_splits, stream, ev_start, ev_stop, impl)
+
+    def append_step(self, stream=None):
+        """The decode step's append: each sequence's newest token (position
+        n_b - 1) is written again from its token state."""
+        if not hasattr(self, "_step_h"):
+            last = self.prefix[1:] - 1
+            self._step_h = self.h_rows(torch.from_numpy(last).to(self.device))
+            self._step_pos = self.pos_q.clone()
+        self.mla.cache_append(self.dims, self._step_h, self.W_DKV, self.W_KR, self._step_pos, self.page_table,
+                              self.c_KV, self.k_R, self.row_stride, self.num_pages, stream=stream)
 
     # ---------------------------------------------------------------- oracle side (CPU, generator only)
     def oracle_inputs(self, b: int) -> dict:
