@@ -8,7 +8,7 @@
 //
 // One launch handles T token rows.  The product [T x d_model] x [d_model x 576]
 // is an MFMA GEMM (bf16 inputs, fp32 accumulation) for bf16 and a VALU GEMM for
-// fp32.  Workgroup tile: 32 tokens x 64 output columns; columns 0..511 come
+// fp32; a decode step's few rows take the split-K variant at the end.  Workgroup tile: 32 tokens x 64 output columns; columns 0..511 come
 // from W^DKV, 512..575 from W^KR (the ninth column tile is exactly k^R, so its
 // RoPE pairs never straddle tiles).  The epilogue stages the fp32 tile in LDS,
 // rotates the k^R pairs (angles in fp64), rounds to the cache type and writes
@@ -171,6 +171,75 @@ __global__ void __launch_bounds__(256) append_bf16_kernel(
                      num_pages, c_KV, k_R, row_stride, rope_base, err_flag);
 }
 
+// Few tokens (a decode step): the product is weight-bandwidth bound, so the
+// grid is spread over output columns.  Workgroup = 16 tokens x 16 output
+// columns; its 4 waves split d_model into quarters (v_mfma_f32_16x16x32_bf16,
+// operands straight from global memory) and the quarter sums are added in LDS.
+__global__ void __launch_bounds__(256) append_bf16_small_kernel(
+    int32_t T_rows, int32_t d_model, const bf16* __restrict__ h, const bf16* __restrict__ W_DKV,
+    const bf16* __restrict__ W_KR, const int32_t* __restrict__ seq_id, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ page_table, int32_t num_seqs, int32_t max_pages, int32_t page_size,
+    bf16* __restrict__ c_KV, bf16* __restrict__ k_R, int64_t row_stride, int32_t num_pages, float rope_base,
+    int32_t* err_flag) {
+  __shared__ float red[4][16][17];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tok0 = blockIdx.x * 16;
+  const int col0 = blockIdx.y * 16;
+  const bf16* W = col0 < D_C ? W_DKV + (int64_t)col0 * d_model : W_KR + (int64_t)(col0 - D_C) * d_model;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int kq4 = d_model / 4;                     // K range of this wave
+  const bf16* wrow = W + (int64_t)r16 * d_model + wave * kq4 + kq;
+  const bf16* hrow = h + (int64_t)min(tok0 + r16, T_rows - 1) * d_model + wave * kq4 + kq;
+  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  int k = 0;
+  for (; k + 64 <= kq4; k += 64) {
+    const bf16x8 w0 = *(const bf16x8*)(wrow + k), w1 = *(const bf16x8*)(wrow + k + 32);
+    const bf16x8 a0 = *(const bf16x8*)(hrow + k), a1 = *(const bf16x8*)(hrow + k + 32);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, w0, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, w1, acc1, 0, 0, 0);
+  }
+  for (; k < kq4; k += 32) {
+    const bf16x8 w0 = *(const bf16x8*)(wrow + k);
+    const bf16x8 a0 = *(const bf16x8*)(hrow + k);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, w0, acc0, 0, 0, 0);
+  }
+  // C layout: lane holds output column lane%16, tokens 4*(lane/16) + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][r16] = acc0[i] + acc1[i];
+  __syncthreads();
+  if (tid < 128) {
+    const int r = tid >> 3, cp = tid & 7;          // token row, column pair
+    const int t = tok0 + r;
+    if (t < T_rows) {
+      float x0 = red[0][r][2 * cp] + red[1][r][2 * cp] + red[2][r][2 * cp] + red[3][r][2 * cp];
+      float x1 = red[0][r][2 * cp + 1] + red[1][r][2 * cp + 1] + red[2][r][2 * cp + 1] + red[3][r][2 * cp + 1];
+      const int32_t sq = seq_id ? seq_id[t] : t;
+      const int32_t p = pos[t];
+      if (sq < 0 || sq >= num_seqs) {
+        if (err_flag) atomicOr(err_flag, MLA_FLAG_BAD_SEQ_ID);
+      } else if (p < 0 || p >= max_pages * page_size) {
+        if (err_flag) atomicOr(err_flag, MLA_FLAG_BAD_POSITION);
+      } else {
+        const int64_t row = pool_row(page_table, max_pages, num_pages, page_size, sq, p, err_flag);
+        const int c = col0 + 2 * cp;
+        bf16* dst;
+        if (c >= D_C) {
+          float cs, sn;
+          rope_cos_sin(p, (c - D_C) / 2, D_R, rope_base, &cs, &sn);
+          const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+          x0 = y0;
+          x1 = y1;
+          dst = k_R + row * row_stride + (c - D_C);
+        } else {
+          dst = c_KV + row * row_stride + c;
+        }
+        dst[0] = (bf16)x0;
+        dst[1] = (bf16)x1;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void* W_DKV, const void* W_KR,
@@ -183,6 +252,12 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
                                           (const float*)W_KR, seq_id, pos, page_table, num_seqs, max_pages,
                                           d.page_size, (float*)c_KV, (float*)k_R, row_stride, num_pages,
                                           d.rope_base, err_flag);
+  } else if (T <= 512 && d.d_model % 128 == 0) {
+    dim3 g2((T + 15) / 16, D_K / 16);
+    append_bf16_small_kernel<<<g2, 256, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV,
+                                                 (const bf16*)W_KR, seq_id, pos, page_table, num_seqs, max_pages,
+                                                 d.page_size, (bf16*)c_KV, (bf16*)k_R, row_stride, num_pages,
+                                                 d.rope_base, err_flag);
   } else {
     append_bf16_kernel<<<grid, 256, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV,
                                            (const bf16*)W_KR, seq_id, pos, page_table, num_seqs, max_pages,

@@ -8,55 +8,87 @@
 // split combine (combine kernel), so K and V are never built (ch.2 §2,
 // absorption paragraph).
 //
-// One workgroup = 4 waves (one per SIMD, occupancy 1) and one contiguous range
-// of the batch's tokens (see split_begin).  All n_h heads of a sequence share
-// each staged tile:
-//  * Tiles of TT = 48 cached rows (54 KB) are copied HBM -> LDS with
-//    global_load_lds (16 B per lane, 1 KB per wave instruction, coalesced),
-//    double buffered.  Row r keeps its 72 16-byte chunks in row-major order
-//    with chunk c stored at slot c ^ swz(r), which makes both LDS read
-//    patterns below bank-conflict free.
+// One workgroup = NW waves (one per SIMD, occupancy 1) and one contiguous
+// range of the batch's tokens (see split_begin).  All n_h = 32*NW heads of a
+// sequence share each staged tile:
+//  * Tiles of TT = 32 cached rows (36 KB) are copied HBM -> LDS with
+//    global_load_lds (16 B per lane, 1 KB per wave instruction), three
+//    buffers deep: two tiles are in flight while one is computed.  Lane l of
+//    every copy instruction always fetches row l%32 of the tile, so a tile
+//    needs one page lookup per lane and each copy is a single address add.
+//    In LDS the tile is chunk-major: 16-byte chunk c of row r sits at
+//    (c/2)*BLK + (c%2)*512 + 16r, with BLK = 1 KB + 64 B of padding, which
+//    keeps both read patterns below free of bank conflicts.
 //  * Scores: wave w owns heads 32w..32w+31.  S^T (16 tokens x 16 heads
-//    blocks) = K_tile . Q^T with v_mfma_f32_16x16x32_bf16; the wave's Q block
-//    (32 heads x 576, bf16) lives in 144 VGPRs, K fragments come from LDS.
+//    blocks) = K_tile . Q^T with v_mfma_f32_16x16x32_bf16.  The wave's query
+//    block (32 heads x 576 bf16) is split: latent dims 0..447 in 112 VGPRs,
+//    dims 448..575 (incl. the RoPE part) staged once per sequence in LDS.
 //  * Online softmax in the owner wave, in log2 units (q~ carries
 //    softmax_scale*log2(e)).  The running reference max only moves when a
-//    tile's max exceeds it by more than 8 (so p <= 2^8), which makes the
-//    O rescale rare.  P (bf16) and the rescale factors go to LDS.
-//  * P.V: wave w owns latent columns [128w, 128w+128) for all heads
-//    (O^T blocks of 32 d x 32 heads, v_mfma_f32_32x32x16_bf16, 256 fp32
-//    accumulators).  V^T fragments are read from the staged tile with
-//    ds_read_b64_tr_b16; P^T fragments with ds_read_b128.
-//  * At the end of each (sequence, range) segment the unnormalised O~, the
-//    reference max m and the sum l go to the segment's partial slot.
+//    tile's max exceeds it by more than 8 (so p <= 2^8), which makes the O
+//    rescale rare.  Row reductions use v_permlane16/32_swap.  P (bf16) and
+//    the rescale factors go to LDS.
+//  * P.V: wave w owns 512/NW latent columns for all heads (O^T blocks of 32
+//    latent columns x 32 heads, v_mfma_f32_32x32x16_bf16, 256 fp32
+//    accumulators kept in AGPRs).  Block dblk = 2g + p holds the columns of
+//    chunks 8g + p + {0, 2, 4, 6}.  V^T fragments are read from the staged
+//    tile with ds_read_b64_tr_b16; P^T fragments with ds_read_b128.
+//  * At the end of each (sequence, range) segment the unnormalised O~ (bf16),
+//    the reference max m and the sum l (fp32) go to the segment's partial slot.
 #include "mla_common.h"
 
 namespace mla {
 namespace {
 
-constexpr int TT = 48;                  // cached rows per tile
-constexpr int ROWB = D_K * 2;           // 1152 bytes per row (bf16)
-constexpr int TILEB = TT * ROWB;        // 55,296 bytes
-constexpr int NINSTR = TT * 72 / 64;    // 54 DMA instructions of 1 KB per tile
-constexpr int PSTR = 112;               // bytes per head row of P in LDS (48 bf16 + pad)
+constexpr int TT = 32;                  // cached rows per tile
+constexpr int NINSTR = TT * 72 / 64;    // 36 copy instructions (blocks of 1 KB) per tile
+constexpr int BLK = 1024 + 64;          // LDS bytes per block: chunks 2k, 2k+1 of 32 rows, padded
+constexpr int TILEB = NINSTR * BLK;     // 39,168 bytes per tile buffer
+constexpr int PSTR = 80;                // bytes per head row of P in LDS (32 bf16 + pad)
 constexpr float RESCALE_T = 8.0f;       // log2 headroom before the reference max moves
 constexpr int KS = D_K / 32;            // 18 K-steps of 32 for the score MFMA
-constexpr int KS_REG = 14;              // K-steps of the query block kept in VGPRs;
-                                        // the last 4 (latent dims 448..511 and the
-                                        // RoPE dims) are staged in LDS
+constexpr int KS_REG = 14;              // K-steps of the query block kept in VGPRs
+constexpr int KS_LDS = KS - KS_REG;     // K-steps staged in LDS (query dims 448..575)
+constexpr int QLB = KS_LDS * 64;        // LDS bytes per head of the staged query part
+
+// s_waitcnt immediate waiting until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left alone).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Slot permutation of row r: chunk c lives at slot c ^ swz(r) (swz < 8).
-__device__ __forceinline__ int swz(int r) {
-  const int t = r >> 1;
-  return ((t & 1) << 2) | ((t >> 1) & 3);
+// HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i's
+// chunk lands at LDS byte lds_base + 16*i.  Issued through asm so that the
+// compiler's wait-count pass does not see an LDS write in flight: with one
+// visible it drains every LDS wait to zero, which would serialise the
+// fragment reads below.  The instruction has no result register; its
+// completion is awaited explicitly (vmcnt(0) + barrier before the tile is
+// read), and the memory clobber keeps LDS accesses on their side of it.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
 }
 
-// The O accumulators are meant to stay in AGPRs for the whole kernel; these
-// helpers touch one accumulator through an "a" operand so that the register
-// allocator never moves the 256 of them into VGPRs.
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float wave_rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float wave_rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// The O accumulators stay in AGPRs for the whole kernel; these macros touch
+// one accumulator through an "a" operand so that the register allocator never
+// moves the 256 of them into VGPRs.
 #define ACC_SCALE(x, a)                                                                        \
   do {                                                                                         \
     float acc_tmp_;                                                                            \
@@ -130,15 +162,16 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1,
 decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV, const bf16* __restrict__ k_R,
                    int64_t row_stride, int32_t num_pages, const int32_t* __restrict__ page_table,
                    int32_t max_pages, int32_t page_size, const int32_t* __restrict__ prefix, int32_t B,
-                   int32_t G, float* __restrict__ part_ml, float* __restrict__ part_o,
+                   int32_t G, float* __restrict__ part_ml, bf16* __restrict__ part_o,
                    int32_t* __restrict__ flags) {
   constexpr int NH = 32 * NW;
-  constexpr int IPW = (NINSTR + NW - 1) / NW;   // DMA instructions per wave
+  constexpr int IPW = NINSTR / NW;              // DMA instructions per wave (NW divides 36)
   constexpr int DB = 16 / NW;                   // 32-wide latent blocks per wave in P.V
   __shared__ __attribute__((aligned(1024))) char kt0[TILEB];
   __shared__ __attribute__((aligned(1024))) char kt1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kt2[TILEB];
+  __shared__ __attribute__((aligned(1024))) char ql[NH * QLB];   // query dims 448..575, swizzled
   __shared__ __attribute__((aligned(16))) char pl[NH * PSTR];
-  __shared__ __attribute__((aligned(1024))) char ql[NH * 256];   // query dims 448..575, swizzled
   __shared__ float alpha_l[NH];
   __shared__ int resc_l[NW];
 
@@ -148,95 +181,65 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   const int32_t P0 = (int32_t)split_begin(blockIdx.x, N, G), P1 = (int32_t)split_begin(blockIdx.x + 1, N, G);
   if (P0 >= P1) return;
 
-  // ---- per-lane constant offsets
+  // ---- per-lane constant offsets (see the tile layout in the header)
   // score A fragment (16x16x32): row 16tb + (lane&15), chunk 4ks + (lane>>4)
-  const int a_row = lane & 15, a_g = lane >> 4;
-  const int a_sw = swz(a_row);
-  // slot of chunk 4ks + g is 8*(ks>>1) + 4*((ks&1) ^ (sw>>2)) + (g ^ (sw&3))
-  const int a_off_even = a_row * ROWB + (4 * (a_sw >> 2) + (a_g ^ (a_sw & 3))) * 16;
-  const int a_off_odd = a_row * ROWB + (4 * (1 - (a_sw >> 2)) + (a_g ^ (a_sw & 3))) * 16;
-  // V^T fragment (ds_read_b64_tr_b16): source lane s reads row kc*16 + 8*(s>>5) + 4rr + ((s&15)>>2),
-  // columns 32*dblk + 16*((s>>4)&1) + 4*(s&3) .. +3
-  const int v_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
-  const int v_colc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);   // chunk within the 32-column block
-  const int v_half = (lane & 1) * 8;                                // byte within the chunk
-  int v_off[2][2];  // [rr][dblk parity]
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int r = v_row + 4 * rr;     // kc*16 adds a multiple of 16: same swizzle
-    const int sw = swz(r);
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      // chunk (4*dblk + v_colc) ^ sw, dblk parity par; the dblk-dependent part
-      // 4*dblk ^ 4*(sw>>2) is 4*(dblk ^ (sw>>2)): for parity par this is
-      // 4*dblk + 4*((par ^ (sw>>2)) - par)
-      const int dpar = 4 * ((par ^ (sw >> 2)) - par);
-      v_off[rr][par] = r * ROWB + (dpar + (v_colc ^ (sw & 3))) * 16 + v_half;
-    }
-  }
+  const int a_off = (lane >> 5) * BLK + ((lane >> 4) & 1) * 512 + (lane & 15) * 16;
+  // staged query fragment: head 32w + 16hb + (lane&15), chunk 4(ks-KS_REG) + (lane>>4),
+  // stored at chunk position c ^ (head & 15)
+  const int q_off = (32 * wave + (lane & 15)) * QLB;
+  // V^T fragment (ds_read_b64_tr_b16) of block dblk = 2g + p, rows kc*16 + 4rr + ...:
+  // source lane s reads row 8*(s>>5) + ((s&15)>>2) (plus kc*16 + 4rr), chunk 8g + p + 2y with
+  // y = 2*((s>>4)&1) + ((s&3)>>1), bytes 8*(s&1) .. +7 of that chunk
+  const int v_y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int v_off = v_y * BLK + (8 * (lane >> 5) + ((lane & 15) >> 2)) * 16 + 8 * (lane & 1);
   // P^T fragment: head 32hb + (lane&31), tokens kc*16 + 8*(lane>>5)
   const int p_off = (lane & 31) * PSTR + (lane >> 5) * 16;
 
   const cprefix_t cpre = (cprefix_t)prefix;
+  const cprefix_t cpt = (cprefix_t)page_table;
   Cursor cur;
   cur.init(cpre, B, P0, P1);
-  TileDesc t_now = cur.next(cpre);     // tile being computed
-  TileDesc t_nxt = cur.next(cpre);     // tile whose rows are in flight
+  TileDesc t_now = cur.next(cpre);   // tile being computed
+  TileDesc t_n1 = cur.next(cpre);    // tile in flight
+  TileDesc t_n2 = cur.next(cpre);    // tile whose copy is issued this iteration
 
-  // Row lookup for a tile in two halves: fetch() issues the page-table load
-  // (lane r < TT handles tile row r) and its result is only consumed by
-  // resolve() one tile later, so no wait on it lands inside a tile's compute.
-  struct RowFetch {
-    int32_t page, slot;
+  // Page lookup of a tile, one iteration before its copy is issued.  Pages
+  // hold at least TT tokens (the host sends smaller pages to the VALU
+  // kernel), so a tile touches at most two pages, whose ids come through
+  // scalar loads: a vector load here would be waited for with the tiles in
+  // flight.
+  auto fetch_rows = [&](const TileDesc& td, int32_t& pg0, int32_t& pg1, int32_t& p0) {
+    pg0 = pg1 = p0 = 0;
+    if (td.n <= 0) return;
+    const int64_t rowbase = (int64_t)td.b * max_pages;
+    p0 = td.t0 / page_size;
+    const int32_t p1 = (td.t0 + td.n - 1) / page_size;
+    pg0 = cpt[rowbase + p0];
+    pg1 = cpt[rowbase + p1];
   };
-  auto fetch_rows = [&](const TileDesc& td) -> RowFetch {
-    RowFetch f;
-    if (td.n <= 0) {
-      f.page = 0;
-      f.slot = 0;
-      return f;
-    }
-    int r = lane < TT ? lane : TT - 1;
-    if (r >= td.n) r = td.n - 1;
+  // Pool row of tile row lane%32 (rows past the tile's end repeat its last row).
+  auto resolve_rows = [&](const TileDesc& td, int32_t pg0, int32_t pg1, int32_t p0) -> int32_t {
+    const int r = min(lane & (TT - 1), td.n - 1);
     const int t = td.t0 + r;
-    f.page = page_table[(int64_t)td.b * max_pages + t / page_size];
-    f.slot = t % page_size;
-    return f;
-  };
-  auto resolve_rows = [&](const RowFetch& f) -> int32_t {
-    int32_t pg = f.page;
+    int32_t pg = t / page_size == p0 ? pg0 : pg1;
     if (pg < 0 || pg >= num_pages) {
       atomicOr(flags, MLA_FLAG_BAD_PAGE);
       pg = pg < 0 ? 0 : num_pages - 1;
     }
-    return pg * page_size + f.slot;
+    return pg * page_size + t % page_size;
   };
-  const char* cbase = (const char*)c_KV;
-  const char* kbase = (const char*)k_R;
+  const char* cbase = (const char*)c_KV + (lane >> 5) * 16;
+  const char* kbase = (const char*)k_R - 1024 + (lane >> 5) * 16;   // chunk c >= 64 is k^R chunk c - 64
   const int64_t stride_b = row_stride * 2;
+  // Copy instruction I of a tile: lane l fetches chunk 2I + l/32 of tile row l%32.
   auto issue_dma = [&](char* kt, int32_t ridx) {
-    // Recomputed for every tile (the empty asm hides the lane id from loop
-    // invariant hoisting, which would otherwise keep 14 addresses live).
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    int wv = __builtin_amdgcn_readfirstlane(wave);
-    asm volatile("" : "+s"(wv));
+    const char* cb = cbase + (int64_t)ridx * stride_b;
+    const char* kb = kbase + (int64_t)ridx * stride_b;
+    const uint32_t lbase = lds_addr(kt);
 #pragma unroll
     for (int k = 0; k < IPW; ++k) {
-      const int I = wv * IPW + k;
-      if (I < NINSTR) {
-        const int sigma = I * 64 + ln;
-        const int row = sigma / 72;
-        const int posn = sigma - row * 72;
-        const int chunk = posn ^ swz(row);
-        const int ra = (I * 64) / 72;
-        const int rb = ra + 1 < TT ? ra + 1 : TT - 1;
-        const int rid_a = __builtin_amdgcn_readlane(ridx, ra);
-        const int rid_b = __builtin_amdgcn_readlane(ridx, rb);
-        const int64_t rid = row == ra ? rid_a : rid_b;
-        const char* src = (chunk < 64 ? cbase : kbase) + rid * stride_b + (chunk & 63) * 16;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(kt + I * 1024), 16, 0, 0);
-      }
+      const int I = wave * IPW + k;
+      dma16((I < 32 ? cb : kb) + 32 * I, __builtin_amdgcn_readfirstlane(lbase + I * BLK));
     }
   };
 
@@ -246,7 +249,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   float m_ref[2], l_sum[2];
 
   auto load_q = [&](int32_t b) {
-    int ln = lane;   // hidden from hoisting, as in issue_dma
+    int ln = lane;   // hidden from loop-invariant hoisting
     asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -254,71 +257,97 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 #pragma unroll
       for (int ks = 0; ks < KS_REG; ++ks) q[hb][ks] = *(const bf16x8*)(qp + 32 * ks);
     }
-    // dims 448..575 of this wave's 32 heads -> ql, 16-byte chunk c of head h
-    // at position c ^ (h & 15)
+    // dims 448..575 of this wave's 32 heads -> ql: 16-byte chunk c of head h
+    // at chunk position c ^ (h & 15)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 32 * QLB / 1024; ++j) {
       const int sigma = 64 * j + ln;
-      const int hl = sigma >> 4, c = (sigma & 15) ^ (hl & 15);
+      const int hl = sigma / (QLB / 16), c = (sigma % (QLB / 16)) ^ (hl & 15);
       const bf16* src = qabs + ((int64_t)b * NH + 32 * wave + hl) * D_K + 32 * KS_REG + 8 * c;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(ql + wave * 8192 + j * 1024), 16, 0, 0);
+      dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(ql + wave * 32 * QLB + j * 1024)));
     }
   };
-  auto reset_state = [&]() {
+
+  // The query registers are loaded once per segment.  Their loads are waited
+  // for right away (vmcnt(0)) and the registers then pass through an empty
+  // asm, so the compiler sees no load of them pending across the loop and
+  // puts no wait in the score loop (a wait there would also hold up the
+  // tiles in flight).
+  auto settle_q = [&]() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 #pragma unroll
-    for (int hb = 0; hb < NW; ++hb)
+    for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ACC_ZERO(o[hb][db][r]);
-    m_ref[0] = m_ref[1] = -INFINITY;
-    l_sum[0] = l_sum[1] = 0.f;
+      for (int ks = 0; ks < KS_REG; ++ks) asm volatile("" : "+v"(q[hb][ks]));
   };
 
-  // ---- prologue: rows of tile 0 -> kt0, row indices of tile 1 ready
-  {
-    issue_dma(kt0, resolve_rows(fetch_rows(t_now)));
-  }
-  RowFetch rows_next = fetch_rows(t_nxt);
-  load_q(t_now.b);
-  reset_state();
-
-  auto process = [&](char* kt, char* kt_other) {
-    // tile t_now is (being) loaded into kt; t_nxt goes to kt_other
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of t_now (and q) have landed
-    __syncthreads();                 // everyone's copies landed; P.V of the previous tile done
-    if (t_nxt.n > 0) issue_dma(kt_other, resolve_rows(rows_next));
-    TileDesc t_after = cur.next(cpre);
-    rows_next = fetch_rows(t_after);
-
-    // ---- scores S^T[token][head] for this wave's 32 heads
-    f32x4 s[3][2];
+  // ---- prologue: tiles 0 and 1 in flight, page ids of tile 2 fetched
 #pragma unroll
-    for (int tb = 0; tb < 3; ++tb)
+  for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ACC_ZERO(o[hb][db][r]);
+  m_ref[0] = m_ref[1] = -INFINITY;
+  l_sum[0] = l_sum[1] = 0.f;
+  int32_t f_pg0, f_pg1, f_p0;      // page ids of tile t_n2
+  fetch_rows(t_now, f_pg0, f_pg1, f_p0);
+  issue_dma(kt0, resolve_rows(t_now, f_pg0, f_pg1, f_p0));
+  if (t_n1.n > 0) {
+    fetch_rows(t_n1, f_pg0, f_pg1, f_p0);
+    issue_dma(kt1, resolve_rows(t_n1, f_pg0, f_pg1, f_p0));
+  }
+  fetch_rows(t_n2, f_pg0, f_pg1, f_p0);
+  load_q(t_now.b);
+  settle_q();
+
+  auto process = [&](char* kt, char* kt_issue) {
+    // Tile t_now was copied into kt two iterations ago; t_n1's copy (issued
+    // last iteration) may stay in flight.
+    if (t_n1.n <= 0)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
+    __syncthreads();   // every wave's copies landed; P.V of the previous tile done everywhere
+    if (t_n2.n > 0) issue_dma(kt_issue, resolve_rows(t_n2, f_pg0, f_pg1, f_p0));
+    TileDesc t_n3 = cur.next(cpre);
+    fetch_rows(t_n3, f_pg0, f_pg1, f_p0);
+
+    // ---- scores S^T[token][head] for this wave's 32 heads (2 x 2 blocks of 16x16)
+    // Software pipelined by hand: the fragments of K-step ks+2 are read before
+    // the MFMAs of K-step ks issue; sched_barrier keeps that order.
+    f32x4 s[2][2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) s[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 af[3][2], qf[3][2];
+    auto load_ks = [&](int ks, int st) {
+      const int off = a_off + 2 * ks * BLK;
+      af[st][0] = *(const bf16x8*)(kt + off);
+      af[st][1] = *(const bf16x8*)(kt + off + 256);
+      if (ks >= KS_REG) {
+        const int qc = ((4 * (ks - KS_REG) + (lane >> 4)) ^ (lane & 15)) << 4;
+        qf[st][0] = *(const bf16x8*)(ql + q_off + qc);
+        qf[st][1] = *(const bf16x8*)(ql + q_off + 16 * QLB + qc);
+      }
+    };
+    load_ks(0, 0);
+    load_ks(1, 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int off = (ks & 1 ? a_off_odd : a_off_even) + 128 * (ks >> 1);
-      bf16x8 qb0, qb1;
-      if (ks < KS_REG) {
-        qb0 = q[0][ks];
-        qb1 = q[1][ks];
-      } else {
-        const int c = 4 * (ks - KS_REG) + (lane >> 4);
-        const int qo = (32 * wave + (lane & 15)) * 256 + ((c ^ (lane & 15)) << 4);
-        qb0 = *(const bf16x8*)(ql + qo);
-        qb1 = *(const bf16x8*)(ql + qo + 16 * 256);
-      }
+      if (ks + 2 < KS) load_ks(ks + 2, (ks + 2) % 3);
+      __builtin_amdgcn_sched_barrier(0);
+      const int st = ks % 3;
+      const bf16x8 qb0 = ks < KS_REG ? q[0][ks] : qf[st][0];
+      const bf16x8 qb1 = ks < KS_REG ? q[1][ks] : qf[st][1];
 #pragma unroll
-      for (int tb = 0; tb < 3; ++tb) {
-        const bf16x8 a = *(const bf16x8*)(kt + off + tb * 16 * ROWB);
-        s[tb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb0, s[tb][0], 0, 0, 0);
-        s[tb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb1, s[tb][1], 0, 0, 0);
+      for (int tb = 0; tb < 2; ++tb) {
+        s[tb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st][tb], qb0, s[tb][0], 0, 0, 0);
+        s[tb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st][tb], qb1, s[tb][1], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // the next sequence's query can be loaded once this segment's scores are done
-    if (t_now.last && t_nxt.n > 0) load_q(t_nxt.b);
 
     // ---- online softmax (owner wave), lane holds heads 32w + 16hb + (lane&15)
     const int n_valid = t_now.n;
@@ -327,15 +356,14 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
     for (int hb = 0; hb < 2; ++hb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int tb = 0; tb < 3; ++tb)
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = 16 * tb + 4 * (lane >> 4) + i;
           if (tok >= n_valid) s[tb][hb][i] = -INFINITY;
           mx = fmaxf(mx, s[tb][hb][i]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = wave_rows_max(mx);
       float alpha = 1.f;
       if (t_now.first) {
         // a new segment: the accumulators restart from zero (alpha = 0)
@@ -343,15 +371,14 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
         any_resc = 1;
         m_ref[hb] = mx;
       } else if (mx > m_ref[hb] + RESCALE_T) {
-        if (m_ref[hb] != -INFINITY) {
-          alpha = __builtin_amdgcn_exp2f(m_ref[hb] - mx);
-          any_resc = 1;
-        }
+        alpha = __builtin_amdgcn_exp2f(m_ref[hb] - mx);
+        any_resc = 1;
         m_ref[hb] = mx;
       }
       float sum = 0.f;
+      const int head = 32 * wave + 16 * hb + (lane & 15);
 #pragma unroll
-      for (int tb = 0; tb < 3; ++tb) {
+      for (int tb = 0; tb < 2; ++tb) {
         bf16x4 pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -359,22 +386,20 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
           pb[i] = (bf16)p;
           sum += (float)pb[i];
         }
-        const int head = 32 * wave + 16 * hb + (lane & 15);
         *(bf16x4*)(pl + head * PSTR + (16 * tb + 4 * (lane >> 4)) * 2) = pb;
       }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
+      sum = wave_rows_sum(sum);
       l_sum[hb] = l_sum[hb] * alpha + sum;
       if (lane < 16) alpha_l[32 * wave + 16 * hb + lane] = alpha;
     }
     const int wave_resc = __builtin_amdgcn_readfirstlane(__any(any_resc) ? 1 : 0);
     if (lane == 0) resc_l[wave] = wave_resc;
     // P, alpha visible to all waves.  Only LDS traffic is waited for: a plain
-    // __syncthreads would also wait for the next tile's copies in flight.
+    // __syncthreads would also wait for the tiles in flight.
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
     __builtin_amdgcn_s_barrier();
 
-    // ---- rescale O if any owner moved its reference max
+    // ---- rescale O if any owner moved its reference max (or a segment starts)
     int resc = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) resc |= resc_l[w];
@@ -389,32 +414,34 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       }
     }
 
-    // ---- O^T[d][head] += V^T[d][tok] P^T[tok][head]
+    // ---- O^T[d][head] += V^T[d][tok] P^T[tok][head], two 16-token chunks;
+    // both chunks' fragments are read before the first chunk's MFMAs issue
+    bf16x8 pf[2][NW], vf[2][DB];
 #pragma unroll
-    for (int kc = 0; kc < 3; ++kc) {
-      __builtin_amdgcn_sched_barrier(0);
-      bf16x8 pf[NW];
+    for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
       for (int hb = 0; hb < NW; ++hb)
-        pf[hb] = *(const bf16x8*)(pl + 32 * hb * PSTR + p_off + kc * 32);
+        pf[kc][hb] = *(const bf16x8*)(pl + 32 * hb * PSTR + p_off + kc * 32);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int dblk = DB * wave + db;
-        const int par = db & 1;   // DB is even, so dblk parity == db parity
-        const int base = kc * 16 * ROWB;
-        const int c0 = 64 * dblk;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(kt + base + v_off[0][par] + c0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(kt + base + v_off[1][par] + c0));
-        bf16x8 vf;
+        const int base = (dblk >> 1) * 4 * BLK + (dblk & 1) * 512 + kc * 16 * 16;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kt + base + v_off));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kt + base + v_off + 4 * 16));
         const bf16x4 lob = __builtin_bit_cast(bf16x4, lo), hib = __builtin_bit_cast(bf16x4, hi);
-        vf[0] = lob[0]; vf[1] = lob[1]; vf[2] = lob[2]; vf[3] = lob[3];
-        vf[4] = hib[0]; vf[5] = hib[1]; vf[6] = hib[2]; vf[7] = hib[3];
+        vf[kc][db][0] = lob[0]; vf[kc][db][1] = lob[1]; vf[kc][db][2] = lob[2]; vf[kc][db][3] = lob[3];
+        vf[kc][db][4] = hib[0]; vf[kc][db][5] = hib[1]; vf[kc][db][6] = hib[2]; vf[kc][db][7] = hib[3];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int hb = 0; hb < NW; ++hb)
-          o[hb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[hb], o[hb][db], 0, 0, 0);
-      }
+          o[hb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc][db], pf[kc][hb], o[hb][db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- segment end: write the partial (O~ unnormalised, m, l)
@@ -423,18 +450,26 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 #pragma unroll
       for (int hb = 0; hb < NW; ++hb) {
         const int head = 32 * hb + (lane & 31);
-        float* dst = part_o + (slot * NH + head) * D_C;
+        bf16* dst = part_o + (slot * NH + head) * D_C;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int d0 = 32 * (DB * wave + db) + 4 * (lane >> 5);
+          const int dblk = DB * wave + db;
+          // accumulator row m = 8*r4 + 4*(lane>>5) + r%4 is latent column
+          // 8*(8g + p + 2*r4) + 4*(lane>>5) + r%4 of block dblk = 2g + p
+          const int d0 = 64 * (dblk >> 1) + 8 * (dblk & 1) + 4 * (lane >> 5);
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            f32x4 v;
-            ACC_READ(v[0], o[hb][db][4 * r4]);
-            ACC_READ(v[1], o[hb][db][4 * r4 + 1]);
-            ACC_READ(v[2], o[hb][db][4 * r4 + 2]);
-            ACC_READ(v[3], o[hb][db][4 * r4 + 3]);
-            *(f32x4*)(dst + d0 + 8 * r4) = v;
+            float v0, v1, v2, v3;
+            ACC_READ(v0, o[hb][db][4 * r4]);
+            ACC_READ(v1, o[hb][db][4 * r4 + 1]);
+            ACC_READ(v2, o[hb][db][4 * r4 + 2]);
+            ACC_READ(v3, o[hb][db][4 * r4 + 3]);
+            bf16x4 v;
+            v[0] = (bf16)v0;
+            v[1] = (bf16)v1;
+            v[2] = (bf16)v2;
+            v[3] = (bf16)v3;
+            *(bf16x4*)(dst + d0 + 16 * r4) = v;
           }
         }
       }
@@ -448,15 +483,26 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       }
       m_ref[0] = m_ref[1] = -INFINITY;
       l_sum[0] = l_sum[1] = 0.f;
+      // the next segment's query, loaded and waited for here (once per
+      // segment) so that no query load is in flight during a later tile
+      if (t_n1.n > 0) {
+        load_q(t_n1.b);
+        settle_q();
+      }
     }
-    t_now = t_nxt;
-    t_nxt = t_after;
+    t_now = t_n1;
+    t_n1 = t_n2;
+    t_n2 = t_n3;
   };
 
+  // three iterations per loop so that the buffer roles stay compile-time:
+  // tile i is computed from buffer i%3 while tile i+2 is copied into (i+2)%3
   while (true) {
-    process(kt0, kt1);
+    process(kt0, kt2);
     if (t_now.n <= 0) break;
     process(kt1, kt0);
+    if (t_now.n <= 0) break;
+    process(kt2, kt1);
     if (t_now.n <= 0) break;
   }
 }
@@ -466,8 +512,9 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                               const void* k_R, int64_t row_stride, int32_t num_pages,
                               const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
-                              int32_t n_splits, float* part_ml, float* part_o, int32_t* flags,
+                              int32_t n_splits, float* part_ml, void* part_o_v, int32_t* flags,
                               hipStream_t s) {
+  bf16* part_o = (bf16*)part_o_v;
   const int nw = d.n_h / 32;
   dim3 grid(n_splits);
   switch (nw) {

@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(256) decode_simple_kernel(
     int32_t n_h, const T* __restrict__ qabs, const T* __restrict__ c_KV, const T* __restrict__ k_R,
     int64_t row_stride, int32_t num_pages, const int32_t* __restrict__ page_table, int32_t max_pages,
     int32_t page_size, const int32_t* __restrict__ prefix, int32_t B, int32_t G, float* __restrict__ part_ml,
-    float* __restrict__ part_o, int32_t* __restrict__ flags) {
+    T* __restrict__ part_o, int32_t* __restrict__ flags) {
   __shared__ float qs[D_K];
   __shared__ float ps[256];
   __shared__ int64_t rows[256];
@@ -131,9 +131,9 @@ __global__ void __launch_bounds__(256) decode_simple_kernel(
         }
         m = m_new;
       }
-      float* dst = part_o + (slot * n_h + h) * D_C;
-      dst[tid] = o0;
-      dst[tid + 256] = o1;
+      T* dst = part_o + (slot * n_h + h) * D_C;
+      dst[tid] = from_f32<T>(o0);
+      dst[tid + 256] = from_f32<T>(o1);
       if (tid == 0) {
         part_ml[(slot * n_h + h) * 2 + 0] = m;
         part_ml[(slot * n_h + h) * 2 + 1] = l;
@@ -153,18 +153,18 @@ hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_tokens, i
 hipError_t launch_decode_simple(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                                 const void* k_R, int64_t row_stride, int32_t num_pages,
                                 const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
-                                int32_t n_splits, float* part_ml, float* part_o, int32_t* flags,
+                                int32_t n_splits, float* part_ml, void* part_o, int32_t* flags,
                                 hipStream_t s) {
   if (d.dtype == MLA_FP32)
     decode_simple_kernel<float><<<n_splits, 256, 0, s>>>(d.n_h, (const float*)qabs, (const float*)c_KV,
                                                          (const float*)k_R, row_stride, num_pages, page_table,
                                                          max_pages, d.page_size, prefix, B, n_splits, part_ml,
-                                                         part_o, flags);
+                                                         (float*)part_o, flags);
   else
     decode_simple_kernel<bf16><<<n_splits, 256, 0, s>>>(d.n_h, (const bf16*)qabs, (const bf16*)c_KV,
                                                         (const bf16*)k_R, row_stride, num_pages, page_table,
                                                         max_pages, d.page_size, prefix, B, n_splits, part_ml,
-                                                        part_o, flags);
+                                                        (bf16*)part_o, flags);
   return hipGetLastError();
 }
 

@@ -142,7 +142,7 @@ mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const
   int32_t* prefix = (int32_t*)(ws + L.prefix);
   void* qabs = ws + L.qabs;
   float* part_ml = (float*)(ws + L.part_ml);
-  float* part_o = (float*)(ws + L.part_o);
+  void* part_o = ws + L.part_o;
   hipStream_t s = (hipStream_t)stream;
   const int32_t max_tokens = max_pages * dims->page_size;
 
@@ -152,7 +152,7 @@ mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const
   if (e == hipSuccess && opts && opts->ev_start) e = hipEventRecord((hipEvent_t)opts->ev_start, s);
   if (e == hipSuccess) {
     const bool mfma = dims->dtype == MLA_BF16 && (dims->n_h == 32 || dims->n_h == 64 || dims->n_h == 128) &&
-                      !(opts && opts->impl == 1);
+                      dims->page_size >= 32 && !(opts && opts->impl == 1);
     if (mfma)
       e = mla::launch_decode_mfma(*dims, B, qabs, c_KV, k_R, row_stride, num_pages, page_table, max_pages, prefix,
                                   n_splits, part_ml, part_o, flags, s);

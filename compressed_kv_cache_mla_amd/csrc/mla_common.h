@@ -68,7 +68,7 @@ inline DecodeWs decode_ws_layout(int32_t B, int32_t n_h, int32_t n_splits, int e
   w.prefix = off;  off += align256((size_t)(B + 1) * 4);
   w.qabs = off;    off += align256((size_t)B * n_h * D_K * elt);
   w.part_ml = off; off += align256((size_t)w.n_slots * n_h * 2 * 4);
-  w.part_o = off;  off += align256((size_t)w.n_slots * n_h * D_C * 4);
+  w.part_o = off;  off += align256((size_t)w.n_slots * n_h * D_C * elt);   // partial O~ in the cache type
   w.total = off;
   return w;
 }
@@ -108,14 +108,14 @@ hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const vo
 hipError_t launch_decode_simple(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                                 const void* k_R, int64_t row_stride, int32_t num_pages,
                                 const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
-                                int32_t n_splits, float* part_ml, float* part_o, int32_t* flags,
+                                int32_t n_splits, float* part_ml, void* part_o, int32_t* flags,
                                 hipStream_t s);
 hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                               const void* k_R, int64_t row_stride, int32_t num_pages,
                               const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
-                              int32_t n_splits, float* part_ml, float* part_o, int32_t* flags,
+                              int32_t n_splits, float* part_ml, void* part_o, int32_t* flags,
                               hipStream_t s);
 hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, int32_t n_splits,
-                          const float* part_ml, const float* part_o, const void* W_UV, float* out,
+                          const float* part_ml, const void* part_o, const void* W_UV, float* out,
                           float* lse, hipStream_t s);
 }  // namespace mla

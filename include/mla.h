@@ -151,8 +151,8 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, const void* q_C, const vo
  * mla_decode).  ev_start / ev_stop are hipEvent_t handles (or NULL) recorded
  * on `stream` right before and right after the split-KV attention kernel, so
  * a caller can time that kernel alone.  impl selects the attention kernel:
- * 0 = default (bf16 MFMA kernel when dtype is bf16 and n_h is 32, 64 or 128;
- * otherwise the VALU kernel), 1 = always the VALU kernel (reference path).
+ * 0 = default (bf16 MFMA kernel when dtype is bf16, n_h is 32, 64 or 128 and
+ * page_size >= 32; otherwise the VALU kernel), 1 = always the VALU kernel.
  */
 typedef struct mla_decode_opts {
   void* ev_start;

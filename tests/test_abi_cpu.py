@@ -93,8 +93,10 @@ def test_workspace_size_grows_with_batch_and_splits():
     b = L.mla_decode_workspace_size(ctypes.byref(d), 128, 256)
     c = L.mla_decode_workspace_size(ctypes.byref(d), 64, 512)
     assert 0 < a < b and a < c
-    # partials (G + B slots) of n_h x (512 + 2) fp32 dominate
-    assert a >= (256 + 64) * 128 * 514 * 4
+    # partials (G + B slots) of n_h x 512 bf16 latents plus (m, l) in fp32 dominate
+    assert a >= (256 + 64) * 128 * (512 * 2 + 8)
+    f = L.mla_decode_workspace_size(ctypes.byref(_dims(dtype=mla.MLA_FP32)), 64, 256)
+    assert f >= (256 + 64) * 128 * (512 * 4 + 8) > a
     assert L.mla_decode_workspace_size(ctypes.byref(_dims(d_c=1)), 64, 256) == 0
 
 

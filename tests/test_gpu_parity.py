@@ -91,6 +91,17 @@ def test_bf16_edge_lengths():
         _check_decode(wl, range(cfg.B))
 
 
+@pytest.mark.parametrize("page_size", [1, 16, 32, 48, 256])
+def test_bf16_page_sizes(page_size):
+    # pages below 32 tokens take the VALU kernel, the others the MFMA kernel
+    cfg = W.scaled(W.CONFIGS["b64_ragged"], name=f"pages{page_size}", d_model=256, B=5, lens=(0, 700),
+                   page_size=page_size, seed=300 + page_size)
+    _say(f"case {cfg.name}")
+    for n_splits in (1, 29):
+        wl = W.Workload(cfg, n_splits=n_splits)
+        _check_decode(wl, range(cfg.B))
+
+
 def test_bf16_page_permutation_is_bitwise_invariant():
     base = W.scaled(W.CONFIGS["b64_ragged"], name="perm", d_model=256, B=6, lens=(100, 900), seed=5)
     _say("case page permutation")
@@ -115,8 +126,11 @@ def test_bf16_deterministic_and_split_invariant():
         torch.cuda.synchronize()
         assert torch.equal(a, wl.out), "same inputs and splits must give bitwise-equal results"
         res[n_splits] = a.double().cpu().numpy()
+    # Split counts change where the softmax is cut and each split's partial
+    # latent is rounded to bf16 once (relative 2^-9); outputs agree to a few
+    # such roundings, well inside the 1e-2 parity bound every split count meets.
     for k, v in res.items():
-        assert rel_err(v, res[1]) < 2e-3, f"splits {k} vs 1"
+        assert rel_err(v, res[1]) < 5e-3, f"splits {k} vs 1"
 
 
 def test_b32_l4096_full():
@@ -159,6 +173,7 @@ def test_bad_device_values_are_flagged_not_faulting():
     wl = W.Workload(cfg, n_splits=8)
     wl.decode()
     assert mla.read_error_flags(wl.workspace) == 0
+    good_out = wl.out.clone()
     good = wl.seq_lens.clone()
     wl.seq_lens[1] = 0
     wl.decode()
@@ -170,4 +185,6 @@ def test_bad_device_values_are_flagged_not_faulting():
     wl.decode()
     assert mla.read_error_flags(wl.workspace) & mla.FLAG_BAD_PAGE
     torch.cuda.synchronize()
-    assert torch.isfinite(wl.out).all()
+    # the bad id was clamped into the pool (sequence 0 then reads rows of
+    # another page, whatever they hold); the other sequences are untouched
+    assert torch.equal(wl.out[1:], good_out[1:])
