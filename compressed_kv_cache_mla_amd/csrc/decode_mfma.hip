@@ -13,20 +13,27 @@
 // sequence share each staged tile:
 //  * Tiles of TT = 32 cached rows (36 KB) are copied HBM -> LDS with
 //    global_load_lds (16 B per lane, 1 KB per wave instruction), three
-//    buffers deep: two tiles are in flight while one is computed.  Lane l of
-//    every copy instruction always fetches row l%32 of the tile, so a tile
-//    needs one page lookup per lane and each copy is a single address add.
-//    In LDS the tile is chunk-major: 16-byte chunk c of row r sits at
-//    (c/2)*BLK + (c%2)*512 + 16r, with BLK = 1 KB + 64 B of padding, which
-//    keeps both read patterns below free of bank conflicts.
+//    buffers deep: two tiles are in flight while one is computed.  A row is
+//    9 lines of 128 B (8 of c^KV, 1 of k^R); copy instruction (g, j) fetches
+//    line j of the 8 rows of row group g, i.e. 8 whole cache lines, into a
+//    1 KB LDS window: the 16-byte chunk c of row r = 8g + m sits in window
+//    9g + c/8 at granule 8*(m ^ (g&1)) + ((c%8) ^ sw(m)), sw swapping the
+//    two low bits of m.  That places the score fragments (16 rows, one
+//    chunk) and the V^T transposed reads (4 rows x 4 chunks) on distinct
+//    LDS banks.  Wave w copies row group w, so a lane resolves one pool row
+//    per tile.  The two page ids a tile can touch (pages hold >= 32 rows)
+//    are copied into LDS one iteration ahead the same way, so they travel in
+//    the same in-order queue as the tiles: no scalar load is pending while
+//    LDS reads are waited for.
 //  * Scores: wave w owns heads 32w..32w+31.  S^T (16 tokens x 16 heads
 //    blocks) = K_tile . Q^T with v_mfma_f32_16x16x32_bf16.  The wave's query
 //    block (32 heads x 576 bf16) is split: latent dims 0..447 in 112 VGPRs,
 //    dims 448..575 (incl. the RoPE part) staged once per sequence in LDS.
 //  * Online softmax in the owner wave, in log2 units (q~ carries
 //    softmax_scale*log2(e)).  The running reference max only moves when a
-//    tile's max exceeds it by more than 8 (so p <= 2^8), which makes the O
-//    rescale rare.  Row reductions use v_permlane16/32_swap.  P (bf16) and
+//    tile's max exceeds it by more than RESCALE_T (so p <= 2^RESCALE_T), which
+//    makes the O rescale rare; the accumulators are zeroed when a segment
+//    ends.  Row reductions use v_permlane16/32_swap.  P (bf16) and
 //    the rescale factors go to LDS.
 //  * P.V: wave w owns 512/NW latent columns for all heads (O^T blocks of 32
 //    latent columns x 32 heads, v_mfma_f32_32x32x16_bf16, 256 fp32
@@ -34,7 +41,9 @@
 //    chunks 8g + p + {0, 2, 4, 6}.  V^T fragments are read from the staged
 //    tile with ds_read_b64_tr_b16; P^T fragments with ds_read_b128.
 //  * At the end of each (sequence, range) segment the unnormalised O~ (bf16),
-//    the reference max m and the sum l (fp32) go to the segment's partial slot.
+//    the reference max m and the sum l (fp32) go to the segment's partial slot;
+//    O~ is transposed through the wave's staged-query LDS area so that every
+//    store writes whole 256-byte row pieces.
 #include "mla_common.h"
 
 namespace mla {
@@ -42,10 +51,10 @@ namespace {
 
 constexpr int TT = 32;                  // cached rows per tile
 constexpr int NINSTR = TT * 72 / 64;    // 36 copy instructions (blocks of 1 KB) per tile
-constexpr int BLK = 1024 + 64;          // LDS bytes per block: chunks 2k, 2k+1 of 32 rows, padded
-constexpr int TILEB = NINSTR * BLK;     // 39,168 bytes per tile buffer
+constexpr int TILEB = NINSTR * 1024;    // 36,864 bytes per tile buffer (36 windows of 1 KB)
+constexpr int PGOFF = TILEB;            // the tile's two page ids follow its windows
 constexpr int PSTR = 80;                // bytes per head row of P in LDS (32 bf16 + pad)
-constexpr float RESCALE_T = 8.0f;       // log2 headroom before the reference max moves
+constexpr float RESCALE_T = 24.0f;      // log2 headroom before the reference max moves
 constexpr int KS = D_K / 32;            // 18 K-steps of 32 for the score MFMA
 constexpr int KS_REG = 14;              // K-steps of the query block kept in VGPRs
 constexpr int KS_LDS = KS - KS_REG;     // K-steps staged in LDS (query dims 448..575)
@@ -65,11 +74,35 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // fragment reads below.  The instruction has no result register; its
 // completion is awaited explicitly (vmcnt(0) + barrier before the tile is
 // read), and the memory clobber keeps LDS accesses on their side of it.
+// m0 (which holds the LDS base) is saved and restored around the copy, with
+// the one wait state required between an m0 write and an LDS-DMA load.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_base) : "memory", "m0");
+  uint32_t m0_save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(m0_save)
+               : "v"(gptr), "s"(lds_base)
+               : "memory");
+}
+// The same for 4 bytes per active lane (lane i -> lds_base + 4*i).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  uint32_t m0_save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(m0_save)
+               : "v"(gptr), "s"(lds_base)
+               : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+
+// Column swizzle of row m (0..7) inside an 8x8 window: swaps bits 0 and 1.
+__device__ __forceinline__ int swz(int m) { return (m & 4) | ((m & 1) << 1) | ((m >> 1) & 1); }
+
+// Split handled by workgroup bid: XCD x = bid % 8 receives the x-th of 8
+// contiguous runs of splits (run sizes differ by at most one).
+__device__ __forceinline__ int32_t xcd_split(int32_t bid, int32_t G) {
+  const int32_t x = bid & 7, q = G >> 3, r = G & 7;
+  return x * q + (x < r ? x : r) + (bid >> 3);
 }
 
 // Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
@@ -100,58 +133,67 @@ __device__ __forceinline__ float wave_rows_sum(float x) {
 #define ACC_ZERO(x) asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(x))
 
 struct TileDesc {
-  int32_t b, t0, n;   // sequence, first token in the sequence, rows (0 = none)
+  int32_t b, t0, n;    // sequence, first token in the sequence, rows (0 = none)
+  int32_t p0, rem;     // page index of t0 within the sequence, t0 % page_size
   int32_t first, last;
 };
 
-// The prefix sums are written by the plan kernel and only read here, so they
-// are read through the constant address space (uniform scalar loads).
-typedef const __attribute__((address_space(4))) int32_t* cprefix_t;
+// Read-only device arrays (plan records, prefix sums, page table) are read
+// through the constant address space so that uniform reads are scalar loads.
+typedef const __attribute__((address_space(4))) int32_t* cint_t;
 
-// Cursor over the tiles of one workgroup's token range [x, P1).
+// Cursor over the tiles of one workgroup's token range [x, P1).  Tiles never
+// straddle two sequences; within a sequence the page index and offset of the
+// next tile advance by TT (pages hold at least TT rows).
 struct Cursor {
   int32_t x, P1, s_beg, s_end, seg_beg;
-  int32_t b, B;
-  __device__ void init(cprefix_t prefix, int32_t B_, int32_t P0, int32_t P1_) {
+  int32_t b, B, pidx, prem, page_size;
+  __device__ void init(cint_t rec, int32_t B_, int32_t P0, int32_t P1_, int32_t ps) {
     B = B_;
     P1 = P1_;
     x = P0;
-    if (x < P1) {
-      int32_t lo = 0, hi = B - 1;   // last b with prefix[b] <= x
-      while (lo < hi) {
-        const int32_t mid = (lo + hi + 1) >> 1;
-        if (prefix[mid] <= x) lo = mid; else hi = mid - 1;
-      }
-      b = lo;
-      s_beg = prefix[b];
-      s_end = prefix[b + 1];
-    } else {
-      b = 0;
-      s_beg = s_end = 0;
-    }
+    page_size = ps;
+    b = rec[0];
+    s_beg = rec[1];
+    s_end = rec[2];
     seg_beg = x;
+    const int32_t t0 = x - s_beg;
+    pidx = t0 / ps;
+    prem = t0 - pidx * ps;
   }
-  __device__ TileDesc next(cprefix_t prefix) {
+  __device__ TileDesc next(cint_t prefix) {
     TileDesc t;
     if (x >= P1) {
-      t.b = 0; t.t0 = 0; t.n = 0; t.first = 0; t.last = 0;
+      t.b = 0; t.t0 = 0; t.n = 0; t.p0 = 0; t.rem = 0; t.first = 0; t.last = 0;
       return t;
     }
     const int32_t seg_end = s_end < P1 ? s_end : P1;
     t.b = b;
     t.t0 = x - s_beg;
     t.n = (seg_end - x) < TT ? (seg_end - x) : TT;
+    t.p0 = pidx;
+    t.rem = prem;
     t.first = (x == seg_beg);
     x += t.n;
     t.last = (x == seg_end);
-    if (t.last && x < P1) {
-      // move to the next sequence holding tokens (skip empty ones)
-      do {
-        ++b;
-        s_beg = s_end;
-        s_end = prefix[b + 1];
-      } while (s_end <= x && b < B - 1);
-      seg_beg = x;
+    if (t.last) {
+      if (x < P1) {
+        // move to the next sequence holding tokens (skip empty ones)
+        do {
+          ++b;
+          s_beg = s_end;
+          s_end = prefix[b + 1];
+        } while (s_end <= x && b < B - 1);
+        seg_beg = x;
+      }
+      pidx = 0;
+      prem = 0;
+    } else {
+      prem += TT;   // a tile that does not end its segment has TT rows
+      if (prem >= page_size) {
+        prem -= page_size;
+        ++pidx;
+      }
     }
     return t;
   }
@@ -161,15 +203,16 @@ template <int NW>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV, const bf16* __restrict__ k_R,
                    int64_t row_stride, int32_t num_pages, const int32_t* __restrict__ page_table,
-                   int32_t max_pages, int32_t page_size, const int32_t* __restrict__ prefix, int32_t B,
-                   int32_t G, float* __restrict__ part_ml, bf16* __restrict__ part_o,
-                   int32_t* __restrict__ flags) {
+                   int32_t max_pages, int32_t page_size, const int32_t* __restrict__ prefix,
+                   const int32_t* __restrict__ split_rec, int32_t B, int32_t G, float* __restrict__ part_ml,
+                   bf16* __restrict__ part_o, int32_t* __restrict__ flags) {
   constexpr int NH = 32 * NW;
   constexpr int IPW = NINSTR / NW;              // DMA instructions per wave (NW divides 36)
   constexpr int DB = 16 / NW;                   // 32-wide latent blocks per wave in P.V
-  __shared__ __attribute__((aligned(1024))) char kt0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char kt1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char kt2[TILEB];
+  constexpr int PIECES = DB / 4;                // 128-column pieces of a wave's latent columns
+  __shared__ __attribute__((aligned(1024))) char kt0[TILEB + 16];
+  __shared__ __attribute__((aligned(1024))) char kt1[TILEB + 16];
+  __shared__ __attribute__((aligned(1024))) char kt2[TILEB + 16];
   __shared__ __attribute__((aligned(1024))) char ql[NH * QLB];   // query dims 448..575, swizzled
   __shared__ __attribute__((aligned(16))) char pl[NH * PSTR];
   __shared__ float alpha_l[NH];
@@ -177,69 +220,95 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t N = ((cprefix_t)prefix)[B];
-  const int32_t P0 = (int32_t)split_begin(blockIdx.x, N, G), P1 = (int32_t)split_begin(blockIdx.x + 1, N, G);
+  const cint_t cpre = (cint_t)prefix;
+  const cint_t cpt = (cint_t)page_table;
+  const int64_t N = cpre[B];
+  // Workgroups are handed to the 8 XCDs round-robin; splits are mapped so
+  // that each XCD runs a contiguous run of splits, whose sequences' queries,
+  // page-table rows and plan records then stay in that XCD's L2.
+  const int32_t split = xcd_split(blockIdx.x, G);
+  const int32_t P0 = (int32_t)split_begin(split, N, G), P1 = (int32_t)split_begin(split + 1, N, G);
   if (P0 >= P1) return;
 
   // ---- per-lane constant offsets (see the tile layout in the header)
-  // score A fragment (16x16x32): row 16tb + (lane&15), chunk 4ks + (lane>>4)
-  const int a_off = (lane >> 5) * BLK + ((lane >> 4) & 1) * 512 + (lane & 15) * 16;
+  // score A fragment (16x16x32): row 16tb + (lane&15), chunk 4ks + (lane>>4);
+  // a_off[ks&1] + 18432*tb + 1024*(ks/2) is its byte in the tile
+  int a_off[2];
+  {
+    const int m = lane & 7, h = (lane >> 3) & 1, q4 = lane >> 4;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) a_off[par] = 16 * (576 * h + 8 * (m ^ h) + ((q4 ^ swz(m)) ^ (4 * par)));
+  }
   // staged query fragment: head 32w + 16hb + (lane&15), chunk 4(ks-KS_REG) + (lane>>4),
   // stored at chunk position c ^ (head & 15)
   const int q_off = (32 * wave + (lane & 15)) * QLB;
   // V^T fragment (ds_read_b64_tr_b16) of block dblk = 2g + p, rows kc*16 + 4rr + ...:
   // source lane s reads row 8*(s>>5) + ((s&15)>>2) (plus kc*16 + 4rr), chunk 8g + p + 2y with
   // y = 2*((s>>4)&1) + ((s&3)>>1), bytes 8*(s&1) .. +7 of that chunk
-  const int v_y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int v_off = v_y * BLK + (8 * (lane >> 5) + ((lane & 15) >> 2)) * 16 + 8 * (lane & 1);
+  // v_off[p][hi] + 1024*g + 18432*kc is that byte in the tile (rows m + 4*hi of the 8-row group)
+  int v_off[2][2];
+  {
+    const int rgb = lane >> 5, y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int m = ((lane & 15) >> 2) + 4 * hi;
+        v_off[p][hi] = 16 * (576 * rgb + 8 * (m ^ rgb) + ((p + 2 * y) ^ swz(m))) + 8 * (lane & 1);
+      }
+  }
   // P^T fragment: head 32hb + (lane&31), tokens kc*16 + 8*(lane>>5)
   const int p_off = (lane & 31) * PSTR + (lane >> 5) * 16;
 
-  const cprefix_t cpre = (cprefix_t)prefix;
-  const cprefix_t cpt = (cprefix_t)page_table;
   Cursor cur;
-  cur.init(cpre, B, P0, P1);
+  cur.init((cint_t)split_rec + 4 * split, B, P0, P1, page_size);
   TileDesc t_now = cur.next(cpre);   // tile being computed
   TileDesc t_n1 = cur.next(cpre);    // tile in flight
   TileDesc t_n2 = cur.next(cpre);    // tile whose copy is issued this iteration
 
-  // Page lookup of a tile, one iteration before its copy is issued.  Pages
-  // hold at least TT tokens (the host sends smaller pages to the VALU
-  // kernel), so a tile touches at most two pages, whose ids come through
-  // scalar loads: a vector load here would be waited for with the tiles in
-  // flight.
-  auto fetch_rows = [&](const TileDesc& td, int32_t& pg0, int32_t& pg1, int32_t& p0) {
-    pg0 = pg1 = p0 = 0;
-    if (td.n <= 0) return;
-    const int64_t rowbase = (int64_t)td.b * max_pages;
-    p0 = td.t0 / page_size;
-    const int32_t p1 = (td.t0 + td.n - 1) / page_size;
-    pg0 = cpt[rowbase + p0];
-    pg1 = cpt[rowbase + p1];
+  // Page-table index of the first (which = 0) or last (which = 1) page a tile touches.
+  auto page_index = [&](const TileDesc& td, int which) -> int64_t {
+    const int32_t p = (which && td.rem + td.n > page_size) ? td.p0 + 1 : td.p0;
+    return (int64_t)td.b * max_pages + p;
   };
-  // Pool row of tile row lane%32 (rows past the tile's end repeat its last row).
-  auto resolve_rows = [&](const TileDesc& td, int32_t pg0, int32_t pg1, int32_t p0) -> int32_t {
-    const int r = min(lane & (TT - 1), td.n - 1);
-    const int t = td.t0 + r;
-    int32_t pg = t / page_size == p0 ? pg0 : pg1;
+  // Pool row of tile row r (rows past the tile's end repeat its last row).
+  auto resolve_row = [&](const TileDesc& td, int r, int32_t pg0, int32_t pg1) -> int32_t {
+    r = min(r, td.n - 1);
+    const int off = td.rem + r;
+    const bool cross = off >= page_size;
+    int32_t pg = cross ? pg1 : pg0;
     if (pg < 0 || pg >= num_pages) {
       atomicOr(flags, MLA_FLAG_BAD_PAGE);
       pg = pg < 0 ? 0 : num_pages - 1;
     }
-    return pg * page_size + t % page_size;
+    return pg * page_size + (cross ? off - page_size : off);
   };
-  const char* cbase = (const char*)c_KV + (lane >> 5) * 16;
-  const char* kbase = (const char*)k_R - 1024 + (lane >> 5) * 16;   // chunk c >= 64 is k^R chunk c - 64
+  // The two page ids of a tile go to the pad after block 0 of a tile buffer
+  // (never written by tile copies, never read by the math).
+  auto issue_page_ids = [&](char* kt, const TileDesc& td) {
+    if (wave == 0 && td.n > 0 && lane < 2)
+      dma4(page_table + page_index(td, lane), __builtin_amdgcn_readfirstlane(lds_addr(kt + PGOFF)));
+  };
   const int64_t stride_b = row_stride * 2;
-  // Copy instruction I of a tile: lane l fetches chunk 2I + l/32 of tile row l%32.
-  auto issue_dma = [&](char* kt, int32_t ridx) {
-    const char* cb = cbase + (int64_t)ridx * stride_b;
-    const char* kb = kbase + (int64_t)ridx * stride_b;
+  // Copy of a tile: wave w fetches row groups w, w + NW, ...; in row group g
+  // lane l fetches row 8g + m, m = (l>>3) ^ (g&1), and chunk 8j + ((l&7) ^
+  // sw(m)) of it for the 9 lines j (line 8 is k^R).  The per-lane addresses
+  // are formed here from the scalar bases, not kept live across the loop.
+  auto issue_dma = [&](char* kt, const TileDesc& td, int32_t pg0, int32_t pg1) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
     const uint32_t lbase = lds_addr(kt);
 #pragma unroll
-    for (int k = 0; k < IPW; ++k) {
-      const int I = wave * IPW + k;
-      dma16((I < 32 ? cb : kb) + 32 * I, __builtin_amdgcn_readfirstlane(lbase + I * BLK));
+    for (int gi = 0; gi < 4 / NW; ++gi) {
+      const int g = wave + NW * gi;
+      const int m = (ln >> 3) ^ (g & 1);
+      const int64_t row = resolve_row(td, 8 * g + m, pg0, pg1);
+      const int64_t off = row * stride_b + 16 * ((ln & 7) ^ swz(m));
+      const char* cb = (const char*)c_KV + off;
+      const char* kb = (const char*)k_R + off;
+#pragma unroll
+      for (int j = 0; j < 9; ++j)
+        dma16(j < 8 ? cb + 128 * j : kb, __builtin_amdgcn_readfirstlane(lbase + (9 * g + j) * 1024));
     }
   };
 
@@ -281,7 +350,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       for (int ks = 0; ks < KS_REG; ++ks) asm volatile("" : "+v"(q[hb][ks]));
   };
 
-  // ---- prologue: tiles 0 and 1 in flight, page ids of tile 2 fetched
+  // ---- prologue: tiles 0 and 1 in flight, page ids of tile 2 in flight
 #pragma unroll
   for (int hb = 0; hb < NW; ++hb)
 #pragma unroll
@@ -290,28 +359,28 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       for (int r = 0; r < 16; ++r) ACC_ZERO(o[hb][db][r]);
   m_ref[0] = m_ref[1] = -INFINITY;
   l_sum[0] = l_sum[1] = 0.f;
-  int32_t f_pg0, f_pg1, f_p0;      // page ids of tile t_n2
-  fetch_rows(t_now, f_pg0, f_pg1, f_p0);
-  issue_dma(kt0, resolve_rows(t_now, f_pg0, f_pg1, f_p0));
-  if (t_n1.n > 0) {
-    fetch_rows(t_n1, f_pg0, f_pg1, f_p0);
-    issue_dma(kt1, resolve_rows(t_n1, f_pg0, f_pg1, f_p0));
-  }
-  fetch_rows(t_n2, f_pg0, f_pg1, f_p0);
+  issue_dma(kt0, t_now, cpt[page_index(t_now, 0)], cpt[page_index(t_now, 1)]);
+  if (t_n1.n > 0) issue_dma(kt1, t_n1, cpt[page_index(t_n1, 0)], cpt[page_index(t_n1, 1)]);
+  issue_page_ids(kt2, t_n2);
   load_q(t_now.b);
   settle_q();
 
   auto process = [&](char* kt, char* kt_issue) {
     // Tile t_now was copied into kt two iterations ago; t_n1's copy (issued
-    // last iteration) may stay in flight.
+    // last iteration, after the page ids of t_n2) may stay in flight.
     if (t_n1.n <= 0)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
-    __syncthreads();   // every wave's copies landed; P.V of the previous tile done everywhere
-    if (t_n2.n > 0) issue_dma(kt_issue, resolve_rows(t_n2, f_pg0, f_pg1, f_p0));
-    TileDesc t_n3 = cur.next(cpre);
-    fetch_rows(t_n3, f_pg0, f_pg1, f_p0);
+    __syncthreads();   // copies and page ids landed; P.V of the previous tile done everywhere
+    const TileDesc t_n3 = cur.next(cpre);
+    // page ids of t_n3 (its buffer is kt) before the copy of t_n2, so that
+    // next iteration's wait covers them
+    issue_page_ids(kt, t_n3);
+    if (t_n2.n > 0) {
+      const int2 pg = *(const int2*)(kt_issue + PGOFF);
+      issue_dma(kt_issue, t_n2, pg.x, pg.y);
+    }
 
     // ---- scores S^T[token][head] for this wave's 32 heads (2 x 2 blocks of 16x16)
     // Software pipelined by hand: the fragments of K-step ks+2 are read before
@@ -323,9 +392,9 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       for (int hb = 0; hb < 2; ++hb) s[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 af[3][2], qf[3][2];
     auto load_ks = [&](int ks, int st) {
-      const int off = a_off + 2 * ks * BLK;
+      const int off = a_off[ks & 1] + 1024 * (ks >> 1);
       af[st][0] = *(const bf16x8*)(kt + off);
-      af[st][1] = *(const bf16x8*)(kt + off + 256);
+      af[st][1] = *(const bf16x8*)(kt + off + 18432);
       if (ks >= KS_REG) {
         const int qc = ((4 * (ks - KS_REG) + (lane >> 4)) ^ (lane & 15)) << 4;
         qf[st][0] = *(const bf16x8*)(ql + q_off + qc);
@@ -355,20 +424,21 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       float mx = -INFINITY;
+      if (n_valid < TT) {   // a segment's last tile may be partial
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * tb + 4 * (lane >> 4) + i >= n_valid) s[tb][hb][i] = -INFINITY;
+      }
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * tb + 4 * (lane >> 4) + i;
-          if (tok >= n_valid) s[tb][hb][i] = -INFINITY;
-          mx = fmaxf(mx, s[tb][hb][i]);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tb][hb][i]);
       mx = wave_rows_max(mx);
       float alpha = 1.f;
       if (t_now.first) {
-        // a new segment: the accumulators restart from zero (alpha = 0)
-        alpha = 0.f;
-        any_resc = 1;
+        // a new segment: the accumulators were zeroed at the previous segment's end
         m_ref[hb] = mx;
       } else if (mx > m_ref[hb] + RESCALE_T) {
         alpha = __builtin_amdgcn_exp2f(m_ref[hb] - mx);
@@ -384,7 +454,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
         for (int i = 0; i < 4; ++i) {
           const float p = __builtin_amdgcn_exp2f(s[tb][hb][i] - m_ref[hb]);
           pb[i] = (bf16)p;
-          sum += (float)pb[i];
+          sum += p;
         }
         *(bf16x4*)(pl + head * PSTR + (16 * tb + 4 * (lane >> 4)) * 2) = pb;
       }
@@ -399,7 +469,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
     __builtin_amdgcn_s_barrier();
 
-    // ---- rescale O if any owner moved its reference max (or a segment starts)
+    // ---- rescale O if any owner moved its reference max (rare)
     int resc = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) resc |= resc_l[w];
@@ -425,9 +495,9 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int dblk = DB * wave + db;
-        const int base = (dblk >> 1) * 4 * BLK + (dblk & 1) * 512 + kc * 16 * 16;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kt + base + v_off));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kt + base + v_off + 4 * 16));
+        const int base = 1024 * (dblk >> 1) + 18432 * kc;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kt + base + v_off[dblk & 1][0]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kt + base + v_off[dblk & 1][1]));
         const bf16x4 lob = __builtin_bit_cast(bf16x4, lo), hib = __builtin_bit_cast(bf16x4, hi);
         vf[kc][db][0] = lob[0]; vf[kc][db][1] = lob[1]; vf[kc][db][2] = lob[2]; vf[kc][db][3] = lob[3];
         vf[kc][db][4] = hib[0]; vf[kc][db][5] = hib[1]; vf[kc][db][6] = hib[2]; vf[kc][db][7] = hib[3];
@@ -435,41 +505,63 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int hb = 0; hb < NW; ++hb)
+        o[hb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0][db], pf[0][hb], o[hb][db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int hb = 0; hb < NW; ++hb)
-          o[hb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc][db], pf[kc][hb], o[hb][db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hb = 0; hb < NW; ++hb)
+        o[hb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1][db], pf[1][hb], o[hb][db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- segment end: write the partial (O~ unnormalised, m, l)
     if (t_now.last) {
-      const int64_t slot = (int64_t)blockIdx.x + t_now.b;
+      const int64_t slot = (int64_t)split + t_now.b;
+      // O~ goes out through the wave's staged-query area (32 heads x 128
+      // latent columns of bf16 at a time, 16-byte chunk c of head row h at
+      // chunk position c ^ (h & 15)), so that each store covers 4 heads x 256
+      // contiguous bytes.  The area is reloaded with the next query below.
+      char* stg = ql + wave * 32 * QLB;
+      int ln = lane;   // hidden from loop-invariant hoisting (the addresses below stay local)
+      asm volatile("" : "+v"(ln));
+      const int wh = ln & 31;                                   // head row written by this lane
+      char* const wrow = stg + wh * 256 + (ln >> 5) * 8;
+      const int rh = ln >> 4, rc = ln & 15;                     // head (mod 4) and chunk read
 #pragma unroll
       for (int hb = 0; hb < NW; ++hb) {
-        const int head = 32 * hb + (lane & 31);
-        bf16* dst = part_o + (slot * NH + head) * D_C;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int dblk = DB * wave + db;
-          // accumulator row m = 8*r4 + 4*(lane>>5) + r%4 is latent column
-          // 8*(8g + p + 2*r4) + 4*(lane>>5) + r%4 of block dblk = 2g + p
-          const int d0 = 64 * (dblk >> 1) + 8 * (dblk & 1) + 4 * (lane >> 5);
+        for (int pc = 0; pc < PIECES; ++pc) {
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            float v0, v1, v2, v3;
-            ACC_READ(v0, o[hb][db][4 * r4]);
-            ACC_READ(v1, o[hb][db][4 * r4 + 1]);
-            ACC_READ(v2, o[hb][db][4 * r4 + 2]);
-            ACC_READ(v3, o[hb][db][4 * r4 + 3]);
-            bf16x4 v;
-            v[0] = (bf16)v0;
-            v[1] = (bf16)v1;
-            v[2] = (bf16)v2;
-            v[3] = (bf16)v3;
-            *(bf16x4*)(dst + d0 + 16 * r4) = v;
+          for (int dq = 0; dq < 4; ++dq) {
+            const int db = 4 * pc + dq;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              // accumulator row m = 8*r4 + 4*(lane>>5) + r%4 of block dblk = 2g + p is
+              // latent column 8*(8g + p + 2*r4) + 4*(lane>>5) + r%4: chunk
+              // 8*(dq>>1) + (dq&1) + 2*r4 of this 128-column piece, half lane>>5
+              float v0, v1, v2, v3;
+              ACC_READ(v0, o[hb][db][4 * r4]);
+              ACC_READ(v1, o[hb][db][4 * r4 + 1]);
+              ACC_READ(v2, o[hb][db][4 * r4 + 2]);
+              ACC_READ(v3, o[hb][db][4 * r4 + 3]);
+              bf16x4 v;
+              v[0] = (bf16)v0;
+              v[1] = (bf16)v1;
+              v[2] = (bf16)v2;
+              v[3] = (bf16)v3;
+              const int chunk = 8 * (dq >> 1) + (dq & 1) + 2 * r4;
+              *(bf16x4*)(wrow + ((chunk ^ (wh & 15)) << 4)) = v;
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int h = 4 * k + rh;
+            const bf16x8 v = *(const bf16x8*)(stg + h * 256 + ((rc ^ (h & 15)) << 4));
+            bf16* dst = part_o + (slot * NH + 32 * hb + h) * D_C + (D_C / NW) * wave + 128 * pc + 8 * rc;
+            *(bf16x8*)dst = v;
           }
         }
       }
@@ -483,9 +575,17 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       }
       m_ref[0] = m_ref[1] = -INFINITY;
       l_sum[0] = l_sum[1] = 0.f;
+      // the next segment accumulates from zero
+#pragma unroll
+      for (int hb = 0; hb < NW; ++hb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ACC_ZERO(o[hb][db][r]);
       // the next segment's query, loaded and waited for here (once per
       // segment) so that no query load is in flight during a later tile
       if (t_n1.n > 0) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // staged reads done before the copies overwrite the area
         load_q(t_n1.b);
         settle_q();
       }
@@ -512,8 +612,8 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                               const void* k_R, int64_t row_stride, int32_t num_pages,
                               const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
-                              int32_t n_splits, float* part_ml, void* part_o_v, int32_t* flags,
-                              hipStream_t s) {
+                              const int32_t* split_rec, int32_t n_splits, float* part_ml, void* part_o_v,
+                              int32_t* flags, hipStream_t s) {
   bf16* part_o = (bf16*)part_o_v;
   const int nw = d.n_h / 32;
   dim3 grid(n_splits);
@@ -521,17 +621,17 @@ hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, co
     case 1:
       decode_mfma_kernel<1><<<grid, 64, 0, s>>>((const bf16*)qabs, (const bf16*)c_KV, (const bf16*)k_R,
                                                row_stride, num_pages, page_table, max_pages, d.page_size,
-                                               prefix, B, n_splits, part_ml, part_o, flags);
+                                               prefix, split_rec, B, n_splits, part_ml, part_o, flags);
       break;
     case 2:
       decode_mfma_kernel<2><<<grid, 128, 0, s>>>((const bf16*)qabs, (const bf16*)c_KV, (const bf16*)k_R,
                                                 row_stride, num_pages, page_table, max_pages, d.page_size,
-                                                prefix, B, n_splits, part_ml, part_o, flags);
+                                                prefix, split_rec, B, n_splits, part_ml, part_o, flags);
       break;
     case 4:
       decode_mfma_kernel<4><<<grid, 256, 0, s>>>((const bf16*)qabs, (const bf16*)c_KV, (const bf16*)k_R,
                                                 row_stride, num_pages, page_table, max_pages, d.page_size,
-                                                prefix, B, n_splits, part_ml, part_o, flags);
+                                                prefix, split_rec, B, n_splits, part_ml, part_o, flags);
       break;
     default:
       return hipErrorInvalidValue;

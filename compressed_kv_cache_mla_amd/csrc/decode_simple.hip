@@ -2,6 +2,9 @@
 //
 // Plan: exclusive prefix sum of the clamped sequence lengths; the decode and
 // combine kernels derive their work split from it (split_begin / split_of).
+// It also records, for every split, the sequence holding its first token and
+// that sequence's global token range, so a decode workgroup starts without a
+// search.
 //
 // VALU decode: the same computation as the MFMA kernel ("DeepSeek-V2：在“大力出
 // 奇迹”的AI军备竞赛中，四两拨千斤", liang.world, ch.2 §1 per-head softmax
@@ -16,7 +19,8 @@ namespace mla {
 namespace {
 
 __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ seq_lens, int32_t B,
-                                                    int32_t max_tokens, int32_t* __restrict__ prefix,
+                                                    int32_t max_tokens, int32_t G, int32_t* __restrict__ prefix,
+                                                    int32_t* __restrict__ split_rec,
                                                     int32_t* __restrict__ flags) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
@@ -51,6 +55,27 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
     run += n;
   }
   if (tid == 1023) prefix[B] = part[1023];
+  // Split w starts at token P_w = floor(w N / G); P_w lies in sequence b iff
+  // prefix[b] <= P_w < prefix[b+1], i.e. ceil(prefix[b] G / N) <= w <
+  // ceil(prefix[b+1] G / N).  Each thread walks its own sequences' splits.
+  const int64_t N = part[1023];
+  if (N <= 0) return;
+  run = tid > 0 ? part[tid - 1] : 0;
+  for (int b = beg; b < end; ++b) {
+    int32_t n = seq_lens[b];
+    n = n < 1 ? 0 : (n > max_tokens ? max_tokens : n);
+    const int64_t lo = run, hi = (int64_t)run + n;
+    const int64_t w0 = (lo * G + N - 1) / N, w1 = (hi * G + N - 1) / N;
+    for (int64_t w = w0; w < w1; ++w) {
+      int4 r;
+      r.x = b;
+      r.y = (int32_t)lo;
+      r.z = (int32_t)hi;
+      r.w = 0;
+      *(int4*)(split_rec + 4 * w) = r;
+    }
+    run += n;
+  }
 }
 
 template <typename T>
@@ -144,9 +169,9 @@ __global__ void __launch_bounds__(256) decode_simple_kernel(
 
 }  // namespace
 
-hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_tokens, int32_t* prefix, int32_t* flags,
-                       hipStream_t s) {
-  plan_kernel<<<1, 1024, 0, s>>>(seq_lens, B, max_tokens, prefix, flags);
+hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_tokens, int32_t n_splits, int32_t* prefix,
+                       int32_t* split_rec, int32_t* flags, hipStream_t s) {
+  plan_kernel<<<1, 1024, 0, s>>>(seq_lens, B, max_tokens, n_splits, prefix, split_rec, flags);
   return hipGetLastError();
 }
 

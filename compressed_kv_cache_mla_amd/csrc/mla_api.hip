@@ -140,13 +140,14 @@ mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const
   char* ws = (char*)workspace;
   int32_t* flags = (int32_t*)(ws + L.flags);
   int32_t* prefix = (int32_t*)(ws + L.prefix);
+  int32_t* split_rec = (int32_t*)(ws + L.splits);
   void* qabs = ws + L.qabs;
   float* part_ml = (float*)(ws + L.part_ml);
   void* part_o = ws + L.part_o;
   hipStream_t s = (hipStream_t)stream;
   const int32_t max_tokens = max_pages * dims->page_size;
 
-  hipError_t e = mla::launch_plan(seq_lens, B, max_tokens, prefix, flags, s);
+  hipError_t e = mla::launch_plan(seq_lens, B, max_tokens, n_splits, prefix, split_rec, flags, s);
   if (e == hipSuccess) e = mla::launch_absorb(*dims, B, q_C, q_R, pos_q, W_UK, qabs, s);
   if (opts && opts->impl != 0 && opts->impl != 1) return fail(MLA_ERR_INVALID_ARG, "opts->impl=%d", opts->impl);
   if (e == hipSuccess && opts && opts->ev_start) e = hipEventRecord((hipEvent_t)opts->ev_start, s);
@@ -155,7 +156,7 @@ mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const
                       dims->page_size >= 32 && !(opts && opts->impl == 1);
     if (mfma)
       e = mla::launch_decode_mfma(*dims, B, qabs, c_KV, k_R, row_stride, num_pages, page_table, max_pages, prefix,
-                                  n_splits, part_ml, part_o, flags, s);
+                                  split_rec, n_splits, part_ml, part_o, flags, s);
     else
       e = mla::launch_decode_simple(*dims, B, qabs, c_KV, k_R, row_stride, num_pages, page_table, max_pages,
                                     prefix, n_splits, part_ml, part_o, flags, s);

@@ -54,7 +54,7 @@ __device__ __forceinline__ void rope_cos_sin(int32_t pos, int k, int d, float ba
 
 // Decode workspace layout (bytes, each part 256-aligned).
 struct DecodeWs {
-  size_t flags, prefix, qabs, part_ml, part_o, total;
+  size_t flags, prefix, splits, qabs, part_ml, part_o, total;
   int32_t n_slots;
 };
 
@@ -66,6 +66,7 @@ inline DecodeWs decode_ws_layout(int32_t B, int32_t n_h, int32_t n_splits, int e
   size_t off = 0;
   w.flags = off;   off += 256;
   w.prefix = off;  off += align256((size_t)(B + 1) * 4);
+  w.splits = off;  off += align256((size_t)n_splits * 16);               // per split: {b, s_beg, s_end, 0}
   w.qabs = off;    off += align256((size_t)B * n_h * D_K * elt);
   w.part_ml = off; off += align256((size_t)w.n_slots * n_h * 2 * 4);
   w.part_o = off;  off += align256((size_t)w.n_slots * n_h * D_C * elt);   // partial O~ in the cache type
@@ -101,8 +102,8 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
                          const int32_t* seq_id, const int32_t* pos, const int32_t* page_table,
                          int32_t num_seqs, int32_t max_pages, void* c_KV, void* k_R, int64_t row_stride,
                          int32_t num_pages, int32_t* err_flag, hipStream_t s);
-hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_tokens, int32_t* prefix, int32_t* flags,
-                       hipStream_t s);
+hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_tokens, int32_t n_splits, int32_t* prefix,
+                       int32_t* split_rec, int32_t* flags, hipStream_t s);
 hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
                          const void* W_UK, void* qabs, hipStream_t s);
 hipError_t launch_decode_simple(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
@@ -113,8 +114,8 @@ hipError_t launch_decode_simple(const mla_dims& d, int32_t B, const void* qabs, 
 hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                               const void* k_R, int64_t row_stride, int32_t num_pages,
                               const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
-                              int32_t n_splits, float* part_ml, void* part_o, int32_t* flags,
-                              hipStream_t s);
+                              const int32_t* split_rec, int32_t n_splits, float* part_ml, void* part_o,
+                              int32_t* flags, hipStream_t s);
 hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, int32_t n_splits,
                           const float* part_ml, const void* part_o, const void* W_UV, float* out,
                           float* lse, hipStream_t s);
