@@ -97,12 +97,17 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b32_l4096")
+    ap.add_argument("--target-workload", default="b64_l8192",
+                    help="second workload reported under target_shape ('' to skip)")
     ap.add_argument("--copies", type=int, default=0, help="workload copies to rotate over (0 = enough to exceed "
                                                          "the 256 MB Infinity Cache twice)")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--impl", type=int, default=0, help="0 = MFMA attention kernel, 1 = VALU reference kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM "
+                         "byte counters of rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not part of it "
@@ -110,53 +115,65 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = 1 << 30
+        x = torch.full((n,), 1, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+        return
     import workloads as W
+    import compressed_kv_cache_mla_amd as mla
 
-    cfg = W.CONFIGS[args.workload]
-    if cfg.layers > 1:
-        cfg = W.scaled(cfg, layers=1)
-    t_build = time.perf_counter()
-    first = W.Workload(cfg, layer=0, n_splits=args.splits)
-    alg = algorithmic(first)
-    per_copy = alg["step_bytes"] + first.workspace.numel()
-    copies = args.copies or max(2, math.ceil(2 * 256e6 / per_copy))
-    wls = [first] + [W.Workload(cfg, layer=i, n_splits=args.splits) for i in range(1, copies)]
-    torch.cuda.synchronize()
-    print(f"# built {copies} copies of {cfg.name} in {time.perf_counter() - t_build:.1f} s "
-          f"({per_copy / 1e6:.0f} MB each)", file=sys.stderr, flush=True)
+    def measure(name, steps, warmup):
+        """Build rotating copies of a workload, run warmup + timed steps;
+        returns (first workload, copies, ms per step, attention-kernel us, wall s)."""
+        cfg = W.CONFIGS[name]
+        if cfg.layers > 1:
+            cfg = W.scaled(cfg, layers=1)
+        t_build = time.perf_counter()
+        first = W.Workload(cfg, layer=0, n_splits=args.splits)
+        alg = algorithmic(first)
+        per_copy = alg["step_bytes"] + first.workspace.numel()
+        copies = args.copies or max(2, math.ceil(2 * 256e6 / per_copy))
+        wls = [first] + [W.Workload(cfg, layer=i, n_splits=args.splits) for i in range(1, copies)]
+        torch.cuda.synchronize()
+        print(f"# built {copies} copies of {cfg.name} in {time.perf_counter() - t_build:.1f} s "
+              f"({per_copy / 1e6:.0f} MB each)", file=sys.stderr, flush=True)
 
-    def step(i, evs=None):
-        wl = wls[i % copies]
-        wl.append_step()
-        if evs is None:
-            wl.decode(impl=args.impl)
-        else:
-            wl.decode(ev_start=evs[0], ev_stop=evs[1], impl=args.impl)
+        def step(i, evs=None):
+            wl = wls[i % copies]
+            wl.append_step()
+            if evs is None:
+                wl.decode(impl=args.impl)
+            else:
+                wl.decode(ev_start=evs[0], ev_stop=evs[1], impl=args.impl)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in kev:        # create the HIP events before the timed region
-        a.record()
-        b.record()
-    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        step(i, kev[i])
-    t_stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    total_ms = t_start.elapsed_time(t_stop)
-    kern_ms = [a.elapsed_time(b) for a, b in kev]
-    kern_avg = sum(kern_ms) / len(kern_ms)
-    ms_per_step = total_ms / args.steps
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        # attention-kernel events: HIP events without the system-scope fence,
+        # recorded on the decode stream by mla_decode_ex around that kernel
+        kev = [(mla.HipEvent(), mla.HipEvent()) for _ in range(steps)]
+        t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        t_start.record()
+        for i in range(steps):
+            step(i, kev[i])
+        t_stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        kern_ms = [a.elapsed_ms(b) for a, b in kev]
+        return first, alg, copies, t_start.elapsed_time(t_stop) / steps, 1e3 * sum(kern_ms) / len(kern_ms), wall
+
+    first, alg, copies, ms_per_step, kern_us, wall = measure(args.workload, args.steps, args.warmup)
+    cfg = first.cfg
     B = cfg.B
     value = B / (ms_per_step * 1e-3)
-
-    achieved = alg["attn_bytes"] / (kern_avg * 1e-3) / 1e9
+    achieved = alg["attn_bytes"] / (kern_us * 1e-6) / 1e9
     traffic = None
     if os.path.exists(COUNTERS):
         cnt = json.load(open(COUNTERS))
@@ -174,14 +191,23 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "split-KV attention (decode_mfma_kernel)" if args.impl == 0 else "decode_simple_kernel",
-                     "kernel_us": round(kern_avg * 1e3, 2),
-                     "mfma_tflops": round(alg["attn_flops"] / (kern_avg * 1e-3) / 1e12, 1),
-                     "mfma_frac": round(alg["attn_flops"] / (kern_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                     "kernel_us": round(kern_us, 2),
+                     "mfma_tflops": round(alg["attn_flops"] / (kern_us * 1e-6) / 1e12, 1),
+                     "mfma_frac": round(alg["attn_flops"] / (kern_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "latent_cache_GBps": round(alg["cache"] / (ms_per_step * 1e-3) / 1e9, 1),
         "step_GBps": round(alg["step_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(alg["step_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "wall_s_timed": round(wall, 4),
     }
+    if args.target_workload and args.target_workload != args.workload:
+        # the batch-64 / 8K-context decode shape the performance target is stated on
+        f2, a2, c2, ms2, k2, _ = measure(args.target_workload, max(5, args.steps // 2), args.warmup)
+        res["target_shape"] = {
+            "workload": f2.cfg.name, "B": f2.cfg.B, "cached_tokens": a2["N"], "ms_per_step": round(ms2, 5),
+            "tokens_per_s": round(f2.cfg.B / (ms2 * 1e-3), 1), "kernel_us": round(k2, 2),
+            "hbm_frac": round(a2["attn_bytes"] / (k2 * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "mfma_frac": round(a2["attn_flops"] / (k2 * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "copies_rotated": c2}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
     print(json.dumps(res), flush=True)

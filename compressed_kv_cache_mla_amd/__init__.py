@@ -135,9 +135,43 @@ def decode_workspace_size(dims: Dims, B: int, n_splits: int = 0) -> int:
     return int(lib().mla_decode_workspace_size(ctypes.byref(d), B, n_splits))
 
 
+class HipEvent:
+    """A HIP timing event created with hipEventDisableSystemFence: recording it
+    between two kernels adds no system-scope release (cache write-back), so it
+    can bracket one kernel without stretching the step.  Uses the HIP runtime
+    that torch (and libmla.so) already loaded."""
+    _hip = None
+
+    def __init__(self):
+        if HipEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._hip = hip
+        self.handle = ctypes.c_void_p()
+        st = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.handle), ctypes.c_uint(0x20000000))
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        st = HipEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return float(ms.value)
+
+    def __del__(self):
+        if self.handle and HipEvent._hip is not None:
+            HipEvent._hip.hipEventDestroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+
 def _event_handle(ev):
     if ev is None:
         return None
+    if isinstance(ev, HipEvent):
+        return ev.handle
     if not ev.cuda_event:      # torch creates the HIP event on its first record
         ev.record()
     return ctypes.c_void_p(ev.cuda_event)
@@ -148,8 +182,8 @@ def decode(dims: Dims, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride: int, 
            impl: int = 0):
     """mla_decode (mla_decode_ex when events or impl are given): one query per
     sequence against its cached latent rows; writes out [B, n_h, d_h] (fp32)
-    and optionally lse [B, n_h].  ev_start / ev_stop (torch.cuda.Event) are
-    recorded around the split-KV attention kernel."""
+    and optionally lse [B, n_h].  ev_start / ev_stop (HipEvent or
+    torch.cuda.Event) are recorded around the split-KV attention kernel."""
     B = q_C.shape[0]
     max_pages = page_table.shape[1]
     if workspace is None:
