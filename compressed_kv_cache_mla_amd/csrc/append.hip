@@ -173,46 +173,56 @@ __global__ void __launch_bounds__(256) append_bf16_kernel(
 
 // Few tokens (a decode step): the product is weight-bandwidth bound, so the
 // grid is spread over output columns.  Workgroup = 16 tokens x 16 output
-// columns; its 4 waves split d_model into quarters (v_mfma_f32_16x16x32_bf16,
-// operands straight from global memory) and the quarter sums are added in LDS.
-__global__ void __launch_bounds__(256) append_bf16_small_kernel(
+// columns, 16 waves; wave w takes the w-th sixteenth of d_model and issues all
+// of its operand loads (v_mfma_f32_16x16x32_bf16 fragments straight from
+// global memory, up to SMALL_KB K-steps per batch) before its MFMAs, so one
+// memory latency covers its slice; the 16 partial sums are added in LDS.
+constexpr int SMALL_W = 16;
+constexpr int SMALL_KB = 10;
+
+__global__ void __launch_bounds__(64 * SMALL_W) append_bf16_small_kernel(
     int32_t T_rows, int32_t d_model, const bf16* __restrict__ h, const bf16* __restrict__ W_DKV,
     const bf16* __restrict__ W_KR, const int32_t* __restrict__ seq_id, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ page_table, int32_t num_seqs, int32_t max_pages, int32_t page_size,
     bf16* __restrict__ c_KV, bf16* __restrict__ k_R, int64_t row_stride, int32_t num_pages, float rope_base,
     int32_t* err_flag) {
-  __shared__ float red[4][16][17];
+  __shared__ float red[SMALL_W][16][17];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int tok0 = blockIdx.x * 16;
   const int col0 = blockIdx.y * 16;
   const bf16* W = col0 < D_C ? W_DKV + (int64_t)col0 * d_model : W_KR + (int64_t)(col0 - D_C) * d_model;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int kq4 = d_model / 4;                     // K range of this wave
-  const bf16* wrow = W + (int64_t)r16 * d_model + wave * kq4 + kq;
-  const bf16* hrow = h + (int64_t)min(tok0 + r16, T_rows - 1) * d_model + wave * kq4 + kq;
-  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-  int k = 0;
-  for (; k + 64 <= kq4; k += 64) {
-    const bf16x8 w0 = *(const bf16x8*)(wrow + k), w1 = *(const bf16x8*)(wrow + k + 32);
-    const bf16x8 a0 = *(const bf16x8*)(hrow + k), a1 = *(const bf16x8*)(hrow + k + 32);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, w0, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, w1, acc1, 0, 0, 0);
-  }
-  for (; k < kq4; k += 32) {
-    const bf16x8 w0 = *(const bf16x8*)(wrow + k);
-    const bf16x8 a0 = *(const bf16x8*)(hrow + k);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, w0, acc0, 0, 0, 0);
+  const int kw = d_model / SMALL_W;                // K range of this wave (a multiple of 32)
+  const int nks = kw / 32;
+  const bf16* wrow = W + (int64_t)r16 * d_model + wave * kw + kq;
+  const bf16* hrow = h + (int64_t)min(tok0 + r16, T_rows - 1) * d_model + wave * kw + kq;
+  f32x4 acc = {0, 0, 0, 0};
+  for (int k0 = 0; k0 < nks; k0 += SMALL_KB) {
+    bf16x8 wv[SMALL_KB], hv[SMALL_KB];
+#pragma unroll
+    for (int i = 0; i < SMALL_KB; ++i)
+      if (k0 + i < nks) {
+        wv[i] = *(const bf16x8*)(wrow + 32 * (k0 + i));
+        hv[i] = *(const bf16x8*)(hrow + 32 * (k0 + i));
+      }
+#pragma unroll
+    for (int i = 0; i < SMALL_KB; ++i)
+      if (k0 + i < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv[i], wv[i], acc, 0, 0, 0);
   }
   // C layout: lane holds output column lane%16, tokens 4*(lane/16) + i
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][r16] = acc0[i] + acc1[i];
+  for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][r16] = acc[i];
   __syncthreads();
   if (tid < 128) {
     const int r = tid >> 3, cp = tid & 7;          // token row, column pair
     const int t = tok0 + r;
     if (t < T_rows) {
-      float x0 = red[0][r][2 * cp] + red[1][r][2 * cp] + red[2][r][2 * cp] + red[3][r][2 * cp];
-      float x1 = red[0][r][2 * cp + 1] + red[1][r][2 * cp + 1] + red[2][r][2 * cp + 1] + red[3][r][2 * cp + 1];
+      float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < SMALL_W; ++w) {
+        x0 += red[w][r][2 * cp];
+        x1 += red[w][r][2 * cp + 1];
+      }
       const int32_t sq = seq_id ? seq_id[t] : t;
       const int32_t p = pos[t];
       if (sq < 0 || sq >= num_seqs) {
@@ -252,9 +262,9 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
                                           (const float*)W_KR, seq_id, pos, page_table, num_seqs, max_pages,
                                           d.page_size, (float*)c_KV, (float*)k_R, row_stride, num_pages,
                                           d.rope_base, err_flag);
-  } else if (T <= 512 && d.d_model % 128 == 0) {
+  } else if (T <= 512 && d.d_model % (32 * SMALL_W) == 0) {
     dim3 g2((T + 15) / 16, D_K / 16);
-    append_bf16_small_kernel<<<g2, 256, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV,
+    append_bf16_small_kernel<<<g2, 64 * SMALL_W, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV,
                                                  (const bf16*)W_KR, seq_id, pos, page_table, num_seqs, max_pages,
                                                  d.page_size, (bf16*)c_KV, (bf16*)k_R, row_stride, num_pages,
                                                  d.rope_base, err_flag);

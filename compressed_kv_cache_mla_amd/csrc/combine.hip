@@ -11,10 +11,9 @@
 //
 // fp32 (VALU): workgroup (head h, 32 sequences); combined latents in LDS,
 // each thread one output column for 16 sequences.
-// bf16 (MFMA): workgroup (head h, 64 sequences); the combined latents are
+// bf16 (MFMA): workgroup (head h, 16 sequences); the combined latents are
 // rounded to bf16 in LDS and o^T[d][b] = W^UV_h[d][:] . O~[b][:] runs as
-// v_mfma_f32_32x32x16_bf16 (M = d, N = sequence, K = latent column), with
-// W^UV rows read straight from global memory in the MFMA lane layout.
+// v_mfma_f32_16x16x32_bf16 (M = d, N = sequence, K = latent column).
 #include "mla_common.h"
 
 namespace mla {
@@ -108,75 +107,118 @@ __global__ void __launch_bounds__(256) combine_f32_kernel(int32_t B, int32_t n_h
   }
 }
 
-// bf16: combined latents in LDS as [64 sequences][512] bf16 with 16-byte chunk
-// c16 of sequence b at chunk c16 ^ (b & 15) (conflict-free column reads).
+// bf16: workgroup (head h, CS = 16 sequences).  Each wave merges four
+// sequences: the per-slot weights 2^(m_s - m*) / L are formed lane-parallel
+// over the slots (lane j holds slot j's weight), then every lane sums 8 latent
+// columns over the slots, four slots' loads in flight at a time.  The merged
+// latents go to LDS as bf16 [16][512] (16-byte chunk c of sequence b at chunk
+// c ^ b: conflict-free fragment reads), and o^T[d][b] = W^UV_h[d][:] . O~[b][:]
+// runs as v_mfma_f32_16x16x32_bf16 (wave w: d = 32w .. 32w+31), W^UV rows read
+// straight from global memory in the A-fragment layout.
+constexpr int CS = 16;
+
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 __global__ void __launch_bounds__(256) combine_mfma_kernel(int32_t B, int32_t n_h, const int32_t* __restrict__ prefix,
                                                            int32_t G, const float* __restrict__ part_ml,
                                                            const bf16* __restrict__ part_o,
                                                            const bf16* __restrict__ W_UV, float* __restrict__ out,
                                                            float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) char ol[64 * D_C * 2];
-  __shared__ MergeInfo info[64];
+  __shared__ __attribute__((aligned(16))) char ol[CS * D_C * 2];
+  __shared__ int empty_l[CS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.x;
-  const int b0 = blockIdx.y * 64;
-  const int nb = min(64, B - b0);
+  const int b0 = blockIdx.y * CS;
+  const int nb = min(CS, B - b0);
   const int64_t N = prefix[B];
-  if (tid < nb) info[tid] = merge_info(b0 + tid, h, n_h, N, G, prefix, part_ml, lse);
-  __syncthreads();
-  // combine: wave w merges sequences w, w+4, ...; lane owns latent columns 8*lane .. 8*lane+7
-  for (int bb = wave; bb < 64; bb += 4) {
+  for (int bb = wave; bb < CS; bb += 4) {
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int empty = 1;
     if (bb < nb) {
       const int b = b0 + bb;
-      const MergeInfo mi = info[bb];
-      for (int i = 0; i < mi.count; ++i) {
-        const int64_t slot = mi.wfirst + i + b;
-        const bf16x8 v = *(const bf16x8*)(part_o + (slot * n_h + h) * D_C + 8 * lane);
-        const float wgt = exp2f(part_ml[(slot * n_h + h) * 2] - mi.mstar) * mi.invL;
+      const int64_t sb = prefix[b], n = prefix[b + 1] - sb;
+      if (n <= 0 && lse && lane == 0) lse[(int64_t)b * n_h + h] = -INFINITY;
+      if (n > 0) {
+        empty = 0;
+        const int64_t w0 = split_of(sb, N, G), w1 = split_of(sb + n - 1, N, G);
+        const int cnt = (int)(w1 - w0 + 1);
+        const float* ml = part_ml + ((w0 + b) * n_h + h) * 2;   // slot w0 + b + i at ml + 2*n_h*i
+        float mx = -INFINITY;
+        for (int i = lane; i < cnt; i += 64) mx = fmaxf(mx, ml[(int64_t)i * 2 * n_h]);
+        mx = wave_max64(mx);
+        float L = 0.f;
+        for (int i = lane; i < cnt; i += 64) L += exp2f(ml[(int64_t)i * 2 * n_h] - mx) * ml[(int64_t)i * 2 * n_h + 1];
+        L = wave_sum64(L);
+        const float invL = 1.f / L;
+        if (lse && lane == 0) lse[(int64_t)b * n_h + h] = (mx + log2f(L)) * 0.69314718055994531f;
+        const bf16* po = part_o + ((w0 + b) * n_h + h) * D_C + 8 * lane;   // slot i at po + n_h*D_C*i
+        const int64_t sstride = (int64_t)n_h * D_C;
+        for (int i0 = 0; i0 < cnt; i0 += 64) {
+          const int m = min(64, cnt - i0);
+          const float wl = lane < m ? exp2f(ml[(int64_t)(i0 + lane) * 2 * n_h] - mx) * invL : 0.f;
+          int i = 0;
+          for (; i + 4 <= m; i += 4) {
+            bf16x8 v[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) a[k] = fmaf(wgt, (float)v[k], a[k]);
+            for (int u = 0; u < 4; ++u) v[u] = *(const bf16x8*)(po + sstride * (i0 + i + u));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float wg = __shfl(wl, i + u);
+#pragma unroll
+              for (int k = 0; k < 8; ++k) a[k] = fmaf(wg, (float)v[u][k], a[k]);
+            }
+          }
+          for (; i < m; ++i) {
+            const bf16x8 v = *(const bf16x8*)(po + sstride * (i0 + i));
+            const float wg = __shfl(wl, i);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) a[k] = fmaf(wg, (float)v[k], a[k]);
+          }
+        }
       }
     }
     bf16x8 r;
 #pragma unroll
     for (int k = 0; k < 8; ++k) r[k] = (bf16)a[k];
-    *(bf16x8*)(ol + bb * 1024 + ((lane ^ (bb & 15)) << 4)) = r;
+    *(bf16x8*)(ol + bb * 1024 + ((lane ^ bb) << 4)) = r;
+    if (lane == 0) empty_l[bb] = empty;
   }
   __syncthreads();
-  // o^T[d][b]: wave w owns d = 32w .. 32w+31, both 32-sequence blocks
-  f32x16 acc0, acc1;
+  // o^T[d][b]: A = W^UV rows d (16 x 32 per MFMA), B = O~^T (32 latent columns x 16 sequences)
+  f32x4 acc[2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    acc0[r] = 0.f;
-    acc1[r] = 0.f;
+  for (int mb = 0; mb < 2; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16* wr = W_UV + ((int64_t)h * D_H + 32 * wave + (lane & 15)) * D_C + 8 * (lane >> 4);
+  const int bq = lane & 15;
+#pragma unroll 4
+  for (int ks = 0; ks < D_C / 32; ++ks) {
+    const int c16 = 4 * ks + (lane >> 4);
+    const bf16x8 bfr = *(const bf16x8*)(ol + bq * 1024 + ((c16 ^ bq) << 4));
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const bf16x8 afr = *(const bf16x8*)(wr + (int64_t)16 * mb * D_C + 32 * ks);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc[mb], 0, 0, 0);
+    }
   }
-  const bf16* wr = W_UV + ((int64_t)h * D_H + 32 * wave + (lane & 31)) * D_C + 8 * (lane >> 5);
-  const int bq0 = lane & 31, bq1 = 32 + (lane & 31);
-#pragma unroll 8
-  for (int ks = 0; ks < 32; ++ks) {
-    const bf16x8 a = *(const bf16x8*)(wr + 16 * ks);
-    const int c16 = 2 * ks + (lane >> 5);
-    const bf16x8 q0 = *(const bf16x8*)(ol + bq0 * 1024 + ((c16 ^ (bq0 & 15)) << 4));
-    const bf16x8 q1 = *(const bf16x8*)(ol + bq1 * 1024 + ((c16 ^ (bq1 & 15)) << 4));
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q0, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q1, acc1, 0, 0, 0);
-  }
-  // C layout: lane -> sequence (lane & 31) of the block, rows d = (r/4)*8 + 4*(lane>>5) + r%4
+  // C layout: lane holds d = 16mb + 4*(lane>>4) + i (of this wave's 32), sequence lane & 15
+  if (bq < nb) {
+    const bool empty = empty_l[bq] != 0;
+    float* dst = out + ((int64_t)(b0 + bq) * n_h + h) * D_H + 32 * wave + 4 * (lane >> 4);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int bb = 32 * j + (lane & 31);
-    if (bb < nb) {
-      const bool empty = info[bb].count == 0;
-      float* dst = out + ((int64_t)(b0 + bb) * n_h + h) * D_H + 32 * wave + 4 * (lane >> 5);
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x16& acc = j ? acc1 : acc0;
-        f32x4 v = {acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
-        if (empty) v = f32x4{0.f, 0.f, 0.f, 0.f};
-        *(f32x4*)(dst + 8 * r4) = v;
-      }
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x4 v = acc[mb];
+      if (empty) v = f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)(dst + 16 * mb) = v;
     }
   }
 }
@@ -191,7 +233,7 @@ hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, i
     combine_f32_kernel<<<grid, 256, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const float*)part_o,
                                             (const float*)W_UV, out, lse);
   } else {
-    dim3 grid(d.n_h, (B + 63) / 64);
+    dim3 grid(d.n_h, (B + CS - 1) / CS);
     combine_mfma_kernel<<<grid, 256, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
                                              (const bf16*)W_UV, out, lse);
   }

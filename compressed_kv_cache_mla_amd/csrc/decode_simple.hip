@@ -23,59 +23,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ split_rec,
                                                     int32_t* __restrict__ flags) {
   __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
-  // the flags describe the latest decode on this workspace
-  if (tid == 0) flags[0] = 0;
-  __syncthreads();
-  const int per = (B + 1023) / 1024;
-  const int beg = tid * per, end = min(beg + per, B);
-  int32_t local = 0;
-  for (int b = beg; b < end; ++b) {
-    int32_t n = seq_lens[b];
-    if (n < 1 || n > max_tokens) {
-      atomicOr(flags, MLA_FLAG_BAD_SEQ_LEN);
-      n = n < 1 ? 0 : max_tokens;
-    }
-    local += n;
-  }
-  part[tid] = local;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 thread totals
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int32_t run = tid > 0 ? part[tid - 1] : 0;
-  for (int b = beg; b < end; ++b) {
-    prefix[b] = run;
-    int32_t n = seq_lens[b];
-    n = n < 1 ? 0 : (n > max_tokens ? max_tokens : n);
-    run += n;
-  }
-  if (tid == 1023) prefix[B] = part[1023];
-  // Split w starts at token P_w = floor(w N / G); P_w lies in sequence b iff
-  // prefix[b] <= P_w < prefix[b+1], i.e. ceil(prefix[b] G / N) <= w <
-  // ceil(prefix[b+1] G / N).  Each thread walks its own sequences' splits.
-  const int64_t N = part[1023];
-  if (N <= 0) return;
-  run = tid > 0 ? part[tid - 1] : 0;
-  for (int b = beg; b < end; ++b) {
-    int32_t n = seq_lens[b];
-    n = n < 1 ? 0 : (n > max_tokens ? max_tokens : n);
-    const int64_t lo = run, hi = (int64_t)run + n;
-    const int64_t w0 = (lo * G + N - 1) / N, w1 = (hi * G + N - 1) / N;
-    for (int64_t w = w0; w < w1; ++w) {
-      int4 r;
-      r.x = b;
-      r.y = (int32_t)lo;
-      r.z = (int32_t)hi;
-      r.w = 0;
-      *(int4*)(split_rec + 4 * w) = r;
-    }
-    run += n;
-  }
+  plan_block<1024>(seq_lens, B, max_tokens, G, prefix, split_rec, flags, part);
 }
 
 template <typename T>

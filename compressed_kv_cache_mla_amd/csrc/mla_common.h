@@ -94,6 +94,61 @@ __device__ __forceinline__ int32_t seq_of(const int32_t* __restrict__ prefix, in
   return lo;
 }
 
+// Decode plan, run by one workgroup of NT threads (part: NT ints of LDS):
+// clears the error flags, writes prefix[0..B] = exclusive sum of the clamped
+// sequence lengths, and for every split w the record {b, prefix[b],
+// prefix[b+1], 0} of the sequence holding its first token P_w = floor(w N / G).
+// P_w lies in sequence b iff prefix[b] <= P_w < prefix[b+1], i.e. iff
+// ceil(prefix[b] G / N) <= w < ceil(prefix[b+1] G / N); each thread walks the
+// splits of its own sequences.
+template <int NT>
+__device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens, int32_t B, int32_t max_tokens,
+                                           int32_t G, int32_t* __restrict__ prefix, int32_t* __restrict__ split_rec,
+                                           int32_t* __restrict__ flags, int32_t* part) {
+  const int tid = threadIdx.x;
+  if (tid == 0) flags[0] = 0;   // the flags describe the latest decode on this workspace
+  __syncthreads();
+  const int per = (B + NT - 1) / NT;
+  const int beg = tid * per, end = min(beg + per, B);
+  int32_t local = 0;
+  for (int b = beg; b < end; ++b) {
+    int32_t n = seq_lens[b];
+    if (n < 1 || n > max_tokens) {
+      atomicOr(flags, MLA_FLAG_BAD_SEQ_LEN);
+      n = n < 1 ? 0 : max_tokens;
+    }
+    local += n;
+  }
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {   // Hillis-Steele inclusive scan of the thread totals
+    const int32_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const int64_t N = part[NT - 1];
+  int32_t run = tid > 0 ? part[tid - 1] : 0;
+  for (int b = beg; b < end; ++b) {
+    int32_t n = seq_lens[b];
+    n = n < 1 ? 0 : (n > max_tokens ? max_tokens : n);
+    prefix[b] = run;
+    if (N > 0) {
+      const int64_t lo = run, hi = (int64_t)run + n;
+      for (int64_t w = (lo * G + N - 1) / N; w < (hi * G + N - 1) / N; ++w) {
+        int4 r;
+        r.x = b;
+        r.y = (int32_t)lo;
+        r.z = (int32_t)hi;
+        r.w = 0;
+        *(int4*)(split_rec + 4 * w) = r;
+      }
+    }
+    run += n;
+  }
+  if (tid == NT - 1) prefix[B] = part[NT - 1];
+}
+
 }  // namespace mla
 
 // Launchers (host side), one per kernel family.
@@ -104,8 +159,11 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
                          int32_t num_pages, int32_t* err_flag, hipStream_t s);
 hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_tokens, int32_t n_splits, int32_t* prefix,
                        int32_t* split_rec, int32_t* flags, hipStream_t s);
+// Query absorption; for bf16 the decode plan runs in the same launch (then
+// launch_plan is not called).
 hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
-                         const void* W_UK, void* qabs, hipStream_t s);
+                         const void* W_UK, void* qabs, const int32_t* seq_lens, int32_t max_tokens,
+                         int32_t n_splits, int32_t* prefix, int32_t* split_rec, int32_t* flags, hipStream_t s);
 hipError_t launch_decode_simple(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                                 const void* k_R, int64_t row_stride, int32_t num_pages,
                                 const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
