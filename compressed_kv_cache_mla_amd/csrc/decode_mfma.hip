@@ -292,29 +292,38 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   const int64_t stride_b = row_stride * 2;
   // Copy of a tile: wave w fetches row groups w, w + NW, ...; in row group g
   // lane l fetches row 8g + m, m = (l>>3) ^ (g&1), and chunk 8j + ((l&7) ^
-  // sw(m)) of it for the 9 lines j (line 8 is k^R).  The per-lane addresses
-  // are formed here from the scalar bases, not kept live across the loop.
-  auto issue_dma = [&](char* kt, const TileDesc& td, int32_t pg0, int32_t pg1) {
+  // sw(m)) of it for the 9 lines j (line 8 is k^R), into window 9g + j.
+  // dma_src() forms a lane's source offset for the wave's gi-th row group
+  // from the scalar bases (nothing is kept live across the loop); copy
+  // instruction I = 9*gi + j of the wave is issued by dma_one().
+  auto dma_src = [&](const TileDesc& td, int gi, int32_t pg0, int32_t pg1) -> int64_t {
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const uint32_t lbase = lds_addr(kt);
+    const int g = wave + NW * gi;
+    const int m = (ln >> 3) ^ (g & 1);
+    const int64_t row = resolve_row(td, 8 * g + m, pg0, pg1);
+    return row * stride_b + 16 * ((ln & 7) ^ swz(m));
+  };
+  auto dma_one = [&](char* kt, int I, int64_t off) {
+    const int gi = I / 9, j = I % 9, g = wave + NW * gi;
+    const char* src = j < 8 ? (const char*)c_KV + off + 128 * j : (const char*)k_R + off;
+    dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(kt) + (9 * g + j) * 1024));
+  };
+  auto issue_dma = [&](char* kt, const TileDesc& td, int32_t pg0, int32_t pg1) {
 #pragma unroll
     for (int gi = 0; gi < 4 / NW; ++gi) {
-      const int g = wave + NW * gi;
-      const int m = (ln >> 3) ^ (g & 1);
-      const int64_t row = resolve_row(td, 8 * g + m, pg0, pg1);
-      const int64_t off = row * stride_b + 16 * ((ln & 7) ^ swz(m));
-      const char* cb = (const char*)c_KV + off;
-      const char* kb = (const char*)k_R + off;
+      const int64_t off = dma_src(td, gi, pg0, pg1);
 #pragma unroll
-      for (int j = 0; j < 9; ++j)
-        dma16(j < 8 ? cb + 128 * j : kb, __builtin_amdgcn_readfirstlane(lbase + (9 * g + j) * 1024));
+      for (int j = 0; j < 9; ++j) dma_one(kt, 9 * gi + j, off);
     }
   };
 
   // ---- state
   bf16x8 q[2][KS_REG];
   f32x16 o[NW][DB];
+  // Softmax state of the lane's heads 32w + 16hb + (lane&15): the reference
+  // max (the same in the four lanes that hold a head) and this lane's part of
+  // the sum (its tokens only; the four parts are added when the segment ends).
   float m_ref[2], l_sum[2];
 
   auto load_q = [&](int32_t b) {
@@ -377,9 +386,14 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
     // page ids of t_n3 (its buffer is kt) before the copy of t_n2, so that
     // next iteration's wait covers them
     issue_page_ids(kt, t_n3);
-    if (t_n2.n > 0) {
+    // t_n2's copy instructions are spread over the score K-steps below, so
+    // that the four waves do not queue them all at once
+    const bool copy = t_n2.n > 0;
+    int64_t doff[4 / NW];
+    {
       const int2 pg = *(const int2*)(kt_issue + PGOFF);
-      issue_dma(kt_issue, t_n2, pg.x, pg.y);
+#pragma unroll
+      for (int gi = 0; gi < 4 / NW; ++gi) doff[gi] = copy ? dma_src(t_n2, gi, pg.x, pg.y) : 0;
     }
 
     // ---- scores S^T[token][head] for this wave's 32 heads (2 x 2 blocks of 16x16)
@@ -415,36 +429,59 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
         s[tb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st][tb], qb0, s[tb][0], 0, 0, 0);
         s[tb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st][tb], qb1, s[tb][1], 0, 0, 0);
       }
+      if (copy) {
+#pragma unroll
+        for (int I = ks * IPW / KS; I < (ks + 1) * IPW / KS; ++I) dma_one(kt_issue, I, doff[I / 9]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- online softmax (owner wave), lane holds heads 32w + 16hb + (lane&15)
+    // ---- online softmax (owner wave), lane holds heads 32w + 16hb + (lane&15),
+    // tokens 16tb + 4(lane>>4) + i.  The cross-lane max is only formed when
+    // a segment starts or when some lane's own max exceeds the reference by
+    // more than RESCALE_T (rare); otherwise every lane checks its own values.
     const int n_valid = t_now.n;
-    int any_resc = 0;
+    if (n_valid < TT) {   // a segment's last tile may be partial
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float mx = -INFINITY;
-      if (n_valid < TT) {   // a segment's last tile may be partial
+      for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (16 * tb + 4 * (lane >> 4) + i >= n_valid) s[tb][hb][i] = -INFINITY;
-      }
+    }
+    float lmax[2];
+    int over = 0;
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+    for (int hb = 0; hb < 2; ++hb) {
+      lmax[hb] = fmaxf(fmaxf(fmaxf(s[0][hb][0], s[0][hb][1]), fmaxf(s[0][hb][2], s[0][hb][3])),
+                       fmaxf(fmaxf(s[1][hb][0], s[1][hb][1]), fmaxf(s[1][hb][2], s[1][hb][3])));
+      over |= lmax[hb] > m_ref[hb] + RESCALE_T ? 1 : 0;
+    }
+    float alpha[2] = {1.f, 1.f};
+    int any_resc = 0;
+    if (t_now.first || __builtin_amdgcn_readfirstlane(__any(over) ? 1 : 0)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tb][hb][i]);
-      mx = wave_rows_max(mx);
-      float alpha = 1.f;
-      if (t_now.first) {
-        // a new segment: the accumulators were zeroed at the previous segment's end
-        m_ref[hb] = mx;
-      } else if (mx > m_ref[hb] + RESCALE_T) {
-        alpha = __builtin_amdgcn_exp2f(m_ref[hb] - mx);
-        any_resc = 1;
-        m_ref[hb] = mx;
+      for (int hb = 0; hb < 2; ++hb) {
+        const float mx = wave_rows_max(lmax[hb]);
+        if (t_now.first) {
+          // a new segment: the accumulators were zeroed at the previous segment's end
+          m_ref[hb] = mx;
+        } else if (mx > m_ref[hb] + RESCALE_T) {
+          alpha[hb] = __builtin_amdgcn_exp2f(m_ref[hb] - mx);
+          any_resc = 1;
+          m_ref[hb] = mx;
+        }
       }
+      any_resc = __builtin_amdgcn_readfirstlane(__any(any_resc) ? 1 : 0);
+      if (any_resc && lane < 16) {
+        alpha_l[32 * wave + lane] = alpha[0];
+        alpha_l[32 * wave + 16 + lane] = alpha[1];
+      }
+    }
+    if (lane == 0) resc_l[wave] = any_resc;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
       float sum = 0.f;
       const int head = 32 * wave + 16 * hb + (lane & 15);
 #pragma unroll
@@ -458,12 +495,8 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
         }
         *(bf16x4*)(pl + head * PSTR + (16 * tb + 4 * (lane >> 4)) * 2) = pb;
       }
-      sum = wave_rows_sum(sum);
-      l_sum[hb] = l_sum[hb] * alpha + sum;
-      if (lane < 16) alpha_l[32 * wave + 16 * hb + lane] = alpha;
+      l_sum[hb] = l_sum[hb] * alpha[hb] + sum;
     }
-    const int wave_resc = __builtin_amdgcn_readfirstlane(__any(any_resc) ? 1 : 0);
-    if (lane == 0) resc_l[wave] = wave_resc;
     // P, alpha visible to all waves.  Only LDS traffic is waited for: a plain
     // __syncthreads would also wait for the tiles in flight.
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
@@ -565,12 +598,13 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
           }
         }
       }
+      const float lt0 = wave_rows_sum(l_sum[0]), lt1 = wave_rows_sum(l_sum[1]);
       if (lane < 16) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const int head = 32 * wave + 16 * hb + lane;
           part_ml[(slot * NH + head) * 2 + 0] = m_ref[hb];
-          part_ml[(slot * NH + head) * 2 + 1] = l_sum[hb];
+          part_ml[(slot * NH + head) * 2 + 1] = hb ? lt1 : lt0;
         }
       }
       m_ref[0] = m_ref[1] = -INFINITY;
