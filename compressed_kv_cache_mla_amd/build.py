@@ -17,7 +17,9 @@ LIB = os.path.join(HERE, "libmla.so")
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU ops.
-HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+# -fno-honor-nans: no NaN inputs are expected (infinities still are: masked
+# scores are -inf), so fmaxf needs no quieting of its operands.
+HIPCC_FLAGS = ["-O3", "-std=c++17", "-fno-honor-nans", "-fPIC", "-shared", f"--offload-arch={ARCH}",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wno-unused-command-line-argument"]
 
