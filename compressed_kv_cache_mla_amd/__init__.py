@@ -23,7 +23,8 @@ MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP
 MLA_BF16, MLA_FP32 = 0, 1
 FLAG_BAD_SEQ_LEN, FLAG_BAD_PAGE, FLAG_BAD_POSITION, FLAG_BAD_SEQ_ID = 1, 2, 4, 8
 
-EXPORTED = ("mla_cache_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_ex",
+EXPORTED = ("mla_cache_append", "mla_cache_append_ws", "mla_cache_append_workspace_size",
+            "mla_decode_workspace_size", "mla_decode", "mla_decode_ex",
             "mla_read_error_flags", "mla_last_error", "mla_device_cu_count")
 
 
@@ -82,6 +83,11 @@ def lib() -> ctypes.CDLL:
         pdims = ctypes.POINTER(mla_dims)
         L.mla_cache_append.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, i64, i32, vp, vp]
         L.mla_cache_append.restype = ctypes.c_int
+        L.mla_cache_append_ws.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, i64, i32, vp, vp,
+                                          sz, vp]
+        L.mla_cache_append_ws.restype = ctypes.c_int
+        L.mla_cache_append_workspace_size.argtypes = [pdims, i32]
+        L.mla_cache_append_workspace_size.restype = sz
         L.mla_decode_workspace_size.argtypes = [pdims, i32, i32]
         L.mla_decode_workspace_size.restype = sz
         L.mla_decode.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32, vp, vp, vp, vp, sz,
@@ -119,15 +125,25 @@ def cu_count() -> int:
 
 
 def cache_append(dims: Dims, h_t, W_DKV, W_KR, pos, page_table, c_KV, k_R, row_stride: int, num_pages: int,
-                 seq_id=None, err_flag=None, stream=None):
-    """mla_cache_append: write c^KV = W^DKV h_t and k^R = RoPE(W^KR h_t) of T
-    token rows into the paged pool (see include/mla.h)."""
+                 seq_id=None, err_flag=None, stream=None, workspace=None):
+    """mla_cache_append (mla_cache_append_ws when a workspace tensor is given):
+    write c^KV = W^DKV h_t and k^R = RoPE(W^KR h_t) of T token rows into the
+    paged pool (see include/mla.h)."""
     T = h_t.shape[0]
     num_seqs, max_pages = page_table.shape
     d = dims.c()
-    _check(lib().mla_cache_append(ctypes.byref(d), T, _ptr(h_t), _ptr(W_DKV), _ptr(W_KR), _ptr(seq_id), _ptr(pos),
-                                  _ptr(page_table), num_seqs, max_pages, _ptr(c_KV), _ptr(k_R), row_stride,
-                                  num_pages, _ptr(err_flag), _stream(stream)))
+    args = (ctypes.byref(d), T, _ptr(h_t), _ptr(W_DKV), _ptr(W_KR), _ptr(seq_id), _ptr(pos), _ptr(page_table),
+            num_seqs, max_pages, _ptr(c_KV), _ptr(k_R), row_stride, num_pages, _ptr(err_flag))
+    if workspace is None:
+        _check(lib().mla_cache_append(*args, _stream(stream)))
+    else:
+        _check(lib().mla_cache_append_ws(*args, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(stream)))
+
+
+def cache_append_workspace_size(dims: Dims, T: int) -> int:
+    d = dims.c()
+    return int(lib().mla_cache_append_workspace_size(ctypes.byref(d), T))
 
 
 def decode_workspace_size(dims: Dims, B: int, n_splits: int = 0) -> int:

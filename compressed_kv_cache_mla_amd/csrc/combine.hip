@@ -11,9 +11,9 @@
 //
 // fp32 (VALU): workgroup (head h, 32 sequences); combined latents in LDS,
 // each thread one output column for 16 sequences.
-// bf16 (MFMA): workgroup (head h, 16 sequences); the combined latents are
-// rounded to bf16 in LDS and o^T[d][b] = W^UV_h[d][:] . O~[b][:] runs as
-// v_mfma_f32_16x16x32_bf16 (M = d, N = sequence, K = latent column).
+// bf16 (MFMA): workgroup (head h, 16 sequences), one wave per sequence; the
+// combined latents are rounded to bf16 in LDS and o^T[d][b] = W^UV_h[d][:] .
+// O~[b][:] runs as v_mfma_f32_16x16x32_bf16 (M = d, N = sequence, K = latent).
 #include "mla_common.h"
 
 namespace mla {
@@ -107,15 +107,16 @@ __global__ void __launch_bounds__(256) combine_f32_kernel(int32_t B, int32_t n_h
   }
 }
 
-// bf16: workgroup (head h, CS = 16 sequences).  Each wave merges four
-// sequences: the per-slot weights 2^(m_s - m*) / L are formed lane-parallel
-// over the slots (lane j holds slot j's weight), then every lane sums 8 latent
-// columns over the slots, four slots' loads in flight at a time.  The merged
-// latents go to LDS as bf16 [16][512] (16-byte chunk c of sequence b at chunk
-// c ^ b: conflict-free fragment reads), and o^T[d][b] = W^UV_h[d][:] . O~[b][:]
-// runs as v_mfma_f32_16x16x32_bf16 (wave w: d = 32w .. 32w+31), W^UV rows read
-// straight from global memory in the A-fragment layout.
+// bf16: workgroup (head h, CS = 16 sequences), 16 waves.  Wave w merges
+// sequence w: the per-slot weights 2^(m_s - m*) / L are formed lane-parallel
+// over the slots (lane j holds slot j's weight), then every lane sums 8
+// latent columns over the slots with up to CB slots' loads in flight.  The
+// merged latents go to LDS as bf16 [16][512] (16-byte chunk c of sequence b
+// at chunk c ^ b: conflict-free fragment reads), and o^T[d][b] = W^UV_h[d][:]
+// . O~[b][:] runs as v_mfma_f32_16x16x32_bf16 in waves 0..7 (wave w: d = 16w
+// .. 16w+15), W^UV rows read straight from global memory in the A layout.
 constexpr int CS = 16;
+constexpr int CB = 8;
 
 __device__ __forceinline__ float wave_max64(float x) {
 #pragma unroll
@@ -128,11 +129,12 @@ __device__ __forceinline__ float wave_sum64(float x) {
   return x;
 }
 
-__global__ void __launch_bounds__(256) combine_mfma_kernel(int32_t B, int32_t n_h, const int32_t* __restrict__ prefix,
-                                                           int32_t G, const float* __restrict__ part_ml,
-                                                           const bf16* __restrict__ part_o,
-                                                           const bf16* __restrict__ W_UV, float* __restrict__ out,
-                                                           float* __restrict__ lse) {
+__global__ void __launch_bounds__(64 * CS) combine_mfma_kernel(int32_t B, int32_t n_h,
+                                                               const int32_t* __restrict__ prefix, int32_t G,
+                                                               const float* __restrict__ part_ml,
+                                                               const bf16* __restrict__ part_o,
+                                                               const bf16* __restrict__ W_UV, float* __restrict__ out,
+                                                               float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) char ol[CS * D_C * 2];
   __shared__ int empty_l[CS];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -141,7 +143,8 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int32_t B, int32_t n_
   const int b0 = blockIdx.y * CS;
   const int nb = min(CS, B - b0);
   const int64_t N = prefix[B];
-  for (int bb = wave; bb < CS; bb += 4) {
+  {
+    const int bb = wave;
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int empty = 1;
     if (bb < nb) {
@@ -153,11 +156,12 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int32_t B, int32_t n_
         const int64_t w0 = split_of(sb, N, G), w1 = split_of(sb + n - 1, N, G);
         const int cnt = (int)(w1 - w0 + 1);
         const float* ml = part_ml + ((w0 + b) * n_h + h) * 2;   // slot w0 + b + i at ml + 2*n_h*i
+        const int64_t mstride = (int64_t)2 * n_h;
         float mx = -INFINITY;
-        for (int i = lane; i < cnt; i += 64) mx = fmaxf(mx, ml[(int64_t)i * 2 * n_h]);
+        for (int i = lane; i < cnt; i += 64) mx = fmaxf(mx, ml[i * mstride]);
         mx = wave_max64(mx);
         float L = 0.f;
-        for (int i = lane; i < cnt; i += 64) L += exp2f(ml[(int64_t)i * 2 * n_h] - mx) * ml[(int64_t)i * 2 * n_h + 1];
+        for (int i = lane; i < cnt; i += 64) L += exp2f(ml[i * mstride] - mx) * ml[i * mstride + 1];
         L = wave_sum64(L);
         const float invL = 1.f / L;
         if (lse && lane == 0) lse[(int64_t)b * n_h + h] = (mx + log2f(L)) * 0.69314718055994531f;
@@ -165,24 +169,19 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int32_t B, int32_t n_
         const int64_t sstride = (int64_t)n_h * D_C;
         for (int i0 = 0; i0 < cnt; i0 += 64) {
           const int m = min(64, cnt - i0);
-          const float wl = lane < m ? exp2f(ml[(int64_t)(i0 + lane) * 2 * n_h] - mx) * invL : 0.f;
-          int i = 0;
-          for (; i + 4 <= m; i += 4) {
-            bf16x8 v[4];
+          const float wl = lane < m ? exp2f(ml[(i0 + lane) * mstride] - mx) * invL : 0.f;
+          for (int i = 0; i < m; i += CB) {
+            bf16x8 v[CB];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = *(const bf16x8*)(po + sstride * (i0 + i + u));
+            for (int u = 0; u < CB; ++u)
+              if (i + u < m) v[u] = *(const bf16x8*)(po + sstride * (i0 + i + u));
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float wg = __shfl(wl, i + u);
+            for (int u = 0; u < CB; ++u)
+              if (i + u < m) {
+                const float wg = __shfl(wl, i + u);
 #pragma unroll
-              for (int k = 0; k < 8; ++k) a[k] = fmaf(wg, (float)v[u][k], a[k]);
-            }
-          }
-          for (; i < m; ++i) {
-            const bf16x8 v = *(const bf16x8*)(po + sstride * (i0 + i));
-            const float wg = __shfl(wl, i);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) a[k] = fmaf(wg, (float)v[k], a[k]);
+                for (int k = 0; k < 8; ++k) a[k] = fmaf(wg, (float)v[u][k], a[k]);
+              }
           }
         }
       }
@@ -194,32 +193,23 @@ __global__ void __launch_bounds__(256) combine_mfma_kernel(int32_t B, int32_t n_
     if (lane == 0) empty_l[bb] = empty;
   }
   __syncthreads();
+  if (wave >= D_H / 16) return;
   // o^T[d][b]: A = W^UV rows d (16 x 32 per MFMA), B = O~^T (32 latent columns x 16 sequences)
-  f32x4 acc[2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bf16* wr = W_UV + ((int64_t)h * D_H + 32 * wave + (lane & 15)) * D_C + 8 * (lane >> 4);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const bf16* wr = W_UV + ((int64_t)h * D_H + 16 * wave + (lane & 15)) * D_C + 8 * (lane >> 4);
   const int bq = lane & 15;
-#pragma unroll 4
+#pragma unroll
   for (int ks = 0; ks < D_C / 32; ++ks) {
     const int c16 = 4 * ks + (lane >> 4);
     const bf16x8 bfr = *(const bf16x8*)(ol + bq * 1024 + ((c16 ^ bq) << 4));
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const bf16x8 afr = *(const bf16x8*)(wr + (int64_t)16 * mb * D_C + 32 * ks);
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc[mb], 0, 0, 0);
-    }
+    const bf16x8 afr = *(const bf16x8*)(wr + 32 * ks);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc, 0, 0, 0);
   }
-  // C layout: lane holds d = 16mb + 4*(lane>>4) + i (of this wave's 32), sequence lane & 15
+  // C layout: lane holds d = 16w + 4*(lane>>4) + i, sequence lane & 15
   if (bq < nb) {
-    const bool empty = empty_l[bq] != 0;
-    float* dst = out + ((int64_t)(b0 + bq) * n_h + h) * D_H + 32 * wave + 4 * (lane >> 4);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x4 v = acc[mb];
-      if (empty) v = f32x4{0.f, 0.f, 0.f, 0.f};
-      *(f32x4*)(dst + 16 * mb) = v;
-    }
+    f32x4 v = acc;
+    if (empty_l[bq]) v = f32x4{0.f, 0.f, 0.f, 0.f};
+    *(f32x4*)(out + ((int64_t)(b0 + bq) * n_h + h) * D_H + 16 * wave + 4 * (lane >> 4)) = v;
   }
 }
 
@@ -234,7 +224,7 @@ hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, i
                                             (const float*)W_UV, out, lse);
   } else {
     dim3 grid(d.n_h, (B + CS - 1) / CS);
-    combine_mfma_kernel<<<grid, 256, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
+    combine_mfma_kernel<<<grid, 64 * CS, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
                                              (const bf16*)W_UV, out, lse);
   }
   return hipGetLastError();

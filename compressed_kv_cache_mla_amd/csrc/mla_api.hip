@@ -74,10 +74,11 @@ const char* mla_last_error(void) { return g_err.c_str(); }
 
 int32_t mla_device_cu_count(void) { return default_splits(); }
 
-mla_status mla_cache_append(const mla_dims* dims, int32_t T, const void* h_t, const void* W_DKV, const void* W_KR,
-                            const int32_t* seq_id, const int32_t* pos, const int32_t* page_table,
-                            int32_t num_seqs, int32_t max_pages, void* c_KV, void* k_R, int64_t row_stride,
-                            int32_t num_pages, int32_t* err_flag, void* stream) {
+static mla_status cache_append_impl(const mla_dims* dims, int32_t T, const void* h_t, const void* W_DKV,
+                                    const void* W_KR, const int32_t* seq_id, const int32_t* pos,
+                                    const int32_t* page_table, int32_t num_seqs, int32_t max_pages, void* c_KV,
+                                    void* k_R, int64_t row_stride, int32_t num_pages, int32_t* err_flag,
+                                    void* workspace, size_t ws_bytes, void* stream) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (T < 0) return fail(MLA_ERR_INVALID_ARG, "T=%d < 0", T);
@@ -92,10 +93,34 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t T, const void* h_t, co
   if (st != MLA_OK) return st;
   if ((int64_t)max_pages * dims->page_size >= ((int64_t)1 << 31))
     return fail(MLA_ERR_UNSUPPORTED, "max_pages*page_size >= 2^31");
+  if (workspace && ((uintptr_t)workspace & 255) != 0)
+    return fail(MLA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   hipError_t e = mla::launch_append(*dims, T, h_t, W_DKV, W_KR, seq_id, pos, page_table, num_seqs, max_pages, c_KV,
-                                    k_R, row_stride, num_pages, err_flag, (hipStream_t)stream);
+                                    k_R, row_stride, num_pages, err_flag, workspace, ws_bytes, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "append launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+mla_status mla_cache_append(const mla_dims* dims, int32_t T, const void* h_t, const void* W_DKV, const void* W_KR,
+                            const int32_t* seq_id, const int32_t* pos, const int32_t* page_table,
+                            int32_t num_seqs, int32_t max_pages, void* c_KV, void* k_R, int64_t row_stride,
+                            int32_t num_pages, int32_t* err_flag, void* stream) {
+  return cache_append_impl(dims, T, h_t, W_DKV, W_KR, seq_id, pos, page_table, num_seqs, max_pages, c_KV, k_R,
+                           row_stride, num_pages, err_flag, nullptr, 0, stream);
+}
+
+size_t mla_cache_append_workspace_size(const mla_dims* dims, int32_t T) {
+  if (check_dims(dims) != MLA_OK || T < 1) return 0;
+  return mla::append_workspace_bytes(*dims, T);
+}
+
+mla_status mla_cache_append_ws(const mla_dims* dims, int32_t T, const void* h_t, const void* W_DKV,
+                               const void* W_KR, const int32_t* seq_id, const int32_t* pos,
+                               const int32_t* page_table, int32_t num_seqs, int32_t max_pages, void* c_KV,
+                               void* k_R, int64_t row_stride, int32_t num_pages, int32_t* err_flag,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  return cache_append_impl(dims, T, h_t, W_DKV, W_KR, seq_id, pos, page_table, num_seqs, max_pages, c_KV, k_R,
+                           row_stride, num_pages, err_flag, workspace, ws_bytes, stream);
 }
 
 size_t mla_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t n_splits) {

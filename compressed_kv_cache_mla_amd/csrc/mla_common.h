@@ -153,10 +153,15 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
 
 // Launchers (host side), one per kernel family.
 namespace mla {
+// Cache append.  With a workspace of append_workspace_bytes(d, T) bytes (0:
+// no workspace path for these sizes) a decode-step batch (bf16, T <= 64) runs
+// split over d_model in two launches; otherwise one kernel does it.
+constexpr int APPEND_WS_MAX_T = 64;
+size_t append_workspace_bytes(const mla_dims& d, int32_t T);
 hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void* W_DKV, const void* W_KR,
                          const int32_t* seq_id, const int32_t* pos, const int32_t* page_table,
                          int32_t num_seqs, int32_t max_pages, void* c_KV, void* k_R, int64_t row_stride,
-                         int32_t num_pages, int32_t* err_flag, hipStream_t s);
+                         int32_t num_pages, int32_t* err_flag, void* ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_tokens, int32_t n_splits, int32_t* prefix,
                        int32_t* split_rec, int32_t* flags, hipStream_t s);
 // Query absorption; for bf16 the decode plan runs in the same launch (then

@@ -110,6 +110,28 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t T, const void* h_t, co
                             int32_t* err_flag, void* stream);
 
 /*
+ * mla_cache_append_workspace_size -- bytes of device workspace with which
+ * mla_cache_append_ws takes its split path for T tokens (bf16, T <= 64,
+ * d_model a multiple of 1024); 0 when that path does not apply.
+ *
+ * mla_cache_append_ws -- mla_cache_append with a caller workspace
+ * (256-byte aligned, device memory, contents need no initialisation).  With
+ * at least mla_cache_append_workspace_size() bytes, a decode-step batch is
+ * computed split over d_model (fp32 partial sums in the workspace, then one
+ * pass that adds them in a fixed order, applies RoPE and stores the rows), so
+ * the weight stream is spread over the whole GPU; results are the same
+ * computation as mla_cache_append up to fp32 summation order.  With a smaller
+ * or NULL workspace it behaves exactly as mla_cache_append.  Calls that share
+ * one workspace must be ordered (e.g. on one stream).
+ */
+size_t mla_cache_append_workspace_size(const mla_dims* dims, int32_t T);
+mla_status mla_cache_append_ws(const mla_dims* dims, int32_t T, const void* h_t, const void* W_DKV,
+                               const void* W_KR, const int32_t* seq_id, const int32_t* pos,
+                               const int32_t* page_table, int32_t num_seqs, int32_t max_pages,
+                               void* c_KV, void* k_R, int64_t row_stride, int32_t num_pages,
+                               int32_t* err_flag, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * mla_decode_workspace_size -- bytes of device workspace mla_decode needs for
  * batch B with n_splits work partitions (0 = the library's default, one per
  * compute unit).  Returns 0 for invalid dims.

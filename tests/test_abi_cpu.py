@@ -134,3 +134,13 @@ def test_split_slots_are_unique_and_contiguous(seed):
             assert w + b not in seen
             seen.add(w + b)
     assert max(seen) < G + B
+
+
+def test_append_workspace_size():
+    L = mla.lib()
+    d = _dims()
+    n = L.mla_cache_append_workspace_size(ctypes.byref(d), 32)
+    assert n == 8 * 32 * 576 * 4
+    assert L.mla_cache_append_workspace_size(ctypes.byref(d), 65) == 0           # decode-step sizes only
+    assert L.mla_cache_append_workspace_size(ctypes.byref(_dims(dtype=mla.MLA_FP32)), 32) == 0
+    assert L.mla_cache_append_workspace_size(ctypes.byref(_dims(d_model=1536)), 32) == 0

@@ -102,6 +102,24 @@ def test_bf16_page_sizes(page_size):
         _check_decode(wl, range(cfg.B))
 
 
+@pytest.mark.parametrize("use_workspace", [True, False])
+def test_decode_step_append_paths(use_workspace):
+    # the decode step's append of each sequence's newest token, with the split
+    # (workspace) path and with the single-kernel path, against the oracle
+    cfg = W.scaled(W.CONFIGS["b32_l4096"], name="step_append", B=7, lens=(50, 300), seed=41)
+    _say(f"case step append (workspace={use_workspace})")
+    wl = W.Workload(cfg)
+    if use_workspace:
+        assert wl.mla.cache_append_workspace_size(wl.dims, cfg.B) > 0
+    last = wl.prefix[1:] - 1
+    rows = wl.pool_rows(np.arange(cfg.B), wl.n - 1)
+    wl.pool[torch.from_numpy(rows).to(wl.device)] = 0
+    wl.append_step(use_workspace=use_workspace)
+    torch.cuda.synchronize()
+    _check_append(wl, range(cfg.B), tokens_per_seq=lambda n: np.array([n - 1]))
+    assert last.size == cfg.B
+
+
 def test_bf16_page_permutation_is_bitwise_invariant():
     base = W.scaled(W.CONFIGS["b64_ragged"], name="perm", d_model=256, B=6, lens=(100, 900), seed=5)
     _say("case page permutation")

@@ -205,15 +205,19 @@ class Workload:
                         self.row_stride, self.num_pages, self.page_table, self.seq_lens, self.out, self.lse,
                         self.workspace, self.n_splits, stream, ev_start, ev_stop, impl)
 
-    def append_step(self, stream=None):
+    def append_step(self, stream=None, use_workspace: bool = True):
         """The decode step's append: each sequence's newest token (position
-        n_b - 1) is written again from its token state."""
+        n_b - 1) is written again from its token state (with the append
+        workspace when the library has a split path for this size)."""
         if not hasattr(self, "_step_h"):
             last = self.prefix[1:] - 1
             self._step_h = self.h_rows(torch.from_numpy(last).to(self.device))
             self._step_pos = self.pos_q.clone()
+            nws = self.mla.cache_append_workspace_size(self.dims, self.cfg.B)
+            self._append_ws = torch.empty(nws, dtype=torch.uint8, device=self.device) if nws > 0 else None
         self.mla.cache_append(self.dims, self._step_h, self.W_DKV, self.W_KR, self._step_pos, self.page_table,
-                              self.c_KV, self.k_R, self.row_stride, self.num_pages, stream=stream)
+                              self.c_KV, self.k_R, self.row_stride, self.num_pages, stream=stream,
+                              workspace=self._append_ws if use_workspace else None)
 
     # ---------------------------------------------------------------- oracle side (CPU, generator only)
     def oracle_inputs(self, b: int) -> dict:
