@@ -89,13 +89,10 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int32_t B, int32_t n_h
                                                           const bf16* __restrict__ q_R,
                                                           const int32_t* __restrict__ pos_q,
                                                           const bf16* __restrict__ W_UK, float qscale,
-                                                          float rope_base, bf16* __restrict__ qabs,
-                                                          const int32_t* __restrict__ seq_lens, int32_t max_tokens,
-                                                          int32_t G, int32_t* __restrict__ prefix,
-                                                          int32_t* __restrict__ split_rec, int32_t* __restrict__ flags) {
+                                                          float rope_base, bf16* __restrict__ qabs, PlanArgs pa) {
   __shared__ __attribute__((aligned(1024))) char wl[D_H * 256];
   if (blockIdx.x == 4 * n_h) {
-    if (blockIdx.y == 0) plan_block<256>(seq_lens, B, max_tokens, G, prefix, split_rec, flags, (int32_t*)wl);
+    if (blockIdx.y == 0) plan_block<256>(pa, (int32_t*)wl, D_H * 256 / 4 - 256);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63;
@@ -187,11 +184,10 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int32_t B, int32_t n_h
 }  // namespace
 
 hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
-                         const void* W_UK, void* qabs, const int32_t* seq_lens, int32_t max_tokens,
-                         int32_t n_splits, int32_t* prefix, int32_t* split_rec, int32_t* flags, hipStream_t s) {
+                         const void* W_UK, void* qabs, const PlanArgs& pa, hipStream_t s) {
   const float qscale = d.softmax_scale * LOG2E;
   if (d.dtype == MLA_FP32) {
-    hipError_t e = launch_plan(seq_lens, B, max_tokens, n_splits, prefix, split_rec, flags, s);
+    hipError_t e = launch_plan(pa, s);
     if (e != hipSuccess) return e;
     dim3 grid(d.n_h, (B + AB_SEQ - 1) / AB_SEQ);
     absorb_kernel<float><<<grid, 256, 0, s>>>(B, d.n_h, (const float*)q_C, (const float*)q_R, pos_q,
@@ -199,8 +195,7 @@ hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const vo
   } else {
     dim3 g2(4 * d.n_h + 1, (B + 63) / 64);
     absorb_mfma_kernel<<<g2, 256, 0, s>>>(B, d.n_h, (const bf16*)q_C, (const bf16*)q_R, pos_q, (const bf16*)W_UK,
-                                         qscale, d.rope_base, (bf16*)qabs, seq_lens, max_tokens, n_splits, prefix,
-                                         split_rec, flags);
+                                         qscale, d.rope_base, (bf16*)qabs, pa);
   }
   return hipGetLastError();
 }

@@ -107,15 +107,16 @@ __global__ void __launch_bounds__(256) combine_f32_kernel(int32_t B, int32_t n_h
   }
 }
 
-// bf16: workgroup (head h, CS = 16 sequences), 16 waves.  Wave w merges
-// sequence w: the per-slot weights 2^(m_s - m*) / L are formed lane-parallel
-// over the slots (lane j holds slot j's weight), then every lane sums 8
-// latent columns over the slots with up to CB slots' loads in flight.  The
-// merged latents go to LDS as bf16 [16][512] (16-byte chunk c of sequence b
-// at chunk c ^ b: conflict-free fragment reads), and o^T[d][b] = W^UV_h[d][:]
-// . O~[b][:] runs as v_mfma_f32_16x16x32_bf16 in waves 0..7 (wave w: d = 16w
-// .. 16w+15), W^UV rows read straight from global memory in the A layout.
-constexpr int CS = 16;
+// bf16: workgroup (head h, CS sequences), 16 waves.  Wave w merges
+// sequences w, w + 16, ...: the per-slot weights 2^(m_s - m*) / L are formed
+// lane-parallel over the slots (lane j holds slot j's weight), then every
+// lane sums 8 latent columns over the slots with up to CB slots' loads in
+// flight.  The merged latents go to LDS as bf16 [CS][512] (16-byte chunk c of
+// sequence b at chunk c ^ (b & 15): conflict-free fragment reads), and
+// o^T[d][b] = W^UV_h[d][:] . O~[b][:] runs as v_mfma_f32_16x16x32_bf16 in
+// waves 0..7 (wave w: d = 16w .. 16w+15, CS/16 blocks of 16 sequences), W^UV
+// rows read straight from global memory in the A layout, once per CS
+// sequences.
 constexpr int CB = 8;
 
 __device__ __forceinline__ float wave_max64(float x) {
@@ -129,12 +130,13 @@ __device__ __forceinline__ float wave_sum64(float x) {
   return x;
 }
 
-__global__ void __launch_bounds__(64 * CS) combine_mfma_kernel(int32_t B, int32_t n_h,
-                                                               const int32_t* __restrict__ prefix, int32_t G,
-                                                               const float* __restrict__ part_ml,
-                                                               const bf16* __restrict__ part_o,
-                                                               const bf16* __restrict__ W_UV, float* __restrict__ out,
-                                                               float* __restrict__ lse) {
+template <int CS>
+__global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n_h, const int32_t* __restrict__ prefix,
+                                                            int32_t G, const float* __restrict__ part_ml,
+                                                            const bf16* __restrict__ part_o,
+                                                            const bf16* __restrict__ W_UV, float* __restrict__ out,
+                                                            float* __restrict__ lse) {
+  constexpr int NBQ = CS / 16;
   __shared__ __attribute__((aligned(16))) char ol[CS * D_C * 2];
   __shared__ int empty_l[CS];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -143,8 +145,7 @@ __global__ void __launch_bounds__(64 * CS) combine_mfma_kernel(int32_t B, int32_
   const int b0 = blockIdx.y * CS;
   const int nb = min(CS, B - b0);
   const int64_t N = prefix[B];
-  {
-    const int bb = wave;
+  for (int bb = wave; bb < CS; bb += 16) {
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int empty = 1;
     if (bb < nb) {
@@ -189,27 +190,36 @@ __global__ void __launch_bounds__(64 * CS) combine_mfma_kernel(int32_t B, int32_
     bf16x8 r;
 #pragma unroll
     for (int k = 0; k < 8; ++k) r[k] = (bf16)a[k];
-    *(bf16x8*)(ol + bb * 1024 + ((lane ^ bb) << 4)) = r;
+    *(bf16x8*)(ol + bb * 1024 + ((lane ^ (bb & 15)) << 4)) = r;
     if (lane == 0) empty_l[bb] = empty;
   }
   __syncthreads();
   if (wave >= D_H / 16) return;
   // o^T[d][b]: A = W^UV rows d (16 x 32 per MFMA), B = O~^T (32 latent columns x 16 sequences)
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NBQ];
+#pragma unroll
+  for (int j = 0; j < NBQ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16* wr = W_UV + ((int64_t)h * D_H + 16 * wave + (lane & 15)) * D_C + 8 * (lane >> 4);
   const int bq = lane & 15;
 #pragma unroll
   for (int ks = 0; ks < D_C / 32; ++ks) {
     const int c16 = 4 * ks + (lane >> 4);
-    const bf16x8 bfr = *(const bf16x8*)(ol + bq * 1024 + ((c16 ^ bq) << 4));
     const bf16x8 afr = *(const bf16x8*)(wr + 32 * ks);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NBQ; ++j) {
+      const bf16x8 bfr = *(const bf16x8*)(ol + (16 * j + bq) * 1024 + ((c16 ^ bq) << 4));
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc[j], 0, 0, 0);
+    }
   }
-  // C layout: lane holds d = 16w + 4*(lane>>4) + i, sequence lane & 15
-  if (bq < nb) {
-    f32x4 v = acc;
-    if (empty_l[bq]) v = f32x4{0.f, 0.f, 0.f, 0.f};
-    *(f32x4*)(out + ((int64_t)(b0 + bq) * n_h + h) * D_H + 16 * wave + 4 * (lane >> 4)) = v;
+  // C layout: lane holds d = 16w + 4*(lane>>4) + i, sequence 16j + (lane & 15)
+#pragma unroll
+  for (int j = 0; j < NBQ; ++j) {
+    const int bb = 16 * j + bq;
+    if (bb < nb) {
+      f32x4 v = acc[j];
+      if (empty_l[bb]) v = f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)(out + ((int64_t)(b0 + bb) * n_h + h) * D_H + 16 * wave + 4 * (lane >> 4)) = v;
+    }
   }
 }
 
@@ -223,9 +233,17 @@ hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, i
     combine_f32_kernel<<<grid, 256, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const float*)part_o,
                                             (const float*)W_UV, out, lse);
   } else {
-    dim3 grid(d.n_h, (B + CS - 1) / CS);
-    combine_mfma_kernel<<<grid, 64 * CS, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
-                                             (const bf16*)W_UV, out, lse);
+    // 32 sequences per workgroup (W^UV read once per 32) unless that leaves
+    // fewer workgroups than compute units
+    if (B > 16 && d.n_h * ((B + 31) / 32) >= 256) {
+      dim3 grid(d.n_h, (B + 31) / 32);
+      combine_mfma_kernel<32><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
+                                                    (const bf16*)W_UV, out, lse);
+    } else {
+      dim3 grid(d.n_h, (B + 15) / 16);
+      combine_mfma_kernel<16><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
+                                                    (const bf16*)W_UV, out, lse);
+    }
   }
   return hipGetLastError();
 }

@@ -261,18 +261,19 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   const int p_off = (lane & 31) * PSTR + (lane >> 5) * 16;
 
   Cursor cur;
-  cur.init((cint_t)split_rec + 4 * split, B, P0, P1, page_size);
+  const cint_t rec = (cint_t)split_rec + SPLIT_REC * split;
+  cur.init(rec, B, P0, P1, page_size);
   TileDesc t_now = cur.next(cpre);   // tile being computed
   TileDesc t_n1 = cur.next(cpre);    // tile in flight
   TileDesc t_n2 = cur.next(cpre);    // tile whose copy is issued this iteration
 
   // Page-table index of the first (which = 0) or last (which = 1) page a tile touches.
-  auto page_index = [&](const TileDesc& td, int which) -> int64_t {
+  auto page_index = [&](const TileDesc& td, int which) __attribute__((always_inline)) -> int64_t {
     const int32_t p = (which && td.rem + td.n > page_size) ? td.p0 + 1 : td.p0;
     return (int64_t)td.b * max_pages + p;
   };
   // Pool row of tile row r (rows past the tile's end repeat its last row).
-  auto resolve_row = [&](const TileDesc& td, int r, int32_t pg0, int32_t pg1) -> int32_t {
+  auto resolve_row = [&](const TileDesc& td, int r, int32_t pg0, int32_t pg1) __attribute__((always_inline)) -> int32_t {
     r = min(r, td.n - 1);
     const int off = td.rem + r;
     const bool cross = off >= page_size;
@@ -285,7 +286,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   };
   // The two page ids of a tile go to the pad after block 0 of a tile buffer
   // (never written by tile copies, never read by the math).
-  auto issue_page_ids = [&](char* kt, const TileDesc& td) {
+  auto issue_page_ids = [&](char* kt, const TileDesc& td) __attribute__((always_inline)) {
     if (wave == 0 && td.n > 0 && lane < 2)
       dma4(page_table + page_index(td, lane), __builtin_amdgcn_readfirstlane(lds_addr(kt + PGOFF)));
   };
@@ -296,7 +297,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   // dma_src() forms a lane's source offset for the wave's gi-th row group
   // from the scalar bases (nothing is kept live across the loop); copy
   // instruction I = 9*gi + j of the wave is issued by dma_one().
-  auto dma_src = [&](const TileDesc& td, int gi, int32_t pg0, int32_t pg1) -> int64_t {
+  auto dma_src = [&](const TileDesc& td, int gi, int32_t pg0, int32_t pg1) __attribute__((always_inline)) -> int64_t {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int g = wave + NW * gi;
@@ -304,12 +305,12 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
     const int64_t row = resolve_row(td, 8 * g + m, pg0, pg1);
     return row * stride_b + 16 * ((ln & 7) ^ swz(m));
   };
-  auto dma_one = [&](char* kt, int I, int64_t off) {
+  auto dma_one = [&](char* kt, int I, int64_t off) __attribute__((always_inline)) {
     const int gi = I / 9, j = I % 9, g = wave + NW * gi;
     const char* src = j < 8 ? (const char*)c_KV + off + 128 * j : (const char*)k_R + off;
     dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(kt) + (9 * g + j) * 1024));
   };
-  auto issue_dma = [&](char* kt, const TileDesc& td, int32_t pg0, int32_t pg1) {
+  auto issue_dma = [&](char* kt, const TileDesc& td, int32_t pg0, int32_t pg1) __attribute__((always_inline)) {
 #pragma unroll
     for (int gi = 0; gi < 4 / NW; ++gi) {
       const int64_t off = dma_src(td, gi, pg0, pg1);
@@ -326,7 +327,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   // the sum (its tokens only; the four parts are added when the segment ends).
   float m_ref[2], l_sum[2];
 
-  auto load_q = [&](int32_t b) {
+  auto load_q = [&](int32_t b) __attribute__((always_inline)) {
     int ln = lane;   // hidden from loop-invariant hoisting
     asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -351,7 +352,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   // asm, so the compiler sees no load of them pending across the loop and
   // puts no wait in the score loop (a wait there would also hold up the
   // tiles in flight).
-  auto settle_q = [&]() {
+  auto settle_q = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
@@ -368,13 +369,32 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       for (int r = 0; r < 16; ++r) ACC_ZERO(o[hb][db][r]);
   m_ref[0] = m_ref[1] = -INFINITY;
   l_sum[0] = l_sum[1] = 0.f;
-  issue_dma(kt0, t_now, cpt[page_index(t_now, 0)], cpt[page_index(t_now, 1)]);
-  if (t_n1.n > 0) issue_dma(kt1, t_n1, cpt[page_index(t_n1, 0)], cpt[page_index(t_n1, 1)]);
-  issue_page_ids(kt2, t_n2);
+  // The query loads go first; the pages of the first two tiles come with the
+  // split's plan record (pages p0 .. p0+2 of its first sequence), so both
+  // copies start one memory latency after the record.
   load_q(t_now.b);
+  {
+    const int32_t r0 = rec[3], r1 = rec[4], r2 = rec[5];
+    const int32_t a0 = r0, a1 = (t_now.rem + t_now.n > page_size) ? r1 : r0;
+    int32_t b0 = 0, b1 = 0;
+    if (t_n1.n > 0) {
+      if (t_n1.b == t_now.b) {
+        const int32_t kf = t_n1.p0 - t_now.p0;
+        const int32_t kl = kf + ((t_n1.rem + t_n1.n > page_size) ? 1 : 0);
+        b0 = kf == 0 ? r0 : r1;
+        b1 = kl == 0 ? r0 : (kl == 1 ? r1 : r2);
+      } else {
+        b0 = cpt[page_index(t_n1, 0)];
+        b1 = cpt[page_index(t_n1, 1)];
+      }
+    }
+    issue_dma(kt0, t_now, a0, a1);
+    if (t_n1.n > 0) issue_dma(kt1, t_n1, b0, b1);
+  }
+  issue_page_ids(kt2, t_n2);
   settle_q();
 
-  auto process = [&](char* kt, char* kt_issue) {
+  auto process = [&](char* kt, char* kt_issue) __attribute__((always_inline)) {
     // Tile t_now was copied into kt two iterations ago; t_n1's copy (issued
     // last iteration, after the page ids of t_n2) may stay in flight.
     if (t_n1.n <= 0)
@@ -405,7 +425,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) s[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 af[3][2], qf[3][2];
-    auto load_ks = [&](int ks, int st) {
+    auto load_ks = [&](int ks, int st) __attribute__((always_inline)) {
       const int off = a_off[ks & 1] + 1024 * (ks >> 1);
       af[st][0] = *(const bf16x8*)(kt + off);
       af[st][1] = *(const bf16x8*)(kt + off + 18432);

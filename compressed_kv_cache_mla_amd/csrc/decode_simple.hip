@@ -18,12 +18,9 @@
 namespace mla {
 namespace {
 
-__global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ seq_lens, int32_t B,
-                                                    int32_t max_tokens, int32_t G, int32_t* __restrict__ prefix,
-                                                    int32_t* __restrict__ split_rec,
-                                                    int32_t* __restrict__ flags) {
-  __shared__ int32_t part[1024];
-  plan_block<1024>(seq_lens, B, max_tokens, G, prefix, split_rec, flags, part);
+__global__ void __launch_bounds__(1024) plan_kernel(PlanArgs pa) {
+  __shared__ int32_t part[1024 + 8192];
+  plan_block<1024>(pa, part, 8192);
 }
 
 template <typename T>
@@ -117,9 +114,8 @@ __global__ void __launch_bounds__(256) decode_simple_kernel(
 
 }  // namespace
 
-hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_tokens, int32_t n_splits, int32_t* prefix,
-                       int32_t* split_rec, int32_t* flags, hipStream_t s) {
-  plan_kernel<<<1, 1024, 0, s>>>(seq_lens, B, max_tokens, n_splits, prefix, split_rec, flags);
+hipError_t launch_plan(const PlanArgs& pa, hipStream_t s) {
+  plan_kernel<<<1, 1024, 0, s>>>(pa);
   return hipGetLastError();
 }
 

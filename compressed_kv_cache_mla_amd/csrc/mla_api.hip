@@ -172,8 +172,18 @@ mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const
   hipStream_t s = (hipStream_t)stream;
   const int32_t max_tokens = max_pages * dims->page_size;
 
-  hipError_t e = mla::launch_absorb(*dims, B, q_C, q_R, pos_q, W_UK, qabs, seq_lens, max_tokens, n_splits, prefix,
-                                    split_rec, flags, s);
+  mla::PlanArgs pa;
+  pa.seq_lens = seq_lens;
+  pa.B = B;
+  pa.max_tokens = max_tokens;
+  pa.G = n_splits;
+  pa.prefix = prefix;
+  pa.split_rec = split_rec;
+  pa.flags = flags;
+  pa.page_table = page_table;
+  pa.max_pages = max_pages;
+  pa.page_size = dims->page_size;
+  hipError_t e = mla::launch_absorb(*dims, B, q_C, q_R, pos_q, W_UK, qabs, pa, s);
   if (opts && opts->impl != 0 && opts->impl != 1) return fail(MLA_ERR_INVALID_ARG, "opts->impl=%d", opts->impl);
   if (e == hipSuccess && opts && opts->ev_start) e = hipEventRecord((hipEvent_t)opts->ev_start, s);
   if (e == hipSuccess) {

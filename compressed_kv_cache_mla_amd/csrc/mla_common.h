@@ -52,6 +52,9 @@ __device__ __forceinline__ void rope_cos_sin(int32_t pos, int k, int d, float ba
   *s = (float)sn;
 }
 
+// Ints per split record (see plan_block).
+constexpr int SPLIT_REC = 8;
+
 // Decode workspace layout (bytes, each part 256-aligned).
 struct DecodeWs {
   size_t flags, prefix, splits, qabs, part_ml, part_o, total;
@@ -66,7 +69,7 @@ inline DecodeWs decode_ws_layout(int32_t B, int32_t n_h, int32_t n_splits, int e
   size_t off = 0;
   w.flags = off;   off += 256;
   w.prefix = off;  off += align256((size_t)(B + 1) * 4);
-  w.splits = off;  off += align256((size_t)n_splits * 16);               // per split: {b, s_beg, s_end, 0}
+  w.splits = off;  off += align256((size_t)n_splits * SPLIT_REC * 4);   // per split: see plan_block
   w.qabs = off;    off += align256((size_t)B * n_h * D_K * elt);
   w.part_ml = off; off += align256((size_t)w.n_slots * n_h * 2 * 4);
   w.part_o = off;  off += align256((size_t)w.n_slots * n_h * D_C * elt);   // partial O~ in the cache type
@@ -94,27 +97,41 @@ __device__ __forceinline__ int32_t seq_of(const int32_t* __restrict__ prefix, in
   return lo;
 }
 
-// Decode plan, run by one workgroup of NT threads (part: NT ints of LDS):
-// clears the error flags, writes prefix[0..B] = exclusive sum of the clamped
-// sequence lengths, and for every split w the record {b, prefix[b],
-// prefix[b+1], 0} of the sequence holding its first token P_w = floor(w N / G).
-// P_w lies in sequence b iff prefix[b] <= P_w < prefix[b+1], i.e. iff
-// ceil(prefix[b] G / N) <= w < ceil(prefix[b+1] G / N); each thread walks the
-// splits of its own sequences.
+// Inputs and outputs of the decode plan.
+struct PlanArgs {
+  const int32_t* seq_lens;
+  int32_t B, max_tokens, G;
+  int32_t* prefix;
+  int32_t* split_rec;
+  int32_t* flags;
+  const int32_t* page_table;
+  int32_t max_pages, page_size;
+};
+
+// Decode plan, run by one workgroup of NT threads.  part: NT + cap ints of
+// LDS (prefix sums are kept there when B + 1 <= cap).  It clears the error
+// flags, writes prefix[0..B] = exclusive sum of the clamped sequence lengths,
+// and for every split w the record
+//   {b, prefix[b], prefix[b+1], pg_0, pg_1, pg_2, 0, 0}
+// of the sequence b holding its first token P_w = floor(w N / G) (the last b
+// with prefix[b] <= P_w), where pg_k is the page-table entry of page p0 + k
+// of b (p0: the page of P_w; indices past the table's row repeat its last
+// entry).  The first two tiles of a split touch at most these three pages
+// when pages hold >= 32 tokens.  One thread per split, so the page-table
+// reads of all splits are in flight together.
 template <int NT>
-__device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens, int32_t B, int32_t max_tokens,
-                                           int32_t G, int32_t* __restrict__ prefix, int32_t* __restrict__ split_rec,
-                                           int32_t* __restrict__ flags, int32_t* part) {
+__device__ __forceinline__ void plan_block(const PlanArgs& pa, int32_t* part, int32_t cap) {
   const int tid = threadIdx.x;
-  if (tid == 0) flags[0] = 0;   // the flags describe the latest decode on this workspace
+  const int32_t B = pa.B, max_tokens = pa.max_tokens, G = pa.G;
+  if (tid == 0) pa.flags[0] = 0;   // the flags describe the latest decode on this workspace
   __syncthreads();
   const int per = (B + NT - 1) / NT;
   const int beg = tid * per, end = min(beg + per, B);
   int32_t local = 0;
   for (int b = beg; b < end; ++b) {
-    int32_t n = seq_lens[b];
+    int32_t n = pa.seq_lens[b];
     if (n < 1 || n > max_tokens) {
-      atomicOr(flags, MLA_FLAG_BAD_SEQ_LEN);
+      atomicOr(pa.flags, MLA_FLAG_BAD_SEQ_LEN);
       n = n < 1 ? 0 : max_tokens;
     }
     local += n;
@@ -127,26 +144,42 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ seq_lens,
     part[tid] += v;
     __syncthreads();
   }
-  const int64_t N = part[NT - 1];
+  const int32_t N = part[NT - 1];
+  const bool in_lds = B + 1 <= cap;
+  int32_t* pl = part + NT;
   int32_t run = tid > 0 ? part[tid - 1] : 0;
   for (int b = beg; b < end; ++b) {
-    int32_t n = seq_lens[b];
+    int32_t n = pa.seq_lens[b];
     n = n < 1 ? 0 : (n > max_tokens ? max_tokens : n);
-    prefix[b] = run;
-    if (N > 0) {
-      const int64_t lo = run, hi = (int64_t)run + n;
-      for (int64_t w = (lo * G + N - 1) / N; w < (hi * G + N - 1) / N; ++w) {
-        int4 r;
-        r.x = b;
-        r.y = (int32_t)lo;
-        r.z = (int32_t)hi;
-        r.w = 0;
-        *(int4*)(split_rec + 4 * w) = r;
-      }
-    }
+    pa.prefix[b] = run;
+    if (in_lds) pl[b] = run;
     run += n;
   }
-  if (tid == NT - 1) prefix[B] = part[NT - 1];
+  if (tid == NT - 1) {
+    pa.prefix[B] = N;
+    if (in_lds) pl[B] = N;
+  }
+  __threadfence_block();
+  __syncthreads();
+  if (N <= 0) return;
+  const int32_t* px = in_lds ? pl : pa.prefix;
+  for (int32_t w = tid; w < G; w += NT) {
+    const int32_t P = (int32_t)((int64_t)w * N / G);
+    int32_t lo = 0, hi = B - 1;   // last b with prefix[b] <= P
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (px[mid] <= P) lo = mid; else hi = mid - 1;
+    }
+    const int32_t s0 = px[lo], s1 = px[lo + 1];
+    const int32_t p0 = (P - s0) / pa.page_size;
+    const int32_t* pt = pa.page_table + (int64_t)lo * pa.max_pages;
+    int32_t pg[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) pg[k] = pt[min(p0 + k, pa.max_pages - 1)];
+    int4* r = (int4*)(pa.split_rec + SPLIT_REC * w);
+    r[0] = int4{lo, s0, s1, pg[0]};
+    r[1] = int4{pg[1], pg[2], 0, 0};
+  }
 }
 
 }  // namespace mla
@@ -162,13 +195,11 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
                          const int32_t* seq_id, const int32_t* pos, const int32_t* page_table,
                          int32_t num_seqs, int32_t max_pages, void* c_KV, void* k_R, int64_t row_stride,
                          int32_t num_pages, int32_t* err_flag, void* ws, size_t ws_bytes, hipStream_t s);
-hipError_t launch_plan(const int32_t* seq_lens, int32_t B, int32_t max_tokens, int32_t n_splits, int32_t* prefix,
-                       int32_t* split_rec, int32_t* flags, hipStream_t s);
+hipError_t launch_plan(const PlanArgs& pa, hipStream_t s);
 // Query absorption; for bf16 the decode plan runs in the same launch (then
 // launch_plan is not called).
 hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
-                         const void* W_UK, void* qabs, const int32_t* seq_lens, int32_t max_tokens,
-                         int32_t n_splits, int32_t* prefix, int32_t* split_rec, int32_t* flags, hipStream_t s);
+                         const void* W_UK, void* qabs, const PlanArgs& pa, hipStream_t s);
 hipError_t launch_decode_simple(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                                 const void* k_R, int64_t row_stride, int32_t num_pages,
                                 const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
