@@ -23,7 +23,7 @@ constexpr int AB_DK = 32;
 template <typename T>
 __global__ void __launch_bounds__(256) absorb_kernel(int32_t B, int32_t n_h, const T* __restrict__ q_C,
                                                      const T* __restrict__ q_R, const int32_t* __restrict__ pos_q,
-                                                     const T* __restrict__ W_UK, float qscale, float rope_base,
+                                                     const T* __restrict__ W_UK, float qscale, RopeTab rope,
                                                      T* __restrict__ qabs) {
   __shared__ float qs[AB_SEQ][D_H + 1];
   __shared__ float ws[AB_DK][D_C];
@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(256) absorb_kernel(int32_t B, int32_t n_h, con
     const T* src = q_R + ((int64_t)b * n_h + h) * D_R;
     const float x0 = to_f32(src[2 * k]), x1 = to_f32(src[2 * k + 1]);
     float cs, sn;
-    rope_cos_sin(pos_q[b], k, D_R, rope_base, &cs, &sn);
+    rope_cos_sin(pos_q[b], k, rope, &cs, &sn);
     T* dst = qabs + ((int64_t)b * n_h + h) * D_K + D_C;
     dst[2 * k] = from_f32<T>((x0 * cs - x1 * sn) * qscale);
     dst[2 * k + 1] = from_f32<T>((x0 * sn + x1 * cs) * qscale);
@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int32_t B, int32_t n_h
                                                           const bf16* __restrict__ q_R,
                                                           const int32_t* __restrict__ pos_q,
                                                           const bf16* __restrict__ W_UK, float qscale,
-                                                          float rope_base, bf16* __restrict__ qabs, PlanArgs pa) {
+                                                          RopeTab rope, bf16* __restrict__ qabs, PlanArgs pa) {
   __shared__ __attribute__((aligned(1024))) char wl[D_H * 256];
   if (blockIdx.x == 4 * n_h) {
     if (blockIdx.y == 0) plan_block<256>(pa, (int32_t*)wl, D_H * 256 / 4 - 256);
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int32_t B, int32_t n_h
       const bf16* src = q_R + ((int64_t)b * n_h + h) * D_R;
       const float x0 = (float)src[2 * k], x1 = (float)src[2 * k + 1];
       float cs, sn;
-      rope_cos_sin(pos_q[b], k, D_R, rope_base, &cs, &sn);
+      rope_cos_sin(pos_q[b], k, rope, &cs, &sn);
       bf16* dst = qabs + ((int64_t)b * n_h + h) * D_K + D_C;
       dst[2 * k] = (bf16)((x0 * cs - x1 * sn) * qscale);
       dst[2 * k + 1] = (bf16)((x0 * sn + x1 * cs) * qscale);
@@ -191,11 +191,11 @@ hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const vo
     if (e != hipSuccess) return e;
     dim3 grid(d.n_h, (B + AB_SEQ - 1) / AB_SEQ);
     absorb_kernel<float><<<grid, 256, 0, s>>>(B, d.n_h, (const float*)q_C, (const float*)q_R, pos_q,
-                                              (const float*)W_UK, qscale, d.rope_base, (float*)qabs);
+                                              (const float*)W_UK, qscale, rope_table(d.rope_base), (float*)qabs);
   } else {
     dim3 g2(4 * d.n_h + 1, (B + 63) / 64);
     absorb_mfma_kernel<<<g2, 256, 0, s>>>(B, d.n_h, (const bf16*)q_C, (const bf16*)q_R, pos_q, (const bf16*)W_UK,
-                                         qscale, d.rope_base, (bf16*)qabs, pa);
+                                         qscale, rope_table(d.rope_base), (bf16*)qabs, pa);
   }
   return hipGetLastError();
 }

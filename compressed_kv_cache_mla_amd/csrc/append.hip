@@ -28,7 +28,7 @@ __device__ void append_store(const float (*res)[AT_COL + 1], int32_t T_rows, int
                              const int32_t* __restrict__ seq_id, const int32_t* __restrict__ pos,
                              const int32_t* __restrict__ page_table, int32_t num_seqs, int32_t max_pages,
                              int32_t page_size, int32_t num_pages, T* __restrict__ c_KV, T* __restrict__ k_R,
-                             int64_t row_stride, float rope_base, int32_t* err_flag) {
+                             int64_t row_stride, const RopeTab& rope, int32_t* err_flag) {
   const int tid = threadIdx.x;
   // 256 threads: 8 tokens at a time, 32 threads per token, 2 columns per thread.
   const int tt = tid >> 5, cp = tid & 31;
@@ -51,7 +51,7 @@ __device__ void append_store(const float (*res)[AT_COL + 1], int32_t T_rows, int
     if (col0 >= D_C) {
       // k^R pair k = cp: rotate by pos * base^(-2k/64)
       float cs, sn;
-      rope_cos_sin(p, cp, D_R, rope_base, &cs, &sn);
+      rope_cos_sin(p, cp, rope, &cs, &sn);
       const float y0 = x0 * cs - x1 * sn;
       const float y1 = x0 * sn + x1 * cs;
       x0 = y0;
@@ -72,7 +72,7 @@ __global__ void __launch_bounds__(256) append_f32_kernel(
     int32_t T_rows, int32_t d_model, const float* __restrict__ h, const float* __restrict__ W_DKV,
     const float* __restrict__ W_KR, const int32_t* __restrict__ seq_id, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ page_table, int32_t num_seqs, int32_t max_pages, int32_t page_size,
-    float* __restrict__ c_KV, float* __restrict__ k_R, int64_t row_stride, int32_t num_pages, float rope_base,
+    float* __restrict__ c_KV, float* __restrict__ k_R, int64_t row_stride, int32_t num_pages, RopeTab rope,
     int32_t* err_flag) {
   __shared__ float hs[AT_TOK][AT_KC + 1];
   __shared__ float ws[AT_COL][AT_KC + 1];
@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(256) append_f32_kernel(
   }
   __syncthreads();
   append_store<float>(res, T_rows, tok0, col0, seq_id, pos, page_table, num_seqs, max_pages, page_size,
-                      num_pages, c_KV, k_R, row_stride, rope_base, err_flag);
+                      num_pages, c_KV, k_R, row_stride, rope, err_flag);
 }
 
 // ---------------------------------------------------------------- bf16 (MFMA)
@@ -127,7 +127,7 @@ __global__ void __launch_bounds__(256) append_bf16_kernel(
     int32_t T_rows, int32_t d_model, const bf16* __restrict__ h, const bf16* __restrict__ W_DKV,
     const bf16* __restrict__ W_KR, const int32_t* __restrict__ seq_id, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ page_table, int32_t num_seqs, int32_t max_pages, int32_t page_size,
-    bf16* __restrict__ c_KV, bf16* __restrict__ k_R, int64_t row_stride, int32_t num_pages, float rope_base,
+    bf16* __restrict__ c_KV, bf16* __restrict__ k_R, int64_t row_stride, int32_t num_pages, RopeTab rope,
     int32_t* err_flag) {
   __shared__ float res[AT_TOK][AT_COL + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -168,7 +168,7 @@ __global__ void __launch_bounds__(256) append_bf16_kernel(
   }
   __syncthreads();
   append_store<bf16>(res, T_rows, tok0, col0, seq_id, pos, page_table, num_seqs, max_pages, page_size,
-                     num_pages, c_KV, k_R, row_stride, rope_base, err_flag);
+                     num_pages, c_KV, k_R, row_stride, rope, err_flag);
 }
 
 // Few tokens (a decode step): the product is weight-bandwidth bound, so the
@@ -184,7 +184,7 @@ __global__ void __launch_bounds__(64 * SMALL_W) append_bf16_small_kernel(
     int32_t T_rows, int32_t d_model, const bf16* __restrict__ h, const bf16* __restrict__ W_DKV,
     const bf16* __restrict__ W_KR, const int32_t* __restrict__ seq_id, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ page_table, int32_t num_seqs, int32_t max_pages, int32_t page_size,
-    bf16* __restrict__ c_KV, bf16* __restrict__ k_R, int64_t row_stride, int32_t num_pages, float rope_base,
+    bf16* __restrict__ c_KV, bf16* __restrict__ k_R, int64_t row_stride, int32_t num_pages, RopeTab rope,
     int32_t* err_flag) {
   __shared__ float red[SMALL_W][16][17];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -235,7 +235,7 @@ __global__ void __launch_bounds__(64 * SMALL_W) append_bf16_small_kernel(
         bf16* dst;
         if (c >= D_C) {
           float cs, sn;
-          rope_cos_sin(p, (c - D_C) / 2, D_R, rope_base, &cs, &sn);
+          rope_cos_sin(p, (c - D_C) / 2, rope, &cs, &sn);
           const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
           x0 = y0;
           x1 = y1;
@@ -299,7 +299,7 @@ __global__ void __launch_bounds__(256) append_finish_kernel(
     int32_t T_rows, const float* __restrict__ part, const int32_t* __restrict__ seq_id,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ page_table, int32_t num_seqs, int32_t max_pages,
     int32_t page_size, bf16* __restrict__ c_KV, bf16* __restrict__ k_R, int64_t row_stride, int32_t num_pages,
-    float rope_base, int32_t* err_flag) {
+    RopeTab rope, int32_t* err_flag) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int t = (int)(idx / (D_K / 2)), cp = (int)(idx % (D_K / 2));
   if (t >= T_rows) return;
@@ -325,7 +325,7 @@ __global__ void __launch_bounds__(256) append_finish_kernel(
   bf16* dst;
   if (c >= D_C) {
     float cs, sn;
-    rope_cos_sin(p, (c - D_C) / 2, D_R, rope_base, &cs, &sn);
+    rope_cos_sin(p, (c - D_C) / 2, rope, &cs, &sn);
     const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
     x0 = y0;
     x1 = y1;
@@ -356,7 +356,7 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
     const int64_t n = (int64_t)T * (D_K / 2);
     append_finish_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
         T, (const float*)ws, seq_id, pos, page_table, num_seqs, max_pages, d.page_size, (bf16*)c_KV, (bf16*)k_R,
-        row_stride, num_pages, d.rope_base, err_flag);
+        row_stride, num_pages, rope_table(d.rope_base), err_flag);
     return hipGetLastError();
   }
   dim3 grid((T + AT_TOK - 1) / AT_TOK, D_K / AT_COL);
@@ -364,18 +364,18 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
     append_f32_kernel<<<grid, 256, 0, s>>>(T, d.d_model, (const float*)h, (const float*)W_DKV,
                                           (const float*)W_KR, seq_id, pos, page_table, num_seqs, max_pages,
                                           d.page_size, (float*)c_KV, (float*)k_R, row_stride, num_pages,
-                                          d.rope_base, err_flag);
+                                          rope_table(d.rope_base), err_flag);
   } else if (T <= 512 && d.d_model % (32 * SMALL_W) == 0) {
     dim3 g2((T + 15) / 16, D_K / 16);
     append_bf16_small_kernel<<<g2, 64 * SMALL_W, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV,
                                                  (const bf16*)W_KR, seq_id, pos, page_table, num_seqs, max_pages,
                                                  d.page_size, (bf16*)c_KV, (bf16*)k_R, row_stride, num_pages,
-                                                 d.rope_base, err_flag);
+                                                 rope_table(d.rope_base), err_flag);
   } else {
     append_bf16_kernel<<<grid, 256, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV,
                                            (const bf16*)W_KR, seq_id, pos, page_table, num_seqs, max_pages,
                                            d.page_size, (bf16*)c_KV, (bf16*)k_R, row_stride, num_pages,
-                                           d.rope_base, err_flag);
+                                           rope_table(d.rope_base), err_flag);
   }
   return hipGetLastError();
 }

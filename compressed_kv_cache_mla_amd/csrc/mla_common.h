@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "../../include/mla.h"
 
 namespace mla {
@@ -42,14 +44,26 @@ __device__ __forceinline__ int64_t pool_row(const int32_t* __restrict__ page_tab
   return (int64_t)pg * page_size + t % page_size;
 }
 
-// RoPE angle of pair k at position pos: pos * base^(-2k/d), in fp64.
-__device__ __forceinline__ void rope_cos_sin(int32_t pos, int k, int d, float base, float* c, float* s) {
-  double theta = pow((double)base, -2.0 * (double)k / (double)d);
-  double a = (double)pos * theta;
-  double sn, cs;
-  sincos(a, &sn, &cs);
-  *c = (float)cs;
-  *s = (float)sn;
+// RoPE frequencies theta_k = base^(-2k/d_hR), k = 0..31, formed once on the
+// host in fp64 and passed to the kernels by value.
+struct RopeTab {
+  double theta[D_R / 2];
+};
+inline RopeTab rope_table(float base) {
+  RopeTab t;
+  for (int k = 0; k < D_R / 2; ++k) t.theta[k] = std::pow((double)base, -2.0 * k / (double)D_R);
+  return t;
+}
+
+// cos / sin of the RoPE angle of pair k at position pos: the angle
+// pos * theta_k is formed and reduced to [-pi, pi] in fp64 (the angle is
+// exact to ~1e-11 for positions below 2^31), then its cosine and sine are
+// taken in fp32.
+__device__ __forceinline__ void rope_cos_sin(int32_t pos, int k, const RopeTab& rt, float* c, float* s) {
+  const double a = (double)pos * rt.theta[k];
+  const double n = rint(a * 0.15915494309189535);   // a / (2 pi), rounded
+  const float r = (float)fma(-n, 6.283185307179586, a);
+  sincosf(r, s, c);
 }
 
 // Ints per split record (see plan_block).
