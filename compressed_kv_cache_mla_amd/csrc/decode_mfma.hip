@@ -522,18 +522,26 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
     __builtin_amdgcn_s_barrier();
 
-    // ---- rescale O if any owner moved its reference max (rare)
-    int resc = 0;
+    // ---- rescale O where an owner moved its reference max (rare).  Only the
+    // heads of the owners that raised their flag are scaled: alpha_l holds
+    // this tile's factors for those owners alone (the others' are stale).
+    // (Four waves test one combined flag, fewer test one flag per owner: the
+    // forms the register allocator fits best.)
+    int resc = NW == 4 ? 0 : 1;
+    if (NW == 4) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) resc |= resc_l[w];
+      for (int w = 0; w < NW; ++w) resc |= resc_l[w];
+    }
     if (resc) {
 #pragma unroll
       for (int hb = 0; hb < NW; ++hb) {
-        const float a = alpha_l[32 * hb + (lane & 31)];
+        if (NW == 4 || resc_l[hb]) {
+          const float a = NW != 4 || resc_l[hb] ? alpha_l[32 * hb + (lane & 31)] : 1.f;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+          for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) ACC_SCALE(o[hb][db][r], a);
+            for (int r = 0; r < 16; ++r) ACC_SCALE(o[hb][db][r], a);
+        }
       }
     }
 

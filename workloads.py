@@ -47,6 +47,8 @@ class Config:
     layers: int = 1
     seed: int = 1234
     query: str = "synthetic"     # "synthetic" | "projected" (q from W^UQ, W^QR; tests only)
+    growth: int = 0              # direct mode: the row at position p of an n-token sequence is
+                                 # scaled by 2^floor(growth * p / n) (scores that keep rising)
 
     def context_lengths(self) -> np.ndarray:
         """Prior context L_b per sequence (the decode token comes on top)."""
@@ -163,8 +165,15 @@ class Workload:
 
     def latent_rows(self, rows, device=None):
         """Direct-mode cache rows [c^KV ; k^R] for global token ids ``rows``."""
-        return si.normal_rows(_key(self.cfg, "latent", self.layer), rows, D_K, 1.0, self.cfg.dtype,
-                              device or self.device)
+        x = si.normal_rows(_key(self.cfg, "latent", self.layer), rows, D_K, 1.0, self.cfg.dtype,
+                           device or self.device)
+        if self.cfg.growth:
+            # power-of-two factors: the scaled rows are exact in any dtype
+            g = np.asarray(rows.cpu() if torch.is_tensor(rows) else rows, dtype=np.int64)
+            b = np.searchsorted(self.prefix, g, side="right") - 1
+            k = (self.cfg.growth * (g - self.prefix[b])) // self.n[b]
+            x = x * torch.from_numpy(np.ldexp(1.0, k).astype(np.float32)).to(x.device, x.dtype)[:, None]
+        return x
 
     def pool_rows(self, seq: np.ndarray, pos: np.ndarray) -> np.ndarray:
         ps = self.cfg.page_size
