@@ -19,8 +19,12 @@ ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU ops.
 # -fno-honor-nans: no NaN inputs are expected (infinities still are: masked
 # scores are -inf), so fmaxf needs no quieting of its operands.
+# -amdgpu-mfma-vgpr-form: MFMA builtins accumulate in VGPRs; the decode
+# kernel's long-lived accumulators are kept in AGPRs by inline asm, so the
+# short-lived score accumulators no longer displace them.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fno-honor-nans", "-fPIC", "-shared", f"--offload-arch={ARCH}",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form",
                "-Wno-unused-command-line-argument"]
 
 

@@ -131,6 +131,13 @@ __device__ __forceinline__ float wave_rows_sum(float x) {
   } while (0)
 #define ACC_READ(dst, x) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(dst) : "a"(x))
 #define ACC_ZERO(x) asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(x))
+// O^T block += A B on the matrix cores, accumulating in place in AGPRs.  The
+// compiler does not see this as an MFMA, so the wait states it would insert
+// are written here: two ahead of the MFMA (a VALU write of a source operand
+// needs them), and ACC_DRAIN before accumulators are read back.
+#define ACC_MFMA(acc, a, b) \
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b))
+#define ACC_DRAIN() asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7")
 
 struct TileDesc {
   int32_t b, t0, n;    // sequence, first token in the sequence, rows (0 = none)
@@ -566,20 +573,17 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
-      for (int hb = 0; hb < NW; ++hb)
-        o[hb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0][db], pf[0][hb], o[hb][db], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int hb = 0; hb < NW; ++hb)
-        o[hb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1][db], pf[1][hb], o[hb][db], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+        for (int hb = 0; hb < NW; ++hb) ACC_MFMA(o[hb][db], vf[kc][db], pf[kc][hb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     // ---- segment end: write the partial (O~ unnormalised, m, l)
     if (t_now.last) {
+      ACC_DRAIN();   // the last MFMAs' results are read back below
       const int64_t slot = (int64_t)split + t_now.b;
       // O~ goes out through the wave's staged-query area (32 heads x 128
       // latent columns of bf16 at a time, 16-byte chunk c of head row h at
