@@ -144,12 +144,13 @@ def main():
               f"({per_copy / 1e6:.0f} MB each)", file=sys.stderr, flush=True)
 
         def step(i, evs=None):
+            # one mla_decode_step call: append of every sequence's newest token,
+            # query absorption, plan, split-KV attention, combine + W^UV
             wl = wls[i % copies]
-            wl.append_step()
             if evs is None:
-                wl.decode(impl=args.impl)
+                wl.step(impl=args.impl)
             else:
-                wl.decode(ev_start=evs[0], ev_stop=evs[1], impl=args.impl)
+                wl.step(ev_start=evs[0], ev_stop=evs[1], impl=args.impl)
 
         for i in range(warmup):
             step(i)

@@ -25,6 +25,7 @@ FLAG_BAD_SEQ_LEN, FLAG_BAD_PAGE, FLAG_BAD_POSITION, FLAG_BAD_SEQ_ID = 1, 2, 4, 8
 
 EXPORTED = ("mla_cache_append", "mla_cache_append_ws", "mla_cache_append_workspace_size",
             "mla_decode_workspace_size", "mla_decode", "mla_decode_ex",
+            "mla_decode_step_workspace_size", "mla_decode_step",
             "mla_read_error_flags", "mla_last_error", "mla_device_cu_count")
 
 
@@ -96,6 +97,11 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_ex.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32, vp, vp, vp, vp, sz,
                                     i32, ctypes.POINTER(mla_decode_opts), vp]
         L.mla_decode_ex.restype = ctypes.c_int
+        L.mla_decode_step_workspace_size.argtypes = [pdims, i32, i32]
+        L.mla_decode_step_workspace_size.restype = sz
+        L.mla_decode_step.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32, vp, vp,
+                                      vp, vp, sz, i32, ctypes.POINTER(mla_decode_opts), vp]
+        L.mla_decode_step.restype = ctypes.c_int
         L.mla_read_error_flags.argtypes = [vp, ctypes.POINTER(i32), vp]
         L.mla_read_error_flags.restype = ctypes.c_int
         L.mla_last_error.argtypes = []
@@ -214,6 +220,32 @@ def decode(dims: Dims, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride: int, 
         o = mla_decode_opts(_event_handle(ev_start), _event_handle(ev_stop), impl)
         _check(lib().mla_decode_ex(*args, ctypes.byref(o), _stream(stream)))
     return workspace
+
+
+def decode_step_workspace_size(dims: Dims, B: int, n_splits: int = 0) -> int:
+    d = dims.c()
+    return int(lib().mla_decode_step_workspace_size(ctypes.byref(d), B, n_splits))
+
+
+def decode_step_workspace(dims: Dims, B: int, n_splits: int = 0, device="cuda"):
+    """A zero-filled workspace for decode_step (the library needs it zeroed once)."""
+    return torch.zeros(decode_step_workspace_size(dims, B, n_splits), dtype=torch.uint8, device=device)
+
+
+def decode_step(dims: Dims, h_new, W_DKV, W_KR, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride: int,
+                num_pages: int, page_table, seq_lens, out, lse, workspace, n_splits: int = 0, stream=None,
+                ev_start=None, ev_stop=None, impl: int = 0):
+    """mla_decode_step: append each sequence's newest token (h_new[b] at
+    position pos_q[b]) to the pool, then decode; the workspace comes from
+    decode_step_workspace() (zero-filled once, reused across calls)."""
+    B = q_C.shape[0]
+    max_pages = page_table.shape[1]
+    d = dims.c()
+    o = mla_decode_opts(_event_handle(ev_start), _event_handle(ev_stop), impl)
+    _check(lib().mla_decode_step(ctypes.byref(d), B, _ptr(h_new), _ptr(W_DKV), _ptr(W_KR), _ptr(q_C), _ptr(q_R),
+                                 _ptr(pos_q), _ptr(W_UK), _ptr(W_UV), _ptr(c_KV), _ptr(k_R), row_stride, num_pages,
+                                 _ptr(page_table), max_pages, _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace),
+                                 workspace.numel(), n_splits, ctypes.byref(o), _stream(stream)))
 
 
 def read_error_flags(workspace_or_flag, stream=None) -> int:

@@ -12,7 +12,7 @@
 // W^UK's row index.  fp32 (VALU): workgroup (head h, 32 sequences), W^UK_h
 // (128 x 512) streamed through LDS in 32-row chunks; each thread owns 2 latent
 // columns for the 32 sequences, q^C comes from LDS.  bf16: the MFMA kernel below.
-#include "mla_common.h"
+#include "absorb_mfma.h"
 
 namespace mla {
 namespace {
@@ -74,17 +74,8 @@ __global__ void __launch_bounds__(256) absorb_kernel(int32_t B, int32_t n_h, con
 }
 
 // ---------------------------------------------------------------- bf16 (MFMA)
-// Workgroup (head h, latent columns 128q .. 128q+127, 64 sequences), 4 waves.
-// q~^T[c][b] = sum_d W^UK_h[d][c] q^C[b][d] as v_mfma_f32_32x32x16_bf16 with
-// M = latent column c, N = sequence, K = d.  The W^UK_h column block (128 rows
-// x 256 B = 32 KB) is copied to LDS with global_load_lds, 4 rows of 256 B per
-// copy instruction; 16-byte chunk c16 of row d sits at chunk c16 ^ 4*(d & 3),
-// which keeps the transposed reads (ds_read_b64_tr_b16, 4 rows x 4 chunks per
-// half-wave) bank-conflict free.  Wave w produces columns 128q + 32w .. +31.
-// The last workgroup of the grid runs the decode plan instead.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-
+// absorb_mfma.h: workgroup (head, latent-column quarter, 64 sequences).  The
+// last workgroup of the grid runs the decode plan instead.
 __global__ void __launch_bounds__(256) absorb_mfma_kernel(int32_t B, int32_t n_h, const bf16* __restrict__ q_C,
                                                           const bf16* __restrict__ q_R,
                                                           const int32_t* __restrict__ pos_q,
@@ -95,90 +86,7 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int32_t B, int32_t n_h
     if (blockIdx.y == 0) plan_block<256>(pa, (int32_t*)wl, D_H * 256 / 4 - 256);
     return;
   }
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.x >> 2, cq = blockIdx.x & 3;
-  const int b0 = blockIdx.y * 64;
-  const int nb = min(64, B - b0);
-  // W^UK_h[:, 128cq .. 128cq+127] -> LDS (2048 chunks of 16 B; 8 copy instructions per wave)
-  const char* wsrc = (const char*)(W_UK + (int64_t)h * D_H * D_C) + 256 * cq;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int sigma = (wave * 8 + k) * 64 + lane;
-    const int d = sigma >> 4, pos = sigma & 15;
-    const int c16 = pos ^ ((d & 3) << 2);
-    __builtin_amdgcn_global_load_lds((const void*)(wsrc + (int64_t)d * 1024 + c16 * 16),
-                                     (lds_void_t*)(wl + (wave * 8 + k) * 1024), 16, 0, 0);
-  }
-  // q^C fragments: lane -> sequence b0 + 32*nblk + (lane & 31), d = 16*ks + 8*(lane >> 5)
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int nblk = 0; nblk < 2; ++nblk) {
-    const int b = min(b0 + 32 * nblk + (lane & 31), B - 1);
-    const bf16* qp = q_C + ((int64_t)b * n_h + h) * D_H + 8 * (lane >> 5);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[nblk][ks] = *(const bf16x8*)(qp + 16 * ks);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // transposed-read source address: row d = 16ks + 8*(lane>>5) + 4rr + ((lane&15)>>2),
-  // local columns 32w + 16*((lane>>4)&1) + 4*(lane&3)
-  const int t_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
-  const int t_c16 = 4 * wave + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int t_half = (lane & 1) * 8;
-  f32x16 acc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    bf16x8 af;
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int d = 16 * ks + t_row + 4 * rr;
-      const int c16 = t_c16 ^ ((d & 3) << 2);
-      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(wl + d * 256 + c16 * 16 + t_half));
-      const bf16x4 vb = __builtin_bit_cast(bf16x4, v);
-      af[4 * rr + 0] = vb[0];
-      af[4 * rr + 1] = vb[1];
-      af[4 * rr + 2] = vb[2];
-      af[4 * rr + 3] = vb[3];
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[j][ks], acc[j], 0, 0, 0);
-  }
-  // C layout: lane -> sequence (lane & 31) of block j, latent rows (r/4)*8 + 4*(lane>>5) + r%4
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int bb = 32 * j + (lane & 31);
-    if (bb < nb) {
-      bf16* dst = qabs + ((int64_t)(b0 + bb) * n_h + h) * D_K + 128 * cq + 32 * wave + 4 * (lane >> 5);
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 o;
-        o[0] = (bf16)(acc[j][4 * r4 + 0] * qscale);
-        o[1] = (bf16)(acc[j][4 * r4 + 1] * qscale);
-        o[2] = (bf16)(acc[j][4 * r4 + 2] * qscale);
-        o[3] = (bf16)(acc[j][4 * r4 + 3] * qscale);
-        *(bf16x4*)(dst + 8 * r4) = o;
-      }
-    }
-  }
-  // RoPE half (32 pairs per sequence), by the column-quarter-0 workgroups
-  if (cq == 0) {
-    for (int i = tid; i < nb * (D_R / 2); i += 256) {
-      const int bb = i / (D_R / 2), k = i % (D_R / 2);
-      const int b = b0 + bb;
-      const bf16* src = q_R + ((int64_t)b * n_h + h) * D_R;
-      const float x0 = (float)src[2 * k], x1 = (float)src[2 * k + 1];
-      float cs, sn;
-      rope_cos_sin(pos_q[b], k, rope, &cs, &sn);
-      bf16* dst = qabs + ((int64_t)b * n_h + h) * D_K + D_C;
-      dst[2 * k] = (bf16)((x0 * cs - x1 * sn) * qscale);
-      dst[2 * k + 1] = (bf16)((x0 * sn + x1 * cs) * qscale);
-    }
-  }
+  absorb_mfma_block(blockIdx.x, blockIdx.y, B, n_h, q_C, q_R, pos_q, W_UK, qscale, rope, qabs, wl);
 }
 
 }  // namespace

@@ -13,7 +13,7 @@
 // RoPE pairs never straddle tiles).  The epilogue stages the fp32 tile in LDS,
 // rotates the k^R pairs (angles in fp64), rounds to the cache type and writes
 // each token's 64 columns (128 B for bf16) into its pool row.
-#include "mla_common.h"
+#include "append_splitk.h"
 
 namespace mla {
 namespace {
@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(256) append_bf16_kernel(
 // global memory, up to SMALL_KB K-steps per batch) before its MFMAs, so one
 // memory latency covers its slice; the 16 partial sums are added in LDS.
 constexpr int SMALL_W = 16;
-constexpr int SMALL_KB = 10;
+constexpr int SMALL_KB = SK_KB;
 
 __global__ void __launch_bounds__(64 * SMALL_W) append_bf16_small_kernel(
     int32_t T_rows, int32_t d_model, const bf16* __restrict__ h, const bf16* __restrict__ W_DKV,
@@ -250,91 +250,22 @@ __global__ void __launch_bounds__(64 * SMALL_W) append_bf16_small_kernel(
   }
 }
 
-// Decode-step append with a workspace: the product is split over d_model as
-// well, so that every workgroup reads only its K-chunk of h and W and the
-// weight stream is spread over all compute units.  Workgroup (16 output
-// columns, K-chunk kc, 16 tokens), 4 waves (quarters of the chunk, all loads
-// issued before the MFMAs); the chunk sums go to part[kc][t][576] in fp32 and
-// append_finish_kernel adds the SK_SPLIT chunks in a fixed order, applies
-// RoPE to the k^R columns and stores the rows (deterministic, no atomics).
-constexpr int SK_SPLIT = 8;
-
+// Decode-step append with a workspace: split over d_model (append_splitk.h),
+// chunk sums in the workspace, then one pass that adds them in a fixed order,
+// applies RoPE and stores the rows (deterministic, no float atomics).
 __global__ void __launch_bounds__(256) append_splitk_kernel(int32_t T_rows, int32_t d_model,
                                                             const bf16* __restrict__ h,
                                                             const bf16* __restrict__ W_DKV,
                                                             const bf16* __restrict__ W_KR, float* __restrict__ part) {
-  __shared__ float red[4][16][17];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col0 = blockIdx.x * 16, kc = blockIdx.y, tok0 = blockIdx.z * 16;
-  const bf16* W = col0 < D_C ? W_DKV + (int64_t)col0 * d_model : W_KR + (int64_t)(col0 - D_C) * d_model;
-  const int kchunk = d_model / SK_SPLIT, kw = kchunk / 4, nks = kw / 32;
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int64_t k0 = (int64_t)kc * kchunk + wave * kw + kq;
-  const bf16* wrow = W + (int64_t)r16 * d_model + k0;
-  const bf16* hrow = h + (int64_t)min(tok0 + r16, T_rows - 1) * d_model + k0;
-  f32x4 acc = {0, 0, 0, 0};
-  for (int b0 = 0; b0 < nks; b0 += SMALL_KB) {
-    bf16x8 wv[SMALL_KB], hv[SMALL_KB];
-#pragma unroll
-    for (int i = 0; i < SMALL_KB; ++i)
-      if (b0 + i < nks) {
-        wv[i] = *(const bf16x8*)(wrow + 32 * (b0 + i));
-        hv[i] = *(const bf16x8*)(hrow + 32 * (b0 + i));
-      }
-#pragma unroll
-    for (int i = 0; i < SMALL_KB; ++i)
-      if (b0 + i < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv[i], wv[i], acc, 0, 0, 0);
-  }
-  // C layout: lane holds output column lane%16, tokens 4*(lane/16) + i
-#pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][r16] = acc[i];
-  __syncthreads();
-  const int r = tid >> 4, c = tid & 15;
-  const int t = tok0 + r;
-  if (t < T_rows)
-    part[((int64_t)kc * T_rows + t) * D_K + col0 + c] = (red[0][r][c] + red[1][r][c]) + (red[2][r][c] + red[3][r][c]);
+  __shared__ float red[4 * 16 * 17];
+  append_splitk_block(blockIdx.x, blockIdx.y, blockIdx.z, T_rows, d_model, h, W_DKV, W_KR, part, red);
 }
 
-__global__ void __launch_bounds__(256) append_finish_kernel(
-    int32_t T_rows, const float* __restrict__ part, const int32_t* __restrict__ seq_id,
-    const int32_t* __restrict__ pos, const int32_t* __restrict__ page_table, int32_t num_seqs, int32_t max_pages,
-    int32_t page_size, bf16* __restrict__ c_KV, bf16* __restrict__ k_R, int64_t row_stride, int32_t num_pages,
-    RopeTab rope, int32_t* err_flag) {
+__global__ void __launch_bounds__(256) append_finish_kernel(int32_t T_rows, const float* __restrict__ part,
+                                                            AppendDst a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int t = (int)(idx / (D_K / 2)), cp = (int)(idx % (D_K / 2));
-  if (t >= T_rows) return;
-  float x0 = 0.f, x1 = 0.f;
-#pragma unroll
-  for (int kc = 0; kc < SK_SPLIT; ++kc) {
-    const float2 v = *(const float2*)(part + ((int64_t)kc * T_rows + t) * D_K + 2 * cp);
-    x0 += v.x;
-    x1 += v.y;
-  }
-  const int32_t sq = seq_id ? seq_id[t] : t;
-  const int32_t p = pos[t];
-  if (sq < 0 || sq >= num_seqs) {
-    if (err_flag && cp == 0) atomicOr(err_flag, MLA_FLAG_BAD_SEQ_ID);
-    return;
-  }
-  if (p < 0 || p >= max_pages * page_size) {
-    if (err_flag && cp == 0) atomicOr(err_flag, MLA_FLAG_BAD_POSITION);
-    return;
-  }
-  const int64_t row = pool_row(page_table, max_pages, num_pages, page_size, sq, p, err_flag);
-  const int c = 2 * cp;
-  bf16* dst;
-  if (c >= D_C) {
-    float cs, sn;
-    rope_cos_sin(p, (c - D_C) / 2, rope, &cs, &sn);
-    const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
-    x0 = y0;
-    x1 = y1;
-    dst = k_R + row * row_stride + (c - D_C);
-  } else {
-    dst = c_KV + row * row_stride + c;
-  }
-  dst[0] = (bf16)x0;
-  dst[1] = (bf16)x1;
+  if (t < T_rows) append_finish_pair(T_rows, t, cp, part, a);
 }
 
 }  // namespace
@@ -354,9 +285,9 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
     append_splitk_kernel<<<g1, 256, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV, (const bf16*)W_KR,
                                            (float*)ws);
     const int64_t n = (int64_t)T * (D_K / 2);
-    append_finish_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-        T, (const float*)ws, seq_id, pos, page_table, num_seqs, max_pages, d.page_size, (bf16*)c_KV, (bf16*)k_R,
-        row_stride, num_pages, rope_table(d.rope_base), err_flag);
+    const AppendDst a{seq_id, pos, page_table, num_seqs, max_pages, d.page_size, num_pages, (bf16*)c_KV,
+                      (bf16*)k_R, row_stride, rope_table(d.rope_base), err_flag};
+    append_finish_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(T, (const float*)ws, a);
     return hipGetLastError();
   }
   dim3 grid((T + AT_TOK - 1) / AT_TOK, D_K / AT_COL);

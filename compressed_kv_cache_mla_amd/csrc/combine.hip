@@ -57,12 +57,25 @@ __device__ __forceinline__ MergeInfo merge_info(int32_t b, int32_t h, int32_t n_
   return mi;
 }
 
+// Decode step: the append's flags (word 1 of the flag area) join the decode's
+// (word 0) once both launches before this one are done; word 1 goes back to 0.
+__device__ __forceinline__ void merge_step_flags(int32_t* flags) {
+  if (flags && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    const int32_t v = flags[1];
+    if (v) {
+      atomicOr(flags, v);
+      flags[1] = 0;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256) combine_f32_kernel(int32_t B, int32_t n_h, const int32_t* __restrict__ prefix,
                                                           int32_t G, const float* __restrict__ part_ml,
                                                           const float* __restrict__ part_o,
                                                           const float* __restrict__ W_UV, float* __restrict__ out,
-                                                          float* __restrict__ lse) {
+                                                          float* __restrict__ lse, int32_t* merge_flags) {
   __shared__ float ol[CB_SEQ][D_C + 4];
+  merge_step_flags(merge_flags);
   __shared__ MergeInfo info[CB_SEQ];
   const int tid = threadIdx.x;
   const int h = blockIdx.x;
@@ -135,8 +148,9 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
                                                             int32_t G, const float* __restrict__ part_ml,
                                                             const bf16* __restrict__ part_o,
                                                             const bf16* __restrict__ W_UV, float* __restrict__ out,
-                                                            float* __restrict__ lse) {
+                                                            float* __restrict__ lse, int32_t* merge_flags) {
   constexpr int NBQ = CS / 16;
+  merge_step_flags(merge_flags);
   __shared__ __attribute__((aligned(16))) char ol[CS * D_C * 2];
   __shared__ int empty_l[CS];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -227,22 +241,22 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
 
 hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, int32_t n_splits,
                           const float* part_ml, const void* part_o, const void* W_UV, float* out,
-                          float* lse, hipStream_t s) {
+                          float* lse, int32_t* merge_flags, hipStream_t s) {
   if (d.dtype == MLA_FP32) {
     dim3 grid(d.n_h, (B + CB_SEQ - 1) / CB_SEQ);
     combine_f32_kernel<<<grid, 256, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const float*)part_o,
-                                            (const float*)W_UV, out, lse);
+                                            (const float*)W_UV, out, lse, merge_flags);
   } else {
     // 32 sequences per workgroup (W^UV read once per 32) unless that leaves
     // fewer workgroups than compute units
     if (B > 16 && d.n_h * ((B + 31) / 32) >= 256) {
       dim3 grid(d.n_h, (B + 31) / 32);
       combine_mfma_kernel<32><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
-                                                    (const bf16*)W_UV, out, lse);
+                                                    (const bf16*)W_UV, out, lse, merge_flags);
     } else {
       dim3 grid(d.n_h, (B + 15) / 16);
       combine_mfma_kernel<16><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
-                                                    (const bf16*)W_UV, out, lse);
+                                                    (const bf16*)W_UV, out, lse, merge_flags);
     }
   }
   return hipGetLastError();

@@ -6,7 +6,7 @@
 
 #include <string>
 
-#include "mla_common.h"
+#include "append_splitk.h"
 
 namespace {
 
@@ -137,11 +137,19 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, const void* q_C, const vo
                        seq_lens, out, lse, workspace, ws_bytes, n_splits, nullptr, stream);
 }
 
-mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
-                         const void* W_UK, const void* W_UV, const void* c_KV, const void* k_R, int64_t row_stride,
-                         int32_t num_pages, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
-                         float* out, float* lse, void* workspace, size_t ws_bytes, int32_t n_splits,
-                         const mla_decode_opts* opts, void* stream) {
+// Inputs of the append half of a decode step.
+struct StepAppendIn {
+  const void* h_new;
+  const void* W_DKV;
+  const void* W_KR;
+};
+
+static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
+                              const void* W_UK, const void* W_UV, const void* c_KV, const void* k_R,
+                              int64_t row_stride, int32_t num_pages, const int32_t* page_table, int32_t max_pages,
+                              const int32_t* seq_lens, float* out, float* lse, void* workspace, size_t ws_bytes,
+                              int32_t n_splits, const mla_decode_opts* opts, const StepAppendIn* step,
+                              void* stream) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
@@ -149,6 +157,12 @@ mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const
     return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(q_C) || !aligned16(q_R) || !aligned16(W_UK) || !aligned16(W_UV) || !aligned16(out))
     return fail(MLA_ERR_INVALID_ARG, "q_C / q_R / W_UK / W_UV / out not 16-byte aligned");
+  if (step) {
+    if (!step->h_new || !step->W_DKV || !step->W_KR)
+      return fail(MLA_ERR_INVALID_ARG, "null pointer among h_new, W_DKV, W_KR");
+    if (!aligned16(step->h_new) || !aligned16(step->W_DKV) || !aligned16(step->W_KR))
+      return fail(MLA_ERR_INVALID_ARG, "h_new / W_DKV / W_KR not 16-byte aligned");
+  }
   if (((uintptr_t)workspace & 255) != 0) return fail(MLA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   st = check_pool(dims, c_KV, k_R, row_stride, num_pages);
   if (st != MLA_OK) return st;
@@ -158,7 +172,7 @@ mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const
     return fail(MLA_ERR_UNSUPPORTED, "B*max_pages*page_size >= 2^31 tokens");
   if (n_splits <= 0) n_splits = default_splits();
   if (n_splits > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d too large", n_splits);
-  const mla::DecodeWs L = mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims));
+  const mla::DecodeWs L = mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims), step != nullptr);
   if (ws_bytes < L.total)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
 
@@ -183,8 +197,21 @@ mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const
   pa.page_table = page_table;
   pa.max_pages = max_pages;
   pa.page_size = dims->page_size;
-  hipError_t e = mla::launch_absorb(*dims, B, q_C, q_R, pos_q, W_UK, qabs, pa, s);
   if (opts && opts->impl != 0 && opts->impl != 1) return fail(MLA_ERR_INVALID_ARG, "opts->impl=%d", opts->impl);
+  hipError_t e = hipSuccess;
+  if (step && mla::step_prep_supported(*dims)) {
+    // append (split-K, finished in the same launch), absorption and plan in one launch
+    const mla::AppendDst dst{nullptr, pos_q, page_table, B, max_pages, dims->page_size, num_pages,
+                             (mla::bf16*)c_KV, (mla::bf16*)k_R, row_stride, mla::rope_table(dims->rope_base),
+                             flags + 1};
+    e = mla::launch_step_prep(*dims, B, step->h_new, step->W_DKV, step->W_KR, q_C, q_R, pos_q, W_UK, qabs, pa,
+                              (float*)(ws + L.app_part), (int32_t*)(ws + L.app_cnt), dst, s);
+  } else {
+    if (step)
+      e = mla::launch_append(*dims, B, step->h_new, step->W_DKV, step->W_KR, nullptr, pos_q, page_table, B,
+                             max_pages, (void*)c_KV, (void*)k_R, row_stride, num_pages, flags + 1, nullptr, 0, s);
+    if (e == hipSuccess) e = mla::launch_absorb(*dims, B, q_C, q_R, pos_q, W_UK, qabs, pa, s);
+  }
   if (e == hipSuccess && opts && opts->ev_start) e = hipEventRecord((hipEvent_t)opts->ev_start, s);
   if (e == hipSuccess) {
     const bool mfma = dims->dtype == MLA_BF16 && (dims->n_h == 32 || dims->n_h == 64 || dims->n_h == 128) &&
@@ -197,9 +224,36 @@ mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const
                                     prefix, n_splits, part_ml, part_o, flags, s);
   }
   if (e == hipSuccess && opts && opts->ev_stop) e = hipEventRecord((hipEvent_t)opts->ev_stop, s);
-  if (e == hipSuccess) e = mla::launch_combine(*dims, B, prefix, n_splits, part_ml, part_o, W_UV, out, lse, s);
+  if (e == hipSuccess)
+    e = mla::launch_combine(*dims, B, prefix, n_splits, part_ml, part_o, W_UV, out, lse, step ? flags : nullptr, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
+                         const void* W_UK, const void* W_UV, const void* c_KV, const void* k_R, int64_t row_stride,
+                         int32_t num_pages, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                         float* out, float* lse, void* workspace, size_t ws_bytes, int32_t n_splits,
+                         const mla_decode_opts* opts, void* stream) {
+  return decode_impl(dims, B, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride, num_pages, page_table, max_pages,
+                     seq_lens, out, lse, workspace, ws_bytes, n_splits, opts, nullptr, stream);
+}
+
+size_t mla_decode_step_workspace_size(const mla_dims* dims, int32_t B, int32_t n_splits) {
+  if (check_dims(dims) != MLA_OK || B < 1) return 0;
+  if (n_splits <= 0) n_splits = default_splits();
+  return mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims), true).total;
+}
+
+mla_status mla_decode_step(const mla_dims* dims, int32_t B, const void* h_new, const void* W_DKV, const void* W_KR,
+                           const void* q_C, const void* q_R, const int32_t* pos_q, const void* W_UK,
+                           const void* W_UV, void* c_KV, void* k_R, int64_t row_stride, int32_t num_pages,
+                           const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, float* out,
+                           float* lse, void* workspace, size_t ws_bytes, int32_t n_splits,
+                           const mla_decode_opts* opts, void* stream) {
+  const StepAppendIn in{h_new, W_DKV, W_KR};
+  return decode_impl(dims, B, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride, num_pages, page_table, max_pages,
+                     seq_lens, out, lse, workspace, ws_bytes, n_splits, opts, &in, stream);
 }
 
 mla_status mla_read_error_flags(void* workspace_or_flag, int32_t* flags, void* stream) {

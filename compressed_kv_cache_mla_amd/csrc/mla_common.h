@@ -69,15 +69,20 @@ __device__ __forceinline__ void rope_cos_sin(int32_t pos, int k, const RopeTab& 
 // Ints per split record (see plan_block).
 constexpr int SPLIT_REC = 8;
 
-// Decode workspace layout (bytes, each part 256-aligned).
+// d_model chunks of the split-K append (append_splitk.h).
+constexpr int APPEND_SK_SPLIT = 8;
+
+// Decode workspace layout (bytes, each part 256-aligned).  flags: word 0 the
+// decode's error flags, word 1 (decode step only) the append's.  The decode
+// step adds the split-K append's chunk sums and its per-tile counters.
 struct DecodeWs {
-  size_t flags, prefix, splits, qabs, part_ml, part_o, total;
+  size_t flags, prefix, splits, qabs, part_ml, part_o, app_part, app_cnt, total;
   int32_t n_slots;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline DecodeWs decode_ws_layout(int32_t B, int32_t n_h, int32_t n_splits, int elt) {
+inline DecodeWs decode_ws_layout(int32_t B, int32_t n_h, int32_t n_splits, int elt, bool step = false) {
   DecodeWs w;
   w.n_slots = n_splits + B;
   size_t off = 0;
@@ -87,6 +92,12 @@ inline DecodeWs decode_ws_layout(int32_t B, int32_t n_h, int32_t n_splits, int e
   w.qabs = off;    off += align256((size_t)B * n_h * D_K * elt);
   w.part_ml = off; off += align256((size_t)w.n_slots * n_h * 2 * 4);
   w.part_o = off;  off += align256((size_t)w.n_slots * n_h * D_C * elt);   // partial O~ in the cache type
+  w.app_part = w.app_cnt = off;
+  if (step) {
+    off += align256((size_t)APPEND_SK_SPLIT * B * D_K * 4);                // fp32 chunk sums
+    w.app_cnt = off;
+    off += align256((size_t)((B + 15) / 16) * (D_K / 16) * 4);             // one counter per tile
+  }
   w.total = off;
   return w;
 }
@@ -214,6 +225,15 @@ hipError_t launch_plan(const PlanArgs& pa, hipStream_t s);
 // launch_plan is not called).
 hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
                          const void* W_UK, void* qabs, const PlanArgs& pa, hipStream_t s);
+// Decode step, first launch: the split-K append of each sequence's newest
+// token (finished in the same launch), the query absorption and the plan, as
+// one grid (bf16, d_model a multiple of 1024; step_prep_supported()).
+struct AppendDst;
+bool step_prep_supported(const mla_dims& d);
+hipError_t launch_step_prep(const mla_dims& d, int32_t B, const void* h_new, const void* W_DKV, const void* W_KR,
+                            const void* q_C, const void* q_R, const int32_t* pos_q, const void* W_UK, void* qabs,
+                            const PlanArgs& pa, float* app_part, int32_t* app_cnt, const AppendDst& dst,
+                            hipStream_t s);
 hipError_t launch_decode_simple(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                                 const void* k_R, int64_t row_stride, int32_t num_pages,
                                 const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
@@ -224,7 +244,9 @@ hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, co
                               const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
                               const int32_t* split_rec, int32_t n_splits, float* part_ml, void* part_o,
                               int32_t* flags, hipStream_t s);
+// merge_flags: NULL, or (decode step) the flag area whose word 1 holds the
+// append's flags, to be OR-ed into word 0 and cleared.
 hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, int32_t n_splits,
                           const float* part_ml, const void* part_o, const void* W_UV, float* out,
-                          float* lse, hipStream_t s);
+                          float* lse, int32_t* merge_flags, hipStream_t s);
 }  // namespace mla

@@ -1,0 +1,99 @@
+// Decode step, first launch: everything the attention kernel waits for, as one
+// grid of independent workgroups.
+//  * workgroup 0: the decode plan (prefix sums, split records; mla_common.h);
+//  * then the split-K append of each sequence's newest token (append_splitk.h):
+//    c^KV = W^DKV h and k^R = RoPE(W^KR h) ("DeepSeek-V2：在“大力出奇迹”的AI军备竞赛中，
+//    四两拨千斤" (liang.world), ch.2 §2-§3), the last workgroup of each
+//    (column, token) tile adding the chunks and storing the rows;
+//  * then the query absorption q~ = W^UK^T q^C and RoPE(q^R) (absorb_mfma.h;
+//    ch.2 §2 absorption paragraph).
+// None of the three reads what another writes, so one launch replaces three
+// (append, append finish, absorb + plan) and their latency chains overlap.
+// The attention kernel reads the new rows after this launch has completed.
+#include "absorb_mfma.h"
+#include "append_splitk.h"
+
+namespace mla {
+namespace {
+
+struct StepPrepArgs {
+  // plan
+  PlanArgs pa;
+  // append
+  const bf16* h_new;
+  const bf16* W_DKV;
+  const bf16* W_KR;
+  float* app_part;
+  int32_t* app_cnt;
+  AppendDst dst;
+  int32_t n_app;        // append workgroups: SK_SPLIT * (D_K / 16) * ceil(B / 16)
+  int32_t d_model;
+  // absorb
+  const bf16* q_C;
+  const bf16* q_R;
+  const int32_t* pos_q;
+  const bf16* W_UK;
+  bf16* qabs;
+  float qscale;
+  int32_t B, n_h;
+};
+
+__global__ void __launch_bounds__(256) step_prep_kernel(StepPrepArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[D_H * 256];   // absorb's W^UK block; reused by the others
+  __shared__ int last_flag;
+  int bid = blockIdx.x;
+  if (bid == 0) {
+    plan_block<256>(a.pa, (int32_t*)smem, D_H * 256 / 4 - 256);
+    return;
+  }
+  bid -= 1;
+  if (bid < a.n_app) {
+    // the SK_SPLIT chunks of a tile are neighbours in the grid
+    const int kc = bid % SK_SPLIT;
+    const int col_blk = (bid / SK_SPLIT) % (D_K / 16);
+    const int tok_blk = bid / (SK_SPLIT * (D_K / 16));
+    append_splitk_block<true>(col_blk, kc, tok_blk, a.B, a.d_model, a.h_new, a.W_DKV, a.W_KR, a.app_part, (float*)smem);
+    append_splitk_finish_tile(col_blk, tok_blk, a.B, a.app_part, a.app_cnt, a.dst, &last_flag);
+    return;
+  }
+  bid -= a.n_app;
+  const int nx = 4 * a.n_h;
+  absorb_mfma_block(bid % nx, bid / nx, a.B, a.n_h, a.q_C, a.q_R, a.pos_q, a.W_UK, a.qscale, a.dst.rope, a.qabs,
+                    smem);
+}
+
+}  // namespace
+
+bool step_prep_supported(const mla_dims& d) {
+  return d.dtype == MLA_BF16 && d.d_model % (SK_SPLIT * 4 * 32) == 0;
+}
+
+hipError_t launch_step_prep(const mla_dims& d, int32_t B, const void* h_new, const void* W_DKV, const void* W_KR,
+                            const void* q_C, const void* q_R, const int32_t* pos_q, const void* W_UK, void* qabs,
+                            const PlanArgs& pa, float* app_part, int32_t* app_cnt, const AppendDst& dst,
+                            hipStream_t s) {
+  StepPrepArgs a;
+  a.pa = pa;
+  a.h_new = (const bf16*)h_new;
+  a.W_DKV = (const bf16*)W_DKV;
+  a.W_KR = (const bf16*)W_KR;
+  a.app_part = app_part;
+  a.app_cnt = app_cnt;
+  a.dst = dst;
+  a.n_app = SK_SPLIT * (D_K / 16) * ((B + 15) / 16);
+  a.d_model = d.d_model;
+  a.q_C = (const bf16*)q_C;
+  a.q_R = (const bf16*)q_R;
+  a.pos_q = pos_q;
+  a.W_UK = (const bf16*)W_UK;
+  a.qabs = (bf16*)qabs;
+  a.qscale = d.softmax_scale * LOG2E;
+  a.B = B;
+  a.n_h = d.n_h;
+  const int64_t n_abs = (int64_t)4 * d.n_h * ((B + 63) / 64);
+  const int64_t grid = 1 + (int64_t)a.n_app + n_abs;
+  step_prep_kernel<<<dim3((unsigned)grid), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

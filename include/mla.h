@@ -190,6 +190,43 @@ mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const
                          const mla_decode_opts* opts, void* stream);
 
 /*
+ * mla_decode_step_workspace_size -- bytes of device workspace mla_decode_step
+ * needs for batch B and n_splits (0 = default); 0 for invalid dims.
+ *
+ * mla_decode_step -- one whole decode step: append each sequence's newest
+ * token to the latent cache, then mla_decode.  Token b's state h_new[b] is
+ * projected and stored exactly as mla_cache_append_ws with T = B, seq_id =
+ * NULL (row b is sequence b) and pos = pos_q (liang.world ch.2 §2 eq. for
+ * c_t^KV; tuntang.top MLA section, k_t formula), and the decode that follows
+ * attends over seq_lens[b] tokens, the new one included (normally seq_lens[b]
+ * = pos_q[b] + 1).  Results are bitwise those of mla_cache_append_ws followed
+ * by mla_decode_ex with the same arguments.  For bf16 with d_model a multiple
+ * of 1024 the append's split-K product (finished inside the same launch by the
+ * last workgroup of each output tile), the query absorption and the plan run
+ * as one launch, followed by the attention and combine launches; otherwise the
+ * append is its own launch before the decode's.
+ *   h_new        [B, d_model]  dtype   device
+ *   W_DKV, W_KR  as for mla_cache_append
+ *   c_KV, k_R    the pool, written (token pos_q[b] of sequence b) and read
+ *   the other arguments as for mla_decode_ex (opts may be NULL).
+ *   workspace    ws_bytes >= mla_decode_step_workspace_size(dims, B, n_splits),
+ *                256-byte aligned device memory, ZERO-FILLED ONCE after
+ *                allocation: it holds counters of the in-launch append
+ *                reduction, which every completed call leaves at zero again.
+ * Error flags: an append position outside [0, max_pages*page_size) skips that
+ * row and raises MLA_FLAG_BAD_POSITION; it and the decode's flags are read
+ * from the workspace with mla_read_error_flags.  Calls that share one
+ * workspace must be ordered (e.g. on one stream).
+ */
+size_t mla_decode_step_workspace_size(const mla_dims* dims, int32_t B, int32_t n_splits);
+mla_status mla_decode_step(const mla_dims* dims, int32_t B, const void* h_new, const void* W_DKV,
+                           const void* W_KR, const void* q_C, const void* q_R, const int32_t* pos_q,
+                           const void* W_UK, const void* W_UV, void* c_KV, void* k_R, int64_t row_stride,
+                           int32_t num_pages, const int32_t* page_table, int32_t max_pages,
+                           const int32_t* seq_lens, float* out, float* lse, void* workspace, size_t ws_bytes,
+                           int32_t n_splits, const mla_decode_opts* opts, void* stream);
+
+/*
  * mla_read_error_flags -- wait for `stream`, then copy the device error flags
  * of a decode workspace (or an append err_flag word) to *flags and clear them.
  */

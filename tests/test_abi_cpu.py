@@ -100,6 +100,38 @@ def test_workspace_size_grows_with_batch_and_splits():
     assert L.mla_decode_workspace_size(ctypes.byref(_dims(d_c=1)), 64, 256) == 0
 
 
+def _step(dims, ws_bytes=1 << 30, ptr=16, B=2, n_splits=8, stride=576, h_new=True):
+    L = mla.lib()
+    p = ctypes.c_void_p(ptr * 4096) if ptr else None
+    h = p if h_new else None
+    return L.mla_decode_step(ctypes.byref(dims) if dims is not None else None, B, h, p, p, p, p, p, p, p, p, p,
+                             stride, 10, p, 4, p, p, None, ctypes.c_void_p(1 << 20), ws_bytes, n_splits, None, None)
+
+
+def test_decode_step_rejects_bad_arguments_before_launching():
+    L = mla.lib()
+    assert _step(None) == mla.MLA_ERR_INVALID_ARG
+    assert _step(_dims(d_c=256)) == mla.MLA_ERR_UNSUPPORTED
+    assert _step(_dims(), B=0) == mla.MLA_ERR_INVALID_ARG
+    assert _step(_dims(), h_new=False) == mla.MLA_ERR_INVALID_ARG
+    assert b"h_new" in L.mla_last_error()
+    assert _step(_dims(), stride=580) == mla.MLA_ERR_INVALID_ARG
+    need = L.mla_decode_step_workspace_size(ctypes.byref(_dims()), 2, 8)
+    assert _step(_dims(), ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE
+
+
+def test_decode_step_workspace_holds_the_append_reduction():
+    L = mla.lib()
+    d = _dims()
+    for B in (1, 16, 17, 64, 200):
+        dec = L.mla_decode_workspace_size(ctypes.byref(d), B, 256)
+        step = L.mla_decode_step_workspace_size(ctypes.byref(d), B, 256)
+        # 8 fp32 chunk sums per output element and one counter per 16 x 16 tile
+        assert step >= dec + 8 * B * 576 * 4 + ((B + 15) // 16) * 36 * 4
+        assert step - dec < 8 * B * 576 * 4 + ((B + 15) // 16) * 36 * 4 + 512
+    assert L.mla_decode_step_workspace_size(ctypes.byref(_dims(d_c=1)), 4, 256) == 0
+
+
 # ---- the split arithmetic the decode and combine kernels share
 def _split_begin(w, N, G):
     return (w * N) // G

@@ -145,6 +145,51 @@ def test_bf16_rising_scores_rescale(n_h):
         assert np.max(np.abs(res[k][1] - res[1][1])) < 1e-3 * np.max(np.abs(res[1][1]))
 
 
+@pytest.mark.parametrize("d_model,B", [(1024, 7), (1024, 20), (512, 7)])
+def test_decode_step_equals_append_then_decode(d_model, B):
+    # mla_decode_step (one launch for append + absorption + plan when d_model is
+    # a multiple of 1024, separate launches otherwise) against the same inputs
+    # through mla_cache_append_ws and mla_decode: bitwise-equal cache rows and
+    # outputs, both within the oracle bound, and again on a second call (the
+    # in-launch reduction counters are reset by each call)
+    cfg = W.scaled(W.CONFIGS["b64_ragged"], name=f"step_d{d_model}_b{B}", d_model=d_model, B=B, lens=(40, 700),
+                   seed=600 + B + d_model)
+    _say(f"case {cfg.name}")
+    wl = W.Workload(cfg, n_splits=37)
+    rows = torch.from_numpy(wl.pool_rows(np.arange(B), wl.n - 1)).to(wl.device)
+    wl.pool[rows] = 0
+    wl.append_step()
+    wl.decode()
+    torch.cuda.synchronize()
+    ref_rows, ref_out, ref_lse = wl.pool[rows].clone(), wl.out.clone(), wl.lse.clone()
+    for call in range(2):
+        wl.pool[rows] = 0
+        wl.out.zero_()
+        wl.step()
+        torch.cuda.synchronize()
+        assert torch.equal(wl.pool[rows], ref_rows), f"call {call}: appended rows differ"
+        assert torch.equal(wl.out, ref_out) and torch.equal(wl.lse, ref_lse), f"call {call}: outputs differ"
+        assert wl.mla.read_error_flags(wl._step_ws) == 0
+    _check_append(wl, [0, B - 1], tokens_per_seq=lambda n: np.array([n - 1]))
+    _check_decode(wl, [0, B - 1])
+
+
+def test_decode_step_flags_a_bad_position():
+    import compressed_kv_cache_mla_amd as mla
+    cfg = W.scaled(W.CONFIGS["b64_ragged"], name="step_flags", d_model=1024, B=3, lens=(40, 300), seed=9)
+    _say("case decode step error flags")
+    wl = W.Workload(cfg, n_splits=8)
+    wl.step()
+    assert mla.read_error_flags(wl._step_ws) == 0
+    good = wl.pos_q.clone()
+    wl.pos_q[1] = wl.max_pages * cfg.page_size    # one past the table: the row is skipped and flagged
+    wl.step()
+    assert mla.read_error_flags(wl._step_ws) & mla.FLAG_BAD_POSITION
+    wl.pos_q.copy_(good)
+    wl.step()
+    assert mla.read_error_flags(wl._step_ws) == 0
+
+
 def test_bf16_page_permutation_is_bitwise_invariant():
     base = W.scaled(W.CONFIGS["b64_ragged"], name="perm", d_model=256, B=6, lens=(100, 900), seed=5)
     _say("case page permutation")

@@ -214,19 +214,36 @@ class Workload:
                         self.row_stride, self.num_pages, self.page_table, self.seq_lens, self.out, self.lse,
                         self.workspace, self.n_splits, stream, ev_start, ev_stop, impl)
 
-    def append_step(self, stream=None, use_workspace: bool = True):
-        """The decode step's append: each sequence's newest token (position
-        n_b - 1) is written again from its token state (with the append
-        workspace when the library has a split path for this size)."""
+    def _newest_token_states(self):
         if not hasattr(self, "_step_h"):
             last = self.prefix[1:] - 1
             self._step_h = self.h_rows(torch.from_numpy(last).to(self.device))
             self._step_pos = self.pos_q.clone()
+        return self._step_h
+
+    def append_step(self, stream=None, use_workspace: bool = True):
+        """The decode step's append: each sequence's newest token (position
+        n_b - 1) is written again from its token state (with the append
+        workspace when the library has a split path for this size)."""
+        self._newest_token_states()
+        if not hasattr(self, "_append_ws"):
             nws = self.mla.cache_append_workspace_size(self.dims, self.cfg.B)
             self._append_ws = torch.empty(nws, dtype=torch.uint8, device=self.device) if nws > 0 else None
         self.mla.cache_append(self.dims, self._step_h, self.W_DKV, self.W_KR, self._step_pos, self.page_table,
                               self.c_KV, self.k_R, self.row_stride, self.num_pages, stream=stream,
                               workspace=self._append_ws if use_workspace else None)
+
+    def step(self, stream=None, ev_start=None, ev_stop=None, impl: int = 0):
+        """One whole decode step through mla_decode_step: each sequence's
+        newest token (position n_b - 1) is appended again from its token
+        state, then every sequence is decoded."""
+        h = self._newest_token_states()
+        if not hasattr(self, "_step_ws"):
+            self._step_ws = self.mla.decode_step_workspace(self.dims, self.cfg.B, self.n_splits, self.device)
+        self.mla.decode_step(self.dims, h, self.W_DKV, self.W_KR, self.q_C, self.q_R, self.pos_q, self.W_UK,
+                             self.W_UV, self.c_KV, self.k_R, self.row_stride, self.num_pages, self.page_table,
+                             self.seq_lens, self.out, self.lse, self._step_ws, self.n_splits, stream, ev_start,
+                             ev_stop, impl)
 
     # ---------------------------------------------------------------- oracle side (CPU, generator only)
     def oracle_inputs(self, b: int) -> dict:
