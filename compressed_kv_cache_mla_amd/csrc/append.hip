@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(256) append_bf16_kernel(
 // global memory, up to SMALL_KB K-steps per batch) before its MFMAs, so one
 // memory latency covers its slice; the 16 partial sums are added in LDS.
 constexpr int SMALL_W = 16;
-constexpr int SMALL_KB = SK_KB;
+constexpr int SMALL_KB = 10;
 
 __global__ void __launch_bounds__(64 * SMALL_W) append_bf16_small_kernel(
     int32_t T_rows, int32_t d_model, const bf16* __restrict__ h, const bf16* __restrict__ W_DKV,
@@ -257,7 +257,7 @@ __global__ void __launch_bounds__(256) append_splitk_kernel(int32_t T_rows, int3
                                                             const bf16* __restrict__ h,
                                                             const bf16* __restrict__ W_DKV,
                                                             const bf16* __restrict__ W_KR, float* __restrict__ part) {
-  __shared__ float red[4 * 16 * 17];
+  __shared__ float red[SK_RED_FLOATS];
   append_splitk_block(blockIdx.x, blockIdx.y, blockIdx.z, T_rows, d_model, h, W_DKV, W_KR, part, red);
 }
 
@@ -281,7 +281,7 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
                          int32_t num_pages, int32_t* err_flag, void* ws, size_t ws_bytes, hipStream_t s) {
   const size_t need = append_workspace_bytes(d, T);
   if (ws && need > 0 && ws_bytes >= need) {
-    dim3 g1(D_K / 16, SK_SPLIT, (T + 15) / 16);
+    dim3 g1(D_K / 16, SK_SPLIT, (T + SK_TOK - 1) / SK_TOK);
     append_splitk_kernel<<<g1, 256, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV, (const bf16*)W_KR,
                                            (float*)ws);
     const int64_t n = (int64_t)T * (D_K / 2);

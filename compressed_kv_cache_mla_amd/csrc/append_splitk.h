@@ -6,7 +6,7 @@
 // 四两拨千斤" (liang.world), ch.2 §2-§3; "DeepSeek 系列模型技术深度解读" (tuntang.top),
 // "RoPE 的兼容性处理").  The [T x d_model] x [d_model x 576] product is split
 // over d_model into SK_SPLIT chunks so that the weight stream is spread over
-// the whole GPU: workgroup (16 output columns, chunk kc, 16 tokens), 4 waves
+// the whole GPU: workgroup (16 output columns, chunk kc, 32 tokens), 4 waves
 // (quarters of the chunk, every operand load issued before the MFMAs); its
 // fp32 chunk sums go to part[kc][t][576].  The chunks of an output element are
 // then added in the fixed order kc = 0 .. SK_SPLIT-1, RoPE is applied to the
@@ -21,7 +21,7 @@
 namespace mla {
 
 constexpr int SK_SPLIT = APPEND_SK_SPLIT;   // d_model chunks
-constexpr int SK_KB = 10;     // K-steps of operand loads issued per batch
+constexpr int SK_KB = 5;      // K-steps of operand loads issued per batch (d_model 5120: all of them)
 
 // Where and how the finished rows are stored.
 struct AppendDst {
@@ -36,8 +36,14 @@ struct AppendDst {
   int32_t* err_flag;       // may be NULL
 };
 
-// Chunk sums of workgroup (col_blk, kc, tok_blk); red: 4*16*17 floats of LDS.
-// COHERENT (in-launch finish): the sums are stored at system scope, i.e.
+// Tokens per workgroup: two 16-token MFMA tiles share each W^DKV / W^KR
+// fragment load.
+constexpr int SK_TOK = 32;
+// LDS of a workgroup's cross-wave reduction (floats): [wave][token][16 + 1]
+constexpr int SK_RED_FLOATS = 4 * SK_TOK * 17;
+
+// Chunk sums of workgroup (col_blk, kc, tok_blk); red: SK_RED_FLOATS floats of
+// LDS.  COHERENT (in-launch finish): the sums are stored at system scope, i.e.
 // written through every cache level, so that a workgroup on another XCD can
 // read them in the same launch without a cache write-back fence.
 template <bool COHERENT = false>
@@ -46,40 +52,52 @@ __device__ __forceinline__ void append_splitk_block(int col_blk, int kc, int tok
                                                     const bf16* __restrict__ W_DKV, const bf16* __restrict__ W_KR,
                                                     float* __restrict__ part, float* red) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col0 = col_blk * 16, tok0 = tok_blk * 16;
+  const int col0 = col_blk * 16, tok0 = tok_blk * SK_TOK;
   const bf16* W = col0 < D_C ? W_DKV + (int64_t)col0 * d_model : W_KR + (int64_t)(col0 - D_C) * d_model;
   const int kchunk = d_model / SK_SPLIT, kw = kchunk / 4, nks = kw / 32;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
   const int64_t k0 = (int64_t)kc * kchunk + wave * kw + kq;
   const bf16* wrow = W + (int64_t)r16 * d_model + k0;
-  const bf16* hrow = h + (int64_t)min(tok0 + r16, T_rows - 1) * d_model + k0;
-  f32x4 acc = {0, 0, 0, 0};
+  const bf16* hrow0 = h + (int64_t)min(tok0 + r16, T_rows - 1) * d_model + k0;
+  const bf16* hrow1 = h + (int64_t)min(tok0 + 16 + r16, T_rows - 1) * d_model + k0;
+  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   for (int b0 = 0; b0 < nks; b0 += SK_KB) {
-    bf16x8 wv[SK_KB], hv[SK_KB];
+    bf16x8 wv[SK_KB], hv0[SK_KB], hv1[SK_KB];
 #pragma unroll
     for (int i = 0; i < SK_KB; ++i)
       if (b0 + i < nks) {
         wv[i] = *(const bf16x8*)(wrow + 32 * (b0 + i));
-        hv[i] = *(const bf16x8*)(hrow + 32 * (b0 + i));
+        hv0[i] = *(const bf16x8*)(hrow0 + 32 * (b0 + i));
+        hv1[i] = *(const bf16x8*)(hrow1 + 32 * (b0 + i));   // rows past T repeat row T-1
       }
 #pragma unroll
     for (int i = 0; i < SK_KB; ++i)
-      if (b0 + i < nks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv[i], wv[i], acc, 0, 0, 0);
+      if (b0 + i < nks) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv0[i], wv[i], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv1[i], wv[i], acc1, 0, 0, 0);
+      }
   }
-  // C layout: lane holds output column lane%16, tokens 4*(lane/16) + i
+  // C layout: lane holds output column lane%16, tokens 4*(lane/16) + i of its tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * (lane >> 4) + i) * 17 + r16] = acc[i];
+  for (int i = 0; i < 4; ++i) {
+    red[(wave * SK_TOK + 4 * (lane >> 4) + i) * 17 + r16] = acc0[i];
+    red[(wave * SK_TOK + 16 + 4 * (lane >> 4) + i) * 17 + r16] = acc1[i];
+  }
   __syncthreads();
-  const int r = tid >> 4, c = tid & 15;
-  const int t = tok0 + r;
-  auto rd = [&](int w) { return red[(w * 16 + r) * 17 + c]; };
-  if (t < T_rows) {
-    float* dst = part + ((int64_t)kc * T_rows + t) * D_K + col0 + c;
-    const float v = (rd(0) + rd(1)) + (rd(2) + rd(3));
-    if (COHERENT)
-      __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    else
-      *dst = v;
+  const int c = tid & 15;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int r = (tid >> 4) + 16 * half;
+    const int t = tok0 + r;
+    auto rd = [&](int w) { return red[(w * SK_TOK + r) * 17 + c]; };
+    if (t < T_rows) {
+      float* dst = part + ((int64_t)kc * T_rows + t) * D_K + col0 + c;
+      const float v = (rd(0) + rd(1)) + (rd(2) + rd(3));
+      if (COHERENT)
+        __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      else
+        *dst = v;
+    }
   }
 }
 
@@ -140,7 +158,7 @@ __device__ __forceinline__ void append_finish_pair(int32_t T_rows, int t, int cp
 // until its system-scope chunk-sum stores have completed and counts itself in
 // with a device-scope atomic; the one that brings the count to SK_SPLIT adds
 // the chunks (system-scope loads, so no cache can hold stale sums) and stores
-// the tile's 16 tokens x 16 columns, then puts the counter back to zero for
+// the tile's 32 tokens x 16 columns, then puts the counter back to zero for
 // the next launch.  The counters start at zero.
 __device__ __forceinline__ void append_splitk_finish_tile(int col_blk, int tok_blk, int32_t T_rows,
                                                           const float* part, int32_t* counters,
@@ -153,9 +171,9 @@ __device__ __forceinline__ void append_splitk_finish_tile(int col_blk, int tok_b
     *lds_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == SK_SPLIT - 1;
   __syncthreads();
   if (!*lds_flag) return;
-  if (tid < 128) {
-    const int r = tid >> 3, cp = tid & 7;   // 16 tokens x 8 column pairs
-    const int t = tok_blk * 16 + r;
+  {
+    const int r = tid >> 3, cp = tid & 7;   // 32 tokens x 8 column pairs
+    const int t = tok_blk * SK_TOK + r;
     if (t < T_rows) append_finish_pair<true>(T_rows, t, col_blk * 8 + cp, part, a);
   }
   if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -96,7 +96,7 @@ inline DecodeWs decode_ws_layout(int32_t B, int32_t n_h, int32_t n_splits, int e
   if (step) {
     off += align256((size_t)APPEND_SK_SPLIT * B * D_K * 4);                // fp32 chunk sums
     w.app_cnt = off;
-    off += align256((size_t)((B + 15) / 16) * (D_K / 16) * 4);             // one counter per tile
+    off += align256((size_t)((B + 31) / 32) * (D_K / 16) * 4);             // one counter per 32 x 16 tile
   }
   w.total = off;
   return w;

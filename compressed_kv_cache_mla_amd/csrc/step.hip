@@ -26,7 +26,7 @@ struct StepPrepArgs {
   float* app_part;
   int32_t* app_cnt;
   AppendDst dst;
-  int32_t n_app;        // append workgroups: SK_SPLIT * (D_K / 16) * ceil(B / 16)
+  int32_t n_app;        // append workgroups: SK_SPLIT * (D_K / 16) * ceil(B / SK_TOK)
   int32_t d_model;
   // absorb
   const bf16* q_C;
@@ -38,9 +38,10 @@ struct StepPrepArgs {
   int32_t B, n_h;
 };
 
-__global__ void __launch_bounds__(256) step_prep_kernel(StepPrepArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[D_H * 256];   // absorb's W^UK block; reused by the others
-  __shared__ int last_flag;
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) step_prep_kernel(StepPrepArgs a) {
+  // absorb's W^UK block (32 KB, so that five workgroups fit in a CU's LDS);
+  // the append uses its first SK_RED_FLOATS floats and one int after them
+  __shared__ __attribute__((aligned(1024))) char smem[D_H * 256];
   int bid = blockIdx.x;
   if (bid == 0) {
     plan_block<256>(a.pa, (int32_t*)smem, D_H * 256 / 4 - 256);
@@ -53,7 +54,7 @@ __global__ void __launch_bounds__(256) step_prep_kernel(StepPrepArgs a) {
     const int col_blk = (bid / SK_SPLIT) % (D_K / 16);
     const int tok_blk = bid / (SK_SPLIT * (D_K / 16));
     append_splitk_block<true>(col_blk, kc, tok_blk, a.B, a.d_model, a.h_new, a.W_DKV, a.W_KR, a.app_part, (float*)smem);
-    append_splitk_finish_tile(col_blk, tok_blk, a.B, a.app_part, a.app_cnt, a.dst, &last_flag);
+    append_splitk_finish_tile(col_blk, tok_blk, a.B, a.app_part, a.app_cnt, a.dst, (int*)(smem + SK_RED_FLOATS * 4));
     return;
   }
   bid -= a.n_app;
@@ -80,7 +81,7 @@ hipError_t launch_step_prep(const mla_dims& d, int32_t B, const void* h_new, con
   a.app_part = app_part;
   a.app_cnt = app_cnt;
   a.dst = dst;
-  a.n_app = SK_SPLIT * (D_K / 16) * ((B + 15) / 16);
+  a.n_app = SK_SPLIT * (D_K / 16) * ((B + SK_TOK - 1) / SK_TOK);
   a.d_model = d.d_model;
   a.q_C = (const bf16*)q_C;
   a.q_R = (const bf16*)q_R;

@@ -126,9 +126,9 @@ def test_decode_step_workspace_holds_the_append_reduction():
     for B in (1, 16, 17, 64, 200):
         dec = L.mla_decode_workspace_size(ctypes.byref(d), B, 256)
         step = L.mla_decode_step_workspace_size(ctypes.byref(d), B, 256)
-        # 8 fp32 chunk sums per output element and one counter per 16 x 16 tile
-        assert step >= dec + 8 * B * 576 * 4 + ((B + 15) // 16) * 36 * 4
-        assert step - dec < 8 * B * 576 * 4 + ((B + 15) // 16) * 36 * 4 + 512
+        # 8 fp32 chunk sums per output element and one counter per 32-token x 16-column tile
+        assert step >= dec + 8 * B * 576 * 4 + ((B + 31) // 32) * 36 * 4
+        assert step - dec < 8 * B * 576 * 4 + ((B + 31) // 32) * 36 * 4 + 512
     assert L.mla_decode_step_workspace_size(ctypes.byref(_dims(d_c=1)), 4, 256) == 0
 
 
