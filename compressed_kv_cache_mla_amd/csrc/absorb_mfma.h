@@ -41,15 +41,17 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int32_t B, int
     __builtin_amdgcn_global_load_lds((const void*)(wsrc + (int64_t)d * 1024 + c16 * 16),
                                      (lds_void_t*)(wl + (wave * 8 + k) * 1024), 16, 0, 0);
   }
-  // q^C fragments: lane -> sequence b0 + 32*nblk + (lane & 31), d = 16*ks + 8*(lane >> 5)
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int nblk = 0; nblk < 2; ++nblk) {
+  // q^C fragments of one 32-sequence block: lane -> sequence b0 + 32*nblk +
+  // (lane & 31), d = 16*ks + 8*(lane >> 5).  The second block (sequences
+  // 32..63) is loaded after the first block's MFMAs have read their operands.
+  bf16x8 qf[8];
+  auto load_qf = [&](int nblk) {
     const int b = min(b0 + 32 * nblk + (lane & 31), B - 1);
     const bf16* qp = q_C + ((int64_t)b * n_h + h) * D_H + 8 * (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[nblk][ks] = *(const bf16x8*)(qp + 16 * ks);
-  }
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
+  };
+  load_qf(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // transposed-read source address: row d = 16ks + 8*(lane>>5) + 4rr + ((lane&15)>>2),
@@ -57,45 +59,50 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int32_t B, int
   const int t_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
   const int t_c16 = 4 * wave + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int t_half = (lane & 1) * 8;
-  f32x16 acc[2];
+  auto block_product = [&]() -> f32x16 {
+    f32x16 acc;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+    for (int ks = 0; ks < 8; ++ks) {
+      bf16x8 af;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    bf16x8 af;
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int d = 16 * ks + t_row + 4 * rr;
-      const int c16 = t_c16 ^ ((d & 3) << 2);
-      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(wl + d * 256 + c16 * 16 + t_half));
-      const bf16x4 vb = __builtin_bit_cast(bf16x4, v);
-      af[4 * rr + 0] = vb[0];
-      af[4 * rr + 1] = vb[1];
-      af[4 * rr + 2] = vb[2];
-      af[4 * rr + 3] = vb[3];
+      for (int rr = 0; rr < 2; ++rr) {
+        const int d = 16 * ks + t_row + 4 * rr;
+        const int c16 = t_c16 ^ ((d & 3) << 2);
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(wl + d * 256 + c16 * 16 + t_half));
+        const bf16x4 vb = __builtin_bit_cast(bf16x4, v);
+        af[4 * rr + 0] = vb[0];
+        af[4 * rr + 1] = vb[1];
+        af[4 * rr + 2] = vb[2];
+        af[4 * rr + 3] = vb[3];
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], acc, 0, 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[j][ks], acc[j], 0, 0, 0);
-  }
-  // C layout: lane -> sequence (lane & 31) of block j, latent rows (r/4)*8 + 4*(lane>>5) + r%4
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int bb = 32 * j + (lane & 31);
+    return acc;
+  };
+  // C layout: lane -> sequence (lane & 31) of the block, latent rows (r/4)*8 + 4*(lane>>5) + r%4
+  auto store_block = [&](const f32x16& acc, int nblk) {
+    const int bb = 32 * nblk + (lane & 31);
     if (bb < nb) {
       bf16* dst = qabs + ((int64_t)(b0 + bb) * n_h + h) * D_K + 128 * cq + 32 * wave + 4 * (lane >> 5);
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 o;
-        o[0] = (bf16)(acc[j][4 * r4 + 0] * qscale);
-        o[1] = (bf16)(acc[j][4 * r4 + 1] * qscale);
-        o[2] = (bf16)(acc[j][4 * r4 + 2] * qscale);
-        o[3] = (bf16)(acc[j][4 * r4 + 3] * qscale);
+        o[0] = (bf16)(acc[4 * r4 + 0] * qscale);
+        o[1] = (bf16)(acc[4 * r4 + 1] * qscale);
+        o[2] = (bf16)(acc[4 * r4 + 2] * qscale);
+        o[3] = (bf16)(acc[4 * r4 + 3] * qscale);
         *(bf16x4*)(dst + 8 * r4) = o;
       }
     }
+  };
+  {
+    const f32x16 acc0 = block_product();
+    if (nb > 32) load_qf(1);
+    store_block(acc0, 0);
   }
+  if (nb > 32) store_block(block_product(), 1);
   // RoPE half (32 pairs per sequence), by the column-quarter-0 workgroups
   if (cq == 0) {
     for (int i = tid; i < nb * (D_R / 2); i += 256) {

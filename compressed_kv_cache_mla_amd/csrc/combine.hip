@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(256) combine_f32_kernel(int32_t B, int32_t n_h
 // waves 0..7 (wave w: d = 16w .. 16w+15, CS/16 blocks of 16 sequences), W^UV
 // rows read straight from global memory in the A layout, once per CS
 // sequences.
-constexpr int CB = 8;
+constexpr int CB_MAX = 8;
 
 __device__ __forceinline__ float wave_max64(float x) {
 #pragma unroll
@@ -150,6 +150,8 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
                                                             const bf16* __restrict__ W_UV, float* __restrict__ out,
                                                             float* __restrict__ lse, int32_t* merge_flags) {
   constexpr int NBQ = CS / 16;
+  constexpr int CB = CB_MAX;
+  constexpr bool PRE = CS == 16;   // registers allow the W^UV prefetch with one accumulator block
   merge_step_flags(merge_flags);
   __shared__ __attribute__((aligned(16))) char ol[CS * D_C * 2];
   __shared__ int empty_l[CS];
@@ -159,6 +161,14 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
   const int b0 = blockIdx.y * CS;
   const int nb = min(CS, B - b0);
   const int64_t N = prefix[B];
+  // With one accumulator block (CS = 16) the epilogue waves' W^UV_h rows are
+  // loaded first, so that their latency passes while the partials are merged.
+  const bf16* wr = W_UV + ((int64_t)h * D_H + 16 * (wave & 7) + (lane & 15)) * D_C + 8 * (lane >> 4);
+  bf16x8 wpre[PRE ? D_C / 32 : 1];
+  if (PRE && wave < D_H / 16) {
+#pragma unroll
+    for (int ks = 0; ks < D_C / 32; ++ks) wpre[ks] = *(const bf16x8*)(wr + 32 * ks);
+  }
   for (int bb = wave; bb < CS; bb += 16) {
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int empty = 1;
@@ -213,12 +223,11 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
   f32x4 acc[NBQ];
 #pragma unroll
   for (int j = 0; j < NBQ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bf16* wr = W_UV + ((int64_t)h * D_H + 16 * wave + (lane & 15)) * D_C + 8 * (lane >> 4);
   const int bq = lane & 15;
 #pragma unroll
   for (int ks = 0; ks < D_C / 32; ++ks) {
     const int c16 = 4 * ks + (lane >> 4);
-    const bf16x8 afr = *(const bf16x8*)(wr + 32 * ks);
+    const bf16x8 afr = PRE ? wpre[PRE ? ks : 0] : *(const bf16x8*)(wr + 32 * ks);
 #pragma unroll
     for (int j = 0; j < NBQ; ++j) {
       const bf16x8 bfr = *(const bf16x8*)(ol + (16 * j + bq) * 1024 + ((c16 ^ bq) << 4));
