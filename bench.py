@@ -24,6 +24,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -54,6 +56,25 @@ def algorithmic(wl):
     step_flops = attn_flops + B * 4 * nh * 128 * 512 + B * 2 * dm * 576
     return dict(N=N, cache=cache, attn_bytes=attn_bytes, attn_flops=attn_flops, step_bytes=step_bytes,
                 step_flops=step_flops)
+
+
+def measured_copy_gbps(torch) -> float:
+    """A second denominator beside the spec peak: read + write bytes per
+    second of a plain 1 GiB device-to-device copy on this GPU (best of 5)."""
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    best = float("inf")
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        y.copy_(x)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del x, y
+    return 2 * n / (best * 1e-3) / 1e9
 
 
 def cpu_baseline(wl, seconds: float):
@@ -158,19 +179,28 @@ def main():
         # attention-kernel events: HIP events without the system-scope fence,
         # recorded on the decode stream by mla_decode_ex around that kernel
         kev = [(mla.HipEvent(), mla.HipEvent()) for _ in range(steps)]
+        # step boundaries, also without the system fence (step i = sev[i] .. sev[i+1])
+        sev = [mla.HipEvent() for _ in range(steps + 1)]
         t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         t_start.record()
         for i in range(steps):
+            sev[i].record()
             step(i, kev[i])
+        sev[steps].record()
         t_stop.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
-        kern_ms = [a.elapsed_ms(b) for a, b in kev]
-        return first, alg, copies, t_start.elapsed_time(t_stop) / steps, 1e3 * sum(kern_ms) / len(kern_ms), wall
+        kern_us = [1e3 * a.elapsed_ms(b) for a, b in kev]
+        step_us = [1e3 * sev[i].elapsed_ms(sev[i + 1]) for i in range(steps)]
+        dist = {"step_us_p10_p50_p90": [round(float(x), 2) for x in np.percentile(step_us, [10, 50, 90])],
+                "kernel_us_p10_p50_p90": [round(float(x), 2) for x in np.percentile(kern_us, [10, 50, 90])]}
+        return (first, alg, copies, t_start.elapsed_time(t_stop) / steps, sum(kern_us) / len(kern_us), wall,
+                dist)
 
-    first, alg, copies, ms_per_step, kern_us, wall = measure(args.workload, args.steps, args.warmup)
+    first, alg, copies, ms_per_step, kern_us, wall, dist = measure(args.workload, args.steps, args.warmup)
+    copy_gbps = measured_copy_gbps(torch)
     cfg = first.cfg
     B = cfg.B
     value = B / (ms_per_step * 1e-3)
@@ -194,7 +224,10 @@ def main():
                      "kernel": "split-KV attention (decode_mfma_kernel)" if args.impl == 0 else "decode_simple_kernel",
                      "kernel_us": round(kern_us, 2),
                      "mfma_tflops": round(alg["attn_flops"] / (kern_us * 1e-6) / 1e12, 1),
-                     "mfma_frac": round(alg["attn_flops"] / (kern_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                     "mfma_frac": round(alg["attn_flops"] / (kern_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "measured_copy_GBps": round(copy_gbps, 1),
+                     "frac_of_measured_copy": round(achieved / copy_gbps, 4)},
+        **dist,
         "latent_cache_GBps": round(alg["cache"] / (ms_per_step * 1e-3) / 1e9, 1),
         "step_GBps": round(alg["step_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(alg["step_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -202,13 +235,14 @@ def main():
     }
     if args.target_workload and args.target_workload != args.workload:
         # the batch-64 / 8K-context decode shape the performance target is stated on
-        f2, a2, c2, ms2, k2, _ = measure(args.target_workload, max(5, args.steps // 2), args.warmup)
+        f2, a2, c2, ms2, k2, _, d2 = measure(args.target_workload, max(5, args.steps // 2), args.warmup)
         res["target_shape"] = {
             "workload": f2.cfg.name, "B": f2.cfg.B, "cached_tokens": a2["N"], "ms_per_step": round(ms2, 5),
             "tokens_per_s": round(f2.cfg.B / (ms2 * 1e-3), 1), "kernel_us": round(k2, 2),
             "hbm_frac": round(a2["attn_bytes"] / (k2 * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "mfma_frac": round(a2["attn_flops"] / (k2 * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "copies_rotated": c2}
+            "hbm_frac_of_measured_copy": round(a2["attn_bytes"] / (k2 * 1e-6) / 1e9 / copy_gbps, 4),
+            "copies_rotated": c2, **d2}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -170,11 +170,18 @@ class HipEvent:
             hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
             hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
             hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             HipEvent._hip = hip
         self.handle = ctypes.c_void_p()
         st = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.handle), ctypes.c_uint(0x20000000))
         if st != 0:
             raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self, stream=None):
+        """Record on `stream` (default: torch's current stream)."""
+        st = HipEvent._hip.hipEventRecord(self.handle, _stream(stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
 
     def elapsed_ms(self, end: "HipEvent") -> float:
         ms = ctypes.c_float()
