@@ -261,11 +261,11 @@ __global__ void __launch_bounds__(256) append_splitk_kernel(int32_t T_rows, int3
   append_splitk_block(blockIdx.x, blockIdx.y, blockIdx.z, T_rows, d_model, h, W_DKV, W_KR, part, red);
 }
 
-__global__ void __launch_bounds__(256) append_finish_kernel(int32_t T_rows, const float* __restrict__ part,
-                                                            AppendDst a) {
+__global__ void __launch_bounds__(256) append_finish_kernel(int32_t T_rows, int32_t d_model,
+                                                            const float* __restrict__ part, AppendDst a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int t = (int)(idx / (D_K / 2)), cp = (int)(idx % (D_K / 2));
-  if (t < T_rows) append_finish_pair(T_rows, t, cp, part, a);
+  if (t < T_rows) append_finish_pair(T_rows, d_model, t, cp, part, a);
 }
 
 }  // namespace
@@ -287,7 +287,7 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
     const int64_t n = (int64_t)T * (D_K / 2);
     const AppendDst a{seq_id, pos, page_table, num_seqs, max_pages, d.page_size, num_pages, (bf16*)c_KV,
                       (bf16*)k_R, row_stride, rope_table(d.rope_base), err_flag};
-    append_finish_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(T, (const float*)ws, a);
+    append_finish_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(T, d.d_model, (const float*)ws, a);
     return hipGetLastError();
   }
   dim3 grid((T + AT_TOK - 1) / AT_TOK, D_K / AT_COL);

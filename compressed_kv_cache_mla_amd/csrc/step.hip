@@ -54,7 +54,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) s
     const int col_blk = (bid / SK_SPLIT) % (D_K / 16);
     const int tok_blk = bid / (SK_SPLIT * (D_K / 16));
     append_splitk_block<true>(col_blk, kc, tok_blk, a.B, a.d_model, a.h_new, a.W_DKV, a.W_KR, a.app_part, (float*)smem);
-    append_splitk_finish_tile(col_blk, tok_blk, a.B, a.app_part, a.app_cnt, a.dst, (int*)(smem + SK_RED_FLOATS * 4));
+    append_splitk_finish_tile(col_blk, tok_blk, a.B, a.d_model, a.app_part, a.app_cnt, a.dst,
+                              (int*)(smem + SK_RED_FLOATS * 4));
     return;
   }
   bid -= a.n_app;

@@ -225,7 +225,7 @@ def test_b32_l4096_full():
     cfg = W.CONFIGS["b32_l4096"]
     _say(f"case {cfg.name}")
     wl = W.Workload(cfg)
-    _check_decode(wl, [0, cfg.B - 1])
+    _check_decode(wl, range(cfg.B))   # every sequence
     _check_decode(wl, [0], "reconstruct", heads=[0, 77, 127])
     _check_append(wl, [0, cfg.B - 1], tokens_per_seq=lambda n: np.arange(0, n, 97))
 
@@ -234,8 +234,10 @@ def test_b64_ragged_paged_full():
     cfg = W.CONFIGS["b64_ragged"]
     _say(f"case {cfg.name}")
     wl = W.Workload(cfg)
-    longest = int(np.argmax(wl.n))
-    _check_decode(wl, sorted({0, cfg.B - 1, longest}))
+    longest, shortest = int(np.argmax(wl.n)), int(np.argmin(wl.n))
+    spread = range(5, cfg.B, 13)
+    _check_decode(wl, sorted({0, cfg.B - 1, longest, shortest, *spread}))
+    _check_decode(wl, [longest], "reconstruct", heads=[0, 64, 127])
 
 
 def test_b4_l131072_full():
