@@ -27,9 +27,16 @@ Readings where the pages are silent (each is listed in the design notes):
 * Weights are stored [out, in] row-major: W^DKV [d_c, d_model],
   W^KR [d_h^R, d_model], W^UK and W^UV [n_h*d_h, d_c] with head i owning rows
   i*d_h .. i*d_h + d_h - 1, W^UQ [n_h*d_h, d_model], W^QR [n_h*d_h^R, d_model].
-* The query path has no down-projection (c^Q := h): q^C = W^UQ h and
-  q^R = W^QR h; the harness computes it, it is not on the decode path.
-* W_O is not applied: the output is each head's o_i.
+* Query path, two forms.  Without a query down-projection (c^Q := h):
+  q^C = W^UQ h and q^R = W^QR h (``query_project``).  With the query's own
+  low-rank compression (``query_project_lowrank``): c^Q = W^DQ h, by analogy
+  with c^KV = W^DKV h (the pages name c^Q but print no formula for it), its
+  rank d_cq a free parameter (the pages give no value); q^C = W^UQ c^Q; and
+  q^R = W^QR h, fed from h_t as [DS-report] writes it.  Both return q^R not
+  yet rotated (the decode rotates it at the query position).
+* The output projection W^O [d_model, n_h*d_h] acts on the heads' outputs
+  concatenated in head order (``output_project``); the decode attention itself
+  returns each head's o_i.
 
 Everything is numpy float64; matrix products are numpy ``@``.
 """
@@ -121,6 +128,33 @@ def query_project(h_q: np.ndarray, W_UQ: np.ndarray, W_QR: np.ndarray, n_h: int)
     q_C = (np.asarray(W_UQ, dtype=np.float64) @ h_q).reshape(n_h, -1)
     q_R = (np.asarray(W_QR, dtype=np.float64) @ h_q).reshape(n_h, -1)
     return q_C, q_R
+
+
+def query_project_lowrank(h_q: np.ndarray, W_DQ: np.ndarray, W_UQ: np.ndarray, W_QR: np.ndarray, n_h: int):
+    """Queries of tokens h_q [..., d_model] through the query's low-rank
+    compression ([V2-arch] ch.2 §2, closing paragraph: q is compressed to c^Q
+    as the keys and values are to c^KV; [DS-report] "RoPE 的兼容性处理": q_t =
+    [W^UQ c_t^Q ; W^QR h_t RoPE(t)]):
+        c^Q = W^DQ h              W_DQ [d_cq, d_model]
+        q^C = W^UQ c^Q            W_UQ [n_h*d_h, d_cq], head i = rows i*d_h ..
+        q^R = W^QR h              W_QR [n_h*d_hR, d_model], NOT yet rotated
+    Returns q_C [..., n_h, d_h] and q_R [..., n_h, d_hR]."""
+    h_q = np.asarray(h_q, dtype=np.float64)
+    c_Q = h_q @ np.asarray(W_DQ, dtype=np.float64).T                 # c^Q = W^DQ h
+    q_C = c_Q @ np.asarray(W_UQ, dtype=np.float64).T                 # q^C = W^UQ c^Q
+    q_R = h_q @ np.asarray(W_QR, dtype=np.float64).T                 # q^R = W^QR h
+    lead = h_q.shape[:-1]
+    return q_C.reshape(*lead, n_h, -1), q_R.reshape(*lead, n_h, -1)
+
+
+def output_project(o: np.ndarray, W_O: np.ndarray) -> np.ndarray:
+    """u = W^O [o_1; o_2; ...; o_{n_h}] for per-head outputs o [..., n_h, d_h]
+    ([V2-arch] ch.2 §1, "输出": the heads' results are concatenated and passed
+    through the output matrix W_O).  W_O [d_model, n_h*d_h]; returns
+    u [..., d_model]."""
+    o = np.asarray(o, dtype=np.float64)
+    cat = o.reshape(*o.shape[:-2], o.shape[-2] * o.shape[-1])        # heads concatenated in order
+    return cat @ np.asarray(W_O, dtype=np.float64).T
 
 
 # ----------------------------------------------------------------------------

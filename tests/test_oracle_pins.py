@@ -11,7 +11,12 @@
 * closed forms of softmax attention (q = 0, one token, identical latents);
 * the absorbed form against the reconstructed form (associativity,
   ch.2 §2 of the same page), bit-exact on integer data;
-* brute-force loops for the down-projection on a tiny input.
+* brute-force loops for the down-projection on a tiny input;
+* the low-rank query path (c^Q = W^DQ h) against the same torch attention with
+  the product matrix W^UQ W^DQ formed first, against the full-rank path when
+  W^DQ is the identity, and by the rank bound it implies;
+* the output projection W^O by head selectors, the sum of heads, and the
+  absorption of W^UV into W^O (ch.2 §2).
 
 The last tests plant typical mistakes in copies of the oracle's functions and
 check that the pins above catch each of them.
@@ -128,7 +133,9 @@ def _torch_mha(P, pos_shift=0):
     kR = rot(h @ t(P["W_KR"]).T, pos)                       # [n, d_hR]
     k = torch.cat([kC, kR.unsqueeze(0).expand(n_h, n, d_hR)], dim=-1)
     hq = h[n - 1]
-    qC = (t(P["W_UQ"]) @ hq).reshape(n_h, d_h)
+    # with a query down-projection, q^C = (W^UQ W^DQ) h: the product matrix is formed first
+    W_q = t(P["W_UQ"]) @ t(P["W_DQ"]) if "W_DQ" in P else t(P["W_UQ"])
+    qC = (W_q @ hq).reshape(n_h, d_h)
     qR = rot((t(P["W_QR"]) @ hq).reshape(n_h, d_hR), pos[n - 1].expand(n_h))
     q = torch.cat([qC, qR], dim=-1)[:, None, :]              # [n_h, 1, E]
     out = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None])[0, :, 0]
@@ -141,7 +148,10 @@ def _oracle_run(P, attend=oracle.attend_reconstruct, pos_shift=0, down=oracle.do
     n = P["n"]
     pos = np.arange(n) + pos_shift
     c, kR = down(P["h"], P["W_DKV"], P["W_KR"], pos, BASE)
-    qC, qR = oracle.query_project(P["h"][n - 1], P["W_UQ"], P["W_QR"], P["n_h"])
+    if "W_DQ" in P:
+        qC, qR = oracle.query_project_lowrank(P["h"][n - 1], P["W_DQ"], P["W_UQ"], P["W_QR"], P["n_h"])
+    else:
+        qC, qR = oracle.query_project(P["h"][n - 1], P["W_UQ"], P["W_QR"], P["n_h"])
     if scale is None:
         scale = oracle.softmax_scale(P["d_h"], P["d_hR"])
     return attend(qC, qR, pos[-1], c, kR, P["W_UK"], P["W_UV"], BASE, scale)
@@ -302,3 +312,152 @@ def test_pins_catch_wrong_key_position():
     bad, _ = _oracle_run(P, down=down_off_by_one)
     ref, _ = _torch_mha(P)
     assert _rel(bad, ref) > 1e-6
+
+
+# ----------------------------------------------------------------------------- query down-projection
+def _with_lowrank_query(P, rng, d_cq, integer=False):
+    """P with a query down-projection W^DQ [d_cq, d_model] and W^UQ [n_h*d_h, d_cq]."""
+    d_model = P["h"].shape[1]
+    if integer:
+        f = lambda *s: rng.integers(-2, 3, size=s).astype(np.float64)  # noqa: E731
+    else:
+        f = lambda *s: rng.standard_normal(s) / math.sqrt(s[-1])       # noqa: E731
+    Q = dict(P)
+    Q["W_DQ"] = f(d_cq, d_model)
+    Q["W_UQ"] = f(P["n_h"] * P["d_h"], d_cq)
+    return Q
+
+
+@pytest.mark.parametrize("seed,d_cq", [(20, 5), (21, 24), (22, 40)])
+def test_lowrank_query_attention_matches_torch_sdpa(seed, d_cq):
+    rng = np.random.default_rng(seed)
+    P = _with_lowrank_query(_problem(rng, n_h=4, d_h=8, d_c=12, d_hR=6, d_model=20, n=9), rng, d_cq)
+    out, lse = _oracle_run(P, oracle.attend_absorbed)
+    ref, ref_lse = _torch_mha(P)
+    assert _rel(out, ref) < 1e-12
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_lowrank_query_with_identity_down_projection_is_the_full_rank_query():
+    rng = np.random.default_rng(23)
+    h = rng.integers(-3, 4, size=(7, 16)).astype(np.float64)
+    W_UQ = rng.integers(-2, 3, size=(4 * 8, 16)).astype(np.float64)
+    W_QR = rng.integers(-2, 3, size=(4 * 6, 16)).astype(np.float64)
+    a_C, a_R = oracle.query_project_lowrank(h, np.eye(16), W_UQ, W_QR, 4)
+    for t in range(7):
+        b_C, b_R = oracle.query_project(h[t], W_UQ, W_QR, 4)
+        assert np.array_equal(a_C[t], b_C) and np.array_equal(a_R[t], b_R)
+
+
+def test_lowrank_query_integer_product_matrix_bitwise():
+    """Integer data: W^UQ (W^DQ h) and (W^UQ W^DQ) h are the same exact integers."""
+    rng = np.random.default_rng(24)
+    h = rng.integers(-3, 4, size=(5, 24)).astype(np.float64)
+    W_DQ = rng.integers(-2, 3, size=(10, 24)).astype(np.float64)
+    W_UQ = rng.integers(-2, 3, size=(3 * 8, 10)).astype(np.float64)
+    W_QR = rng.integers(-2, 3, size=(3 * 4, 24)).astype(np.float64)
+    q_C, q_R = oracle.query_project_lowrank(h, W_DQ, W_UQ, W_QR, 3)
+    for t in range(5):
+        for i in range(3):
+            for d in range(8):
+                r = i * 8 + d
+                want = sum(sum(W_UQ[r, k] * W_DQ[k, j] for k in range(10)) * h[t, j] for j in range(24))
+                assert q_C[t, i, d] == want
+            for d in range(4):
+                assert q_R[t, i, d] == sum(W_QR[i * 4 + d, j] * h[t, j] for j in range(24))
+
+
+def test_lowrank_query_rank_bound_and_rope_input():
+    """Every q^C lies in the d_cq-dimensional image of W^UQ (so 60 tokens give a
+    rank-d_cq matrix), and q^R does not depend on W^DQ (it is fed from h)."""
+    rng = np.random.default_rng(25)
+    n_h, d_h, d_hR, d_model, d_cq = 4, 8, 6, 32, 5
+    h = rng.standard_normal((60, d_model))
+    W_DQ = rng.standard_normal((d_cq, d_model))
+    W_UQ = rng.standard_normal((n_h * d_h, d_cq))
+    W_QR = rng.standard_normal((n_h * d_hR, d_model))
+    q_C, q_R = oracle.query_project_lowrank(h, W_DQ, W_UQ, W_QR, n_h)
+    sv = np.linalg.svd(q_C.reshape(60, -1), compute_uv=False)
+    assert sv[d_cq - 1] > 1e-6 * sv[0] and sv[d_cq] < 1e-10 * sv[0]
+    _, q_R2 = oracle.query_project_lowrank(h, rng.standard_normal((d_cq, d_model)), W_UQ, W_QR, n_h)
+    assert np.array_equal(q_R, q_R2)
+
+
+def test_lowrank_query_head_layout():
+    """Head i's q^C comes from rows i*d_h .. i*d_h + d_h - 1 of W^UQ only."""
+    rng = np.random.default_rng(26)
+    n_h, d_h, d_hR, d_model, d_cq = 4, 8, 6, 16, 6
+    h = rng.standard_normal((3, d_model))
+    W_UQ = np.zeros((n_h * d_h, d_cq))
+    W_UQ[2 * d_h:3 * d_h] = rng.standard_normal((d_h, d_cq))
+    W_QR = np.zeros((n_h * d_hR, d_model))
+    W_QR[1 * d_hR:2 * d_hR] = rng.standard_normal((d_hR, d_model))
+    q_C, q_R = oracle.query_project_lowrank(h, rng.standard_normal((d_cq, d_model)), W_UQ, W_QR, n_h)
+    assert np.all(q_C[:, [0, 1, 3]] == 0) and np.all(q_C[:, 2] != 0)
+    assert np.all(q_R[:, [0, 2, 3]] == 0) and np.all(q_R[:, 1] != 0)
+
+
+# ----------------------------------------------------------------------------- output projection
+def test_output_projection_selects_and_sums_heads():
+    rng = np.random.default_rng(27)
+    n_h, d_h = 5, 4
+    o = rng.standard_normal((3, n_h, d_h))
+    for i in range(n_h):                       # W^O = [0 .. I .. 0]: u = o_i exactly
+        W_O = np.zeros((d_h, n_h * d_h))
+        W_O[:, i * d_h:(i + 1) * d_h] = np.eye(d_h)
+        assert np.array_equal(oracle.output_project(o, W_O), o[:, i])
+    W_O = np.tile(np.eye(d_h), (1, n_h))       # [I I .. I]: u = sum_i o_i
+    np.testing.assert_allclose(oracle.output_project(o, W_O), o.sum(axis=1), rtol=0, atol=1e-14)
+    W_O = rng.standard_normal((7, n_h * d_h))  # d_model != n_h*d_h: u = sum_i W^O_i o_i
+    u = oracle.output_project(o, W_O)
+    assert u.shape == (3, 7)
+    ref = sum(o[:, i] @ W_O[:, i * d_h:(i + 1) * d_h].T for i in range(n_h))
+    np.testing.assert_allclose(u, ref, rtol=0, atol=1e-12)
+
+
+def test_output_projection_absorbs_the_value_up_projection():
+    """W^UV folded into W^O ([V2-arch] ch.2 §2): with W^O_i W^UV_i as the
+    projection of head i's latent output O~_i (obtained with W^UV = I, d_h =
+    d_c), u is the same as W^O applied to the o_i = W^UV_i O~_i."""
+    rng = np.random.default_rng(28)
+    n_h, d_c, d_hR, n, d_model = 3, 8, 4, 13, 11
+    q_C = rng.standard_normal((n_h, d_c))
+    q_R = rng.standard_normal((n_h, d_hR))
+    c = rng.standard_normal((n, d_c))
+    kR = rng.standard_normal((n, d_hR))
+    W_UK = rng.standard_normal((n_h * d_c, d_c))
+    W_UV = rng.standard_normal((n_h * d_c, d_c))
+    W_O = rng.standard_normal((d_model, n_h * d_c))
+    o, _ = oracle.attend_reconstruct(q_C, q_R, n - 1, c, kR, W_UK, W_UV, BASE, 0.3)
+    o_lat, _ = oracle.attend_reconstruct(q_C, q_R, n - 1, c, kR, W_UK, np.tile(np.eye(d_c), (n_h, 1)), BASE, 0.3)
+    W_abs = np.concatenate([W_O[:, i * d_c:(i + 1) * d_c] @ W_UV[i * d_c:(i + 1) * d_c] for i in range(n_h)], axis=1)
+    np.testing.assert_allclose(oracle.output_project(o, W_O), oracle.output_project(o_lat, W_abs), rtol=1e-12,
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["interleaved_concat", "transposed_head_block", "rope_from_latent_query"])
+def test_projection_pins_catch_planted_mistakes(kind):
+    rng = np.random.default_rng(29)
+    if kind == "rope_from_latent_query":       # q^R = W^QR c^Q instead of W^QR h (d_cq = d_model)
+        h = rng.standard_normal((60, 16))
+        W_DQ, W_UQ, W_QR = (rng.standard_normal((16, 16)), rng.standard_normal((32, 16)),
+                            rng.standard_normal((24, 16)))
+        bad = lambda Wd: (h @ Wd.T) @ W_QR.T    # noqa: E731
+        good = oracle.query_project_lowrank(h, W_DQ, W_UQ, W_QR, 4)[1].reshape(60, -1)
+        assert np.array_equal(good, oracle.query_project_lowrank(h, 2 * W_DQ, W_UQ, W_QR, 4)[1].reshape(60, -1))
+        assert not np.array_equal(bad(W_DQ), bad(2 * W_DQ))   # the rope-input pin fails it
+        return
+    n_h, d_h = 4, 4
+    o = rng.standard_normal((2, n_h, d_h))
+    if kind == "interleaved_concat":           # heads concatenated element-major
+        proj = lambda o, W: o.transpose(0, 2, 1).reshape(o.shape[0], -1) @ W.T    # noqa: E731
+    else:                                      # each head's d_h x d_h block used transposed
+        proj = lambda o, W: sum(o[:, i] @ W[:, i * d_h:(i + 1) * d_h] for i in range(n_h))  # noqa: E731
+    caught = False
+    for i in range(n_h):
+        W_O = np.zeros((d_h, n_h * d_h))
+        W_O[:, i * d_h:(i + 1) * d_h] = rng.standard_normal((d_h, d_h)) if kind != "interleaved_concat" \
+            else np.eye(d_h)
+        assert np.allclose(oracle.output_project(o, W_O), o[:, i] @ W_O[:, i * d_h:(i + 1) * d_h].T)
+        caught |= not np.allclose(proj(o, W_O), o[:, i] @ W_O[:, i * d_h:(i + 1) * d_h].T)
+    assert caught
