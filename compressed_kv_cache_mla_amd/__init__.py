@@ -2,8 +2,9 @@
 
 A thin ctypes binding over libmla.so (the C ABI in include/mla.h): it only
 marshals arguments -- torch tensors' device pointers, sizes and the current
-HIP stream.  Every step of the path (cache append, query absorption, split-KV
-decode, combine, W^UV epilogue) runs in the library's HIP kernels.
+HIP stream.  Every step of the path (cache append, query projection, query
+absorption, split-KV decode, combine, W^UV epilogue, output projection) runs
+in the library's HIP kernels.
 
 Importing this package does not touch the GPU.  Loading fails loudly if
 libmla.so has not been built (python -m compressed_kv_cache_mla_amd.build).
@@ -26,6 +27,8 @@ FLAG_BAD_SEQ_LEN, FLAG_BAD_PAGE, FLAG_BAD_POSITION, FLAG_BAD_SEQ_ID = 1, 2, 4, 8
 EXPORTED = ("mla_cache_append", "mla_cache_append_ws", "mla_cache_append_workspace_size",
             "mla_decode_workspace_size", "mla_decode", "mla_decode_ex",
             "mla_decode_step_workspace_size", "mla_decode_step",
+            "mla_pack_weight", "mla_query_project_workspace_size", "mla_query_project",
+            "mla_output_project_workspace_size", "mla_output_project",
             "mla_read_error_flags", "mla_last_error", "mla_device_cu_count")
 
 
@@ -102,6 +105,16 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_step.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32, vp, vp,
                                       vp, vp, sz, i32, ctypes.POINTER(mla_decode_opts), vp]
         L.mla_decode_step.restype = ctypes.c_int
+        L.mla_pack_weight.argtypes = [pdims, i32, i32, vp, vp, vp]
+        L.mla_pack_weight.restype = ctypes.c_int
+        L.mla_query_project_workspace_size.argtypes = [pdims, i32, i32]
+        L.mla_query_project_workspace_size.restype = sz
+        L.mla_query_project.argtypes = [pdims, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.mla_query_project.restype = ctypes.c_int
+        L.mla_output_project_workspace_size.argtypes = [pdims, i32]
+        L.mla_output_project_workspace_size.restype = sz
+        L.mla_output_project.argtypes = [pdims, i32, vp, vp, vp, vp, sz, vp]
+        L.mla_output_project.restype = ctypes.c_int
         L.mla_read_error_flags.argtypes = [vp, ctypes.POINTER(i32), vp]
         L.mla_read_error_flags.restype = ctypes.c_int
         L.mla_last_error.argtypes = []
@@ -191,8 +204,9 @@ class HipEvent:
         return float(ms.value)
 
     def __del__(self):
-        if self.handle and HipEvent._hip is not None:
-            HipEvent._hip.hipEventDestroy(self.handle)
+        hip = type(self)._hip      # the class, not the module global (gone at interpreter exit)
+        if self.handle and hip is not None:
+            hip.hipEventDestroy(self.handle)
             self.handle = ctypes.c_void_p()
 
 
@@ -253,6 +267,59 @@ def decode_step(dims: Dims, h_new, W_DKV, W_KR, q_C, q_R, pos_q, W_UK, W_UV, c_K
                                  _ptr(pos_q), _ptr(W_UK), _ptr(W_UV), _ptr(c_KV), _ptr(k_R), row_stride, num_pages,
                                  _ptr(page_table), max_pages, _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace),
                                  workspace.numel(), n_splits, ctypes.byref(o), _stream(stream)))
+
+
+def pack_weight(dims: Dims, W, stream=None):
+    """mla_pack_weight: a new tensor holding W [rows, K] in the packed layout
+    the projection kernels stream (same dtype, same element count)."""
+    if not W.is_contiguous():
+        raise ValueError("pack_weight needs a contiguous row-major W")
+    rows, K = W.shape
+    out = torch.empty_like(W)
+    d = dims.c()
+    _check(lib().mla_pack_weight(ctypes.byref(d), rows, K, _ptr(W), _ptr(out), _stream(stream)))
+    return out
+
+
+def query_project_workspace_size(dims: Dims, B: int, d_cq: int) -> int:
+    d = dims.c()
+    return int(lib().mla_query_project_workspace_size(ctypes.byref(d), B, d_cq))
+
+
+def query_project_workspace(dims: Dims, B: int, d_cq: int, device="cuda"):
+    """A zero-filled workspace for query_project (the library needs it zeroed once)."""
+    return torch.zeros(query_project_workspace_size(dims, B, d_cq), dtype=torch.uint8, device=device)
+
+
+def query_project(dims: Dims, h, W_DQ, W_UQ, W_QR, q_C, q_R, workspace, stream=None):
+    """mla_query_project: q^C = W^UQ (W^DQ h) and q^R = W^QR h (unrotated) for
+    B token states h [B, d_model] into q_C [B, n_h, d_h], q_R [B, n_h, d_hR].
+    The weights are packed (pack_weight); W_DQ None means no query
+    down-projection (c^Q = h)."""
+    B = h.shape[0]
+    d_cq = 0 if W_DQ is None else W_DQ.shape[0]
+    d = dims.c()
+    _check(lib().mla_query_project(ctypes.byref(d), B, d_cq, _ptr(h), _ptr(W_DQ), _ptr(W_UQ), _ptr(W_QR),
+                                   _ptr(q_C), _ptr(q_R), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def output_project_workspace_size(dims: Dims, B: int) -> int:
+    d = dims.c()
+    return int(lib().mla_output_project_workspace_size(ctypes.byref(d), B))
+
+
+def output_project_workspace(dims: Dims, B: int, device="cuda"):
+    """A zero-filled workspace for output_project (the library needs it zeroed once)."""
+    return torch.zeros(output_project_workspace_size(dims, B), dtype=torch.uint8, device=device)
+
+
+def output_project(dims: Dims, o, W_O, u, workspace, stream=None):
+    """mla_output_project: u [B, d_model] = W^O [o_1; ...; o_n_h] for the
+    per-head outputs o [B, n_h, d_h] (fp32); W_O packed (pack_weight)."""
+    B = o.shape[0]
+    d = dims.c()
+    _check(lib().mla_output_project(ctypes.byref(d), B, _ptr(o), _ptr(W_O), _ptr(u), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
 
 
 def read_error_flags(workspace_or_flag, stream=None) -> int:

@@ -44,9 +44,11 @@ __device__ __forceinline__ GemmArgs append_gemm(int32_t T_rows, int32_t d_model,
   GemmArgs g;
   g.X = h;
   g.ldx = d_model;
-  g.W1 = W_DKV;
-  g.W2 = W_KR;
-  g.n_split = D_C;
+  g.W[0] = W_DKV;
+  g.W[1] = W_KR;
+  g.W[2] = g.W[3] = nullptr;
+  g.seg_end[0] = D_C;
+  g.seg_end[1] = g.seg_end[2] = g.seg_end[3] = D_K;
   g.M = T_rows;
   g.N = D_K;
   g.K = d_model;

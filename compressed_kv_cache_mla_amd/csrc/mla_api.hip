@@ -4,7 +4,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <initializer_list>
 #include <string>
+#include <tuple>
 
 #include "append_splitk.h"
 
@@ -199,7 +202,7 @@ static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, 
   pa.page_size = dims->page_size;
   if (opts && opts->impl != 0 && opts->impl != 1) return fail(MLA_ERR_INVALID_ARG, "opts->impl=%d", opts->impl);
   hipError_t e = hipSuccess;
-  if (step && mla::step_prep_supported(*dims)) {
+  if (step && mla::step_prep_supported(*dims, B)) {
     // append (split-K, finished in the same launch), absorption and plan in one launch
     const mla::AppendDst dst{nullptr, pos_q, page_table, B, max_pages, dims->page_size, num_pages,
                              (mla::bf16*)c_KV, (mla::bf16*)k_R, row_stride, mla::rope_table(dims->rope_base),
@@ -254,6 +257,212 @@ mla_status mla_decode_step(const mla_dims* dims, int32_t B, const void* h_new, c
   const StepAppendIn in{h_new, W_DKV, W_KR};
   return decode_impl(dims, B, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride, num_pages, page_table, max_pages,
                      seq_lens, out, lse, workspace, ws_bytes, n_splits, opts, &in, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- projections
+namespace {
+
+// Launch plan of the query projection for batch B.  d_cq > 0: product 1 is
+// h . [W^DQ ; W^QR]^T -> (c^Q in the workspace, q^R), product 2 is
+// c^Q . W^UQ^T -> q^C.  d_cq == 0 (no down-projection): product 1 is
+// h . [W^UQ ; W^QR]^T -> (q^C, q^R).
+struct QueryPlan {
+  bool lowrank, packed;
+  int32_t N1, S1, N2, S2;
+  size_t off_h, off_cq, off_part, total;
+};
+
+// Workspace: split-K tile counters (fixed offset 0), h packed (bf16, more
+// than a few rows), c^Q (packed like h, else row-major), then the chunk sums
+// (shared by the two products, which run one after the other).
+QueryPlan query_plan(const mla_dims& d, int32_t B, int32_t d_cq) {
+  QueryPlan p{};
+  const bool bf = d.dtype == MLA_BF16;
+  p.lowrank = d_cq > 0;
+  p.packed = bf && mla::gemm_x_packed(B);
+  const int64_t rows = p.packed ? mla::gemm_rows_padded(B) : B;
+  p.N1 = (p.lowrank ? d_cq : d.n_h * mla::D_H) + d.n_h * mla::D_R;
+  p.S1 = bf ? mla::gemm_pick_splits(B, p.N1, d.d_model) : 1;
+  p.N2 = p.lowrank ? d.n_h * mla::D_H : 0;
+  p.S2 = bf && p.lowrank ? mla::gemm_pick_splits(B, p.N2, d_cq) : 1;
+  p.off_h = mla::SPLITK_COUNTER_BYTES;
+  p.off_cq = p.off_h + (p.packed ? mla::align256((size_t)rows * d.d_model * 2) : 0);
+  p.off_part = p.off_cq + (p.lowrank ? mla::align256((size_t)rows * d_cq * (bf ? 2 : 4)) : 0);
+  const size_t part = std::max(mla::gemm_part_bytes(B, p.N1, p.S1), p.lowrank ? mla::gemm_part_bytes(B, p.N2, p.S2) : 0);
+  p.total = p.off_part + (bf ? part : 0);
+  return p;
+}
+
+// Output projection workspace: counters, o packed (bf16, more than a few
+// rows), chunk sums.
+struct OutputPlan {
+  bool packed;
+  int32_t S;
+  size_t off_o, off_part, total;
+};
+
+OutputPlan output_plan(const mla_dims& d, int32_t B) {
+  OutputPlan p{};
+  const bool bf = d.dtype == MLA_BF16;
+  const int32_t K = d.n_h * mla::D_H;
+  p.packed = bf && mla::gemm_x_packed(B);
+  p.S = bf ? mla::gemm_pick_splits(B, d.d_model, K) : 1;
+  p.off_o = mla::SPLITK_COUNTER_BYTES;
+  p.off_part = p.off_o + (p.packed ? mla::align256((size_t)mla::gemm_rows_padded(B) * K * 2) : 0);
+  p.total = p.off_part + (bf ? mla::gemm_part_bytes(B, d.d_model, p.S) : 0);
+  return p;
+}
+
+mla_status check_query_dims(const mla_dims* dims, int32_t B, int32_t d_cq) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (B < 1 || B > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "B=%d out of range", B);
+  if (d_cq < 0 || d_cq > 65536 || d_cq % 128 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "d_cq=%d must be 0 or a positive multiple of 128 up to 65536", d_cq);
+  if (dims->dtype == MLA_BF16 && dims->d_model % 128 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 projections need d_model %% 128 == 0 (got %d)", dims->d_model);
+  return MLA_OK;
+}
+
+mla::GemmArgs gemm_args(const void* X, int64_t ldx, int32_t M, int32_t K, char* counters) {
+  mla::GemmArgs g{};
+  g.counters = (int32_t*)counters;
+  g.X = X;
+  g.ldx = ldx;
+  g.M = M;
+  g.K = K;
+  g.S = 1;
+  return g;
+}
+
+// Stacks the weight segments (W, rows) of a product; unused segments end at N.
+void gemm_segments(mla::GemmArgs& g, mla::GemmOut& o, std::initializer_list<std::tuple<const void*, int32_t, void*, int64_t>> segs) {
+  int i = 0, end = 0;
+  for (const auto& sg : segs) {
+    end += std::get<1>(sg);
+    g.W[i] = (const mla::bf16*)std::get<0>(sg);
+    g.seg_end[i] = end;
+    o.Y[i] = std::get<2>(sg);
+    o.ldy[i] = std::get<3>(sg);
+    ++i;
+  }
+  g.N = end;
+  for (; i < mla::GK_SEG; ++i) {
+    g.W[i] = nullptr;
+    g.seg_end[i] = end;
+    o.Y[i] = nullptr;
+    o.ldy[i] = 0;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_query_project_workspace_size(const mla_dims* dims, int32_t B, int32_t d_cq) {
+  if (check_query_dims(dims, B, d_cq) != MLA_OK) return 0;
+  return query_plan(*dims, B, d_cq).total;
+}
+
+mla_status mla_query_project(const mla_dims* dims, int32_t B, int32_t d_cq, const void* h, const void* W_DQ,
+                             const void* W_UQ, const void* W_QR, void* q_C, void* q_R, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  mla_status st = check_query_dims(dims, B, d_cq);
+  if (st != MLA_OK) return st;
+  if (!h || !W_UQ || !W_QR || !q_C || !q_R || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer among h, W_UQ, W_QR, q_C, q_R, workspace");
+  if ((d_cq > 0) != (W_DQ != nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "W_DQ must be given exactly when d_cq > 0 (d_cq=%d)", d_cq);
+  if (!aligned16(h) || !aligned16(W_UQ) || !aligned16(W_QR) || !aligned16(q_C) || !aligned16(q_R) ||
+      (W_DQ && !aligned16(W_DQ)))
+    return fail(MLA_ERR_INVALID_ARG, "h / weights / q_C / q_R not 16-byte aligned");
+  if (((uintptr_t)workspace & 255) != 0) return fail(MLA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  const QueryPlan p = query_plan(*dims, B, d_cq);
+  if (ws_bytes < p.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, p.total);
+  const bool f32 = dims->dtype == MLA_FP32;
+  const int32_t nq = dims->n_h * mla::D_H, nr = dims->n_h * mla::D_R;
+  char* ws = (char*)workspace;
+  void* c_Q = ws + p.off_cq;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t rows = mla::gemm_rows_padded(B);
+  hipError_t e = hipSuccess;
+  const void* X1 = h;
+  if (p.packed) {
+    e = mla::launch_pack(h, dims->d_model, B, rows, dims->d_model, false, false, ws + p.off_h, s);
+    X1 = ws + p.off_h;
+  }
+  mla::GemmArgs g = gemm_args(X1, dims->d_model, B, dims->d_model, ws);
+  mla::GemmOut o{};
+  if (p.lowrank)
+    gemm_segments(g, o, {{W_DQ, d_cq, c_Q, p.packed ? -(int64_t)d_cq : d_cq}, {W_QR, nr, q_R, nr}});
+  else
+    gemm_segments(g, o, {{W_UQ, nq, q_C, nq}, {W_QR, nr, q_R, nr}});
+  g.S = p.S1;
+  g.part = (float*)(ws + p.off_part);
+  if (e == hipSuccess) e = mla::launch_gemm(g, o, f32, f32, f32, s);
+  if (e == hipSuccess && p.lowrank) {
+    mla::GemmArgs g2 = gemm_args(c_Q, d_cq, B, d_cq, ws);
+    mla::GemmOut o2{};
+    gemm_segments(g2, o2, {{W_UQ, nq, q_C, nq}});
+    g2.S = p.S2;
+    g2.part = (float*)(ws + p.off_part);
+    e = mla::launch_gemm(g2, o2, f32, f32, f32, s);
+  }
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "query projection launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t mla_output_project_workspace_size(const mla_dims* dims, int32_t B) {
+  if (check_query_dims(dims, B, 0) != MLA_OK) return 0;
+  return output_plan(*dims, B).total;
+}
+
+mla_status mla_output_project(const mla_dims* dims, int32_t B, const float* o, const void* W_O, float* u,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  mla_status st = check_query_dims(dims, B, 0);
+  if (st != MLA_OK) return st;
+  if (!o || !W_O || !u || !workspace) return fail(MLA_ERR_INVALID_ARG, "null pointer among o, W_O, u, workspace");
+  if (!aligned16(o) || !aligned16(W_O) || !aligned16(u))
+    return fail(MLA_ERR_INVALID_ARG, "o / W_O / u not 16-byte aligned");
+  if (((uintptr_t)workspace & 255) != 0) return fail(MLA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  const OutputPlan p = output_plan(*dims, B);
+  if (ws_bytes < p.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, p.total);
+  const bool f32 = dims->dtype == MLA_FP32;
+  const int32_t K = dims->n_h * mla::D_H;
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  const void* X = o;
+  if (p.packed) {
+    e = mla::launch_pack(o, K, B, mla::gemm_rows_padded(B), K, true, true, ws + p.off_o, s);
+    X = ws + p.off_o;
+  }
+  mla::GemmArgs g = gemm_args(X, K, B, K, ws);
+  mla::GemmOut out{};
+  gemm_segments(g, out, {{W_O, dims->d_model, u, dims->d_model}});
+  g.S = p.S;
+  g.part = (float*)(ws + p.off_part);
+  if (e == hipSuccess) e = mla::launch_gemm(g, out, f32, true, true, s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "output projection launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mla_status mla_pack_weight(const mla_dims* dims, int32_t rows, int32_t K, const void* W, void* W_packed,
+                           void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (rows < 16 || rows % 16 != 0 || K < 32 || K % 32 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "rows=%d must be a positive multiple of 16 and K=%d of 32", rows, K);
+  if ((int64_t)rows * K >= ((int64_t)1 << 40)) return fail(MLA_ERR_INVALID_ARG, "matrix too large");
+  if (!W || !W_packed) return fail(MLA_ERR_INVALID_ARG, "W / W_packed is NULL");
+  if (!aligned16(W) || !aligned16(W_packed)) return fail(MLA_ERR_INVALID_ARG, "W / W_packed not 16-byte aligned");
+  const bool f32 = dims->dtype == MLA_FP32;
+  hipError_t e = mla::launch_pack(W, K, rows, rows, K, f32, false, W_packed, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "pack launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 mla_status mla_read_error_flags(void* workspace_or_flag, int32_t* flags, void* stream) {

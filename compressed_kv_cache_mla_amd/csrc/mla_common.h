@@ -73,8 +73,9 @@ constexpr int SPLIT_REC = 8;
 constexpr int APPEND_SK_SPLIT = 8;
 
 // Decode workspace layout (bytes, each part 256-aligned).  flags: word 0 the
-// decode's error flags, word 1 (decode step only) the append's.  The decode
-// step adds the split-K append's chunk sums and its per-tile counters.
+// decode's error flags, word 1 (decode step only) the append's; then the
+// split-K tile counters (used by the decode step's append).  The decode step
+// adds the split-K append's chunk sums.
 struct DecodeWs {
   size_t flags, prefix, splits, qabs, part_ml, part_o, app_part, app_cnt, total;
   int32_t n_slots;
@@ -82,22 +83,28 @@ struct DecodeWs {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Tile counters of in-launch split-K reductions.  A product is split only
+// while it has fewer tiles than fill the GPU (1024 workgroups), so 1024
+// counters serve any product; they sit at a fixed offset of every workspace
+// (right after the flags) and each completed launch leaves them at zero, so
+// a workspace zero-filled once stays valid for every batch size and for
+// consecutive products.
+constexpr int SPLITK_COUNTERS = 1024;
+constexpr size_t SPLITK_COUNTER_BYTES = SPLITK_COUNTERS * 4;
+
 inline DecodeWs decode_ws_layout(int32_t B, int32_t n_h, int32_t n_splits, int elt, bool step = false) {
   DecodeWs w;
   w.n_slots = n_splits + B;
   size_t off = 0;
   w.flags = off;   off += 256;
+  w.app_cnt = off; off += SPLITK_COUNTER_BYTES;
   w.prefix = off;  off += align256((size_t)(B + 1) * 4);
   w.splits = off;  off += align256((size_t)n_splits * SPLIT_REC * 4);   // per split: see plan_block
   w.qabs = off;    off += align256((size_t)B * n_h * D_K * elt);
   w.part_ml = off; off += align256((size_t)w.n_slots * n_h * 2 * 4);
   w.part_o = off;  off += align256((size_t)w.n_slots * n_h * D_C * elt);   // partial O~ in the cache type
-  w.app_part = w.app_cnt = off;
-  if (step) {
-    off += align256((size_t)APPEND_SK_SPLIT * B * D_K * 4);                // fp32 chunk sums
-    w.app_cnt = off;
-    off += align256((size_t)((B + 31) / 32) * (D_K / 16) * 4);             // one counter per 32 x 16 tile
-  }
+  w.app_part = off;
+  if (step) off += align256((size_t)APPEND_SK_SPLIT * B * D_K * 4);       // fp32 chunk sums
   w.total = off;
   return w;
 }
@@ -229,7 +236,7 @@ hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const vo
 // token (finished in the same launch), the query absorption and the plan, as
 // one grid (bf16, d_model a multiple of 1024; step_prep_supported()).
 struct AppendDst;
-bool step_prep_supported(const mla_dims& d);
+bool step_prep_supported(const mla_dims& d, int32_t B);
 hipError_t launch_step_prep(const mla_dims& d, int32_t B, const void* h_new, const void* W_DKV, const void* W_KR,
                             const void* q_C, const void* q_R, const int32_t* pos_q, const void* W_UK, void* qabs,
                             const PlanArgs& pa, float* app_part, int32_t* app_cnt, const AppendDst& dst,

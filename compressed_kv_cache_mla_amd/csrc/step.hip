@@ -66,8 +66,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) s
 
 }  // namespace
 
-bool step_prep_supported(const mla_dims& d) {
-  return d.dtype == MLA_BF16 && d.d_model % (SK_SPLIT * 4 * 32) == 0;
+bool step_prep_supported(const mla_dims& d, int32_t B) {
+  return d.dtype == MLA_BF16 && d.d_model % (SK_SPLIT * 4 * 32) == 0 &&
+         (int64_t)((B + SK_TOK - 1) / SK_TOK) * (D_K / 16) <= SPLITK_COUNTERS;
 }
 
 hipError_t launch_step_prep(const mla_dims& d, int32_t B, const void* h_new, const void* W_DKV, const void* W_KR,

@@ -19,7 +19,8 @@
  *     1/sqrt(d_h + d_hR)); softmax over every cached token of the sequence.
  *   - Weights are [out, in] row-major: W^DKV [d_c, d_model], W^KR [d_hR, d_model],
  *     W^UK and W^UV [n_h*d_h, d_c]; head i owns rows i*d_h .. i*d_h+d_h-1.
- *   - The output is each head's o_i = W^UV_i O~_i (fp32); W_O is not applied.
+ *   - The attention output is each head's o_i = W^UV_i O~_i (fp32);
+ *     mla_output_project applies W_O to it.
  *
  * Latent cache (paged pool, owned by the caller):
  *   A pool row r holds one token: c^KV at c_KV + r*row_stride (d_c elements)
@@ -225,6 +226,75 @@ mla_status mla_decode_step(const mla_dims* dims, int32_t B, const void* h_new, c
                            int32_t num_pages, const int32_t* page_table, int32_t max_pages,
                            const int32_t* seq_lens, float* out, float* lse, void* workspace, size_t ws_bytes,
                            int32_t n_splits, const mla_decode_opts* opts, void* stream);
+
+/*
+ * mla_pack_weight -- copy a row-major weight W [rows, K] (dims.dtype) into
+ * the packed layout the projection kernels stream (mla_query_project,
+ * mla_output_project): blocks of 16 rows x 32 columns, block (rb, ks) at
+ * element (rb*K/32 + ks)*512, inside it lane l's 8 elements (row 16rb + l%16,
+ * columns 32ks + 8(l/16) .. +7) at l*8 -- the lane order of a 16x16x32 MFMA
+ * operand, so that a wave reads each block as one contiguous 1 KB run.  A
+ * permutation: W_packed holds rows*K elements.  Done once per weight.
+ *   rows: multiple of 16; K: multiple of 32; W, W_packed 16-byte aligned,
+ *   device memory, not overlapping.
+ */
+mla_status mla_pack_weight(const mla_dims* dims, int32_t rows, int32_t K, const void* W, void* W_packed,
+                           void* stream);
+
+/*
+ * mla_query_project_workspace_size -- bytes of device workspace
+ * mla_query_project needs for batch B and query rank d_cq; 0 for invalid
+ * arguments.
+ *
+ * mla_query_project -- the decode queries of B tokens from their states h
+ * (liang.world ch.2 §2, closing paragraph: the query has its own low-rank
+ * compression c^Q; tuntang.top MLA section, "RoPE 的兼容性处理": q_t =
+ * [W^UQ c_t^Q ; W^QR h_t RoPE(t)]):
+ *     c^Q = W^DQ h     (d_cq wide; the pages give no formula or width for it:
+ *                       this is the analogue of c^KV = W^DKV h)
+ *     q^C = W^UQ c^Q   per head,  q^R = W^QR h  per head, NOT rotated
+ * so that q_C / q_R feed mla_decode / mla_decode_step directly (they rotate
+ * q^R at the query position).  d_cq == 0 means no down-projection (c^Q = h,
+ * W_DQ NULL, W_UQ [n_h*d_h, d_model]).
+ *   h          [B, d_model]          dtype   device
+ *   W_DQ       [d_cq, d_model]       dtype   device, packed (NULL iff d_cq == 0)
+ *   W_UQ       [n_h*d_h, d_cq]       dtype   device, packed ([n_h*d_h, d_model] when d_cq == 0)
+ *   W_QR       [n_h*d_hR, d_model]   dtype   device, packed
+ *   (packed: the weight's row-major form passed through mla_pack_weight)
+ *   q_C        [B, n_h, d_h]         dtype   device, written
+ *   q_R        [B, n_h, d_hR]        dtype   device, written
+ *   workspace  ws_bytes >= mla_query_project_workspace_size(dims, B, d_cq),
+ *              256-byte aligned device memory, ZERO-FILLED ONCE after
+ *              allocation (it holds counters of in-launch split-K reductions,
+ *              which every completed call leaves at zero); it also holds c^Q.
+ * d_cq must be 0 or a multiple of 128; for bf16 d_model must be a multiple of
+ * 128.  bf16: operands bf16, fp32 accumulation, c^Q rounded to bf16 before
+ * the second product; fp32: everything fp32.  Deterministic for fixed inputs.
+ * Calls that share one workspace must be ordered (e.g. on one stream).
+ */
+size_t mla_query_project_workspace_size(const mla_dims* dims, int32_t B, int32_t d_cq);
+mla_status mla_query_project(const mla_dims* dims, int32_t B, int32_t d_cq, const void* h, const void* W_DQ,
+                             const void* W_UQ, const void* W_QR, void* q_C, void* q_R, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * mla_output_project_workspace_size -- bytes of device workspace
+ * mla_output_project needs for batch B; 0 for invalid arguments.
+ *
+ * mla_output_project -- u = W^O [o_1; ...; o_{n_h}] per token: the heads'
+ * outputs concatenated in head order and multiplied by the output matrix
+ * (liang.world ch.2 §1, the attention output step).
+ *   o          [B, n_h, d_h]        fp32    device (as mla_decode writes it;
+ *                                            rounded to bf16 for the bf16 product)
+ *   W_O        [d_model, n_h*d_h]   dtype   device, packed (mla_pack_weight)
+ *   u          [B, d_model]         fp32    device, written
+ *   workspace  ws_bytes >= mla_output_project_workspace_size(dims, B),
+ *              256-byte aligned, ZERO-FILLED ONCE (as for mla_query_project).
+ * Deterministic for fixed inputs; calls sharing a workspace must be ordered.
+ */
+size_t mla_output_project_workspace_size(const mla_dims* dims, int32_t B);
+mla_status mla_output_project(const mla_dims* dims, int32_t B, const float* o, const void* W_O, float* u,
+                              void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * mla_read_error_flags -- wait for `stream`, then copy the device error flags

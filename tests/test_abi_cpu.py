@@ -126,10 +126,148 @@ def test_decode_step_workspace_holds_the_append_reduction():
     for B in (1, 16, 17, 64, 200):
         dec = L.mla_decode_workspace_size(ctypes.byref(d), B, 256)
         step = L.mla_decode_step_workspace_size(ctypes.byref(d), B, 256)
-        # 8 fp32 chunk sums per output element and one counter per 32-token x 16-column tile
-        assert step >= dec + 8 * B * 576 * 4 + ((B + 31) // 32) * 36 * 4
-        assert step - dec < 8 * B * 576 * 4 + ((B + 31) // 32) * 36 * 4 + 512
+        # 8 fp32 chunk sums per output element (the tile counters sit in every layout)
+        assert step >= dec + 8 * B * 576 * 4
+        assert step - dec < 8 * B * 576 * 4 + 256
     assert L.mla_decode_step_workspace_size(ctypes.byref(_dims(d_c=1)), 4, 256) == 0
+
+
+# ---- projections
+COUNTER_BYTES = 1024 * 4          # split-K tile counters at the start of the workspace
+
+
+def _splits(M, N, K):
+    """K chunks of a bf16 projection: double while the grid has fewer than
+    1024 workgroups, up to 16, while 128 * 2S divides K."""
+    tiles = (N // 16) * ((M + 31) // 32)
+    S = 1
+    while S < 16 and tiles * S < 1024 and K % (2 * S * 128) == 0:
+        S *= 2
+    return S
+
+
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+def _splits_rows(M):
+    return 16 if M <= 16 else 32 if M <= 32 else 64
+
+
+def _splits(M, N, K):
+    """K chunks of a bf16 projection: none from 512 tiles on, else double
+    while the grid has fewer than 1024 workgroups, up to 16, while 128 * 2S
+    divides K (16, 32 or 64 rows per workgroup)."""
+    rows = _splits_rows(M)
+    tiles = (N // 16) * ((M + rows - 1) // rows)
+    if tiles >= 512:                       # two tiles per CU: not split
+        return 1
+    S = 1
+    while S < 16 and tiles * S < 1024 and K % (2 * S * 128) == 0:
+        S *= 2
+    return S
+
+
+@pytest.mark.parametrize("B,d_cq,n_h,d_model", [(32, 1536, 128, 5120), (64, 1536, 128, 5120), (1, 512, 16, 1024),
+                                                (5, 256, 16, 1024), (40, 0, 16, 1024), (300, 1536, 128, 5120),
+                                                (9, 128, 16, 1024)])
+def test_query_project_workspace_size(B, d_cq, n_h, d_model):
+    L = mla.lib()
+    d = _dims(n_h=n_h, d_model=d_model)
+    N1 = (d_cq if d_cq else n_h * 128) + n_h * 64
+    S1 = _splits(B, N1, d_model)
+    part = S1 * B * N1 * 4 if S1 > 1 else 0
+    if d_cq:
+        S2 = _splits(B, n_h * 128, d_cq)
+        part = max(part, S2 * B * n_h * 128 * 4 if S2 > 1 else 0)
+    packed = B > 8                         # activations packed above 8 rows, padded to 64
+    rows = (B + 63) // 64 * 64 if packed else B
+    h = _a256(rows * d_model * 2) if packed else 0
+    cq = _a256(rows * d_cq * 2)
+    assert L.mla_query_project_workspace_size(ctypes.byref(d), B, d_cq) == COUNTER_BYTES + h + cq + _a256(part)
+    f = _dims(n_h=n_h, d_model=d_model, dtype=mla.MLA_FP32)
+    assert L.mla_query_project_workspace_size(ctypes.byref(f), B, d_cq) == COUNTER_BYTES + _a256(B * d_cq * 4)
+
+
+def test_split_products_fit_the_tile_counters():
+    """A product is split only while it has fewer than 1024 tiles."""
+    for M in (1, 7, 16, 17, 32, 33, 64, 100, 500):
+        for N, K in ((9728, 5120), (16384, 1536), (5120, 16384), (576, 5120), (1280, 1024), (2048, 256)):
+            S = _splits(M, N, K)
+            rows = _splits_rows(M)
+            assert S == 1 or (N // 16) * ((M + rows - 1) // rows) <= 1024
+
+
+def test_output_project_workspace_size():
+    L = mla.lib()
+    for B, n_h, d_model in ((32, 128, 5120), (64, 128, 5120), (1, 16, 1024), (37, 16, 1024), (128, 128, 5120),
+                            (8, 16, 1024), (9, 16, 1024)):
+        d = _dims(n_h=n_h, d_model=d_model)
+        K = n_h * 128
+        S = _splits(B, d_model, K)
+        o = _a256((B + 63) // 64 * 64 * K * 2) if B > 8 else 0
+        want = COUNTER_BYTES + o + (_a256(S * B * d_model * 4) if S > 1 else 0)
+        assert L.mla_output_project_workspace_size(ctypes.byref(d), B) == want
+        f = _dims(n_h=n_h, d_model=d_model, dtype=mla.MLA_FP32)
+        assert L.mla_output_project_workspace_size(ctypes.byref(f), B) == COUNTER_BYTES
+
+
+def test_pack_weight_rejects_bad_shapes():
+    L = mla.lib()
+    p = ctypes.c_void_p(16 * 4096)
+    d = _dims()
+    assert L.mla_pack_weight(ctypes.byref(d), 24, 64, p, p, None) == mla.MLA_ERR_INVALID_ARG    # rows % 16
+    assert L.mla_pack_weight(ctypes.byref(d), 32, 48, p, p, None) == mla.MLA_ERR_INVALID_ARG    # K % 32
+    assert L.mla_pack_weight(ctypes.byref(d), 0, 64, p, p, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_pack_weight(ctypes.byref(d), 32, 64, None, p, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_pack_weight(ctypes.byref(d), 32, 64, p, ctypes.c_void_p(16 * 4096 + 2), None) == \
+        mla.MLA_ERR_INVALID_ARG
+    assert L.mla_pack_weight(None, 32, 64, p, p, None) == mla.MLA_ERR_INVALID_ARG
+
+
+def _query(dims, B=4, d_cq=512, ptr=16, wdq=True, ws_bytes=1 << 30, ws=1 << 20):
+    L = mla.lib()
+    p = ctypes.c_void_p(ptr * 4096) if ptr else None
+    return L.mla_query_project(ctypes.byref(dims) if dims is not None else None, B, d_cq, p, p if wdq else None, p,
+                               p, p, p, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_query_project_rejects_bad_arguments_before_launching():
+    L = mla.lib()
+    assert _query(None) == mla.MLA_ERR_INVALID_ARG
+    assert _query(_dims(d_c=256)) == mla.MLA_ERR_UNSUPPORTED
+    assert _query(_dims(), B=0) == mla.MLA_ERR_INVALID_ARG
+    assert _query(_dims(), d_cq=100) == mla.MLA_ERR_UNSUPPORTED      # not a multiple of 128
+    assert _query(_dims(), d_cq=-128) == mla.MLA_ERR_UNSUPPORTED
+    assert _query(_dims(d_model=5056)) == mla.MLA_ERR_UNSUPPORTED    # bf16 needs d_model % 128 == 0
+    assert _query(_dims(), wdq=False) == mla.MLA_ERR_INVALID_ARG     # d_cq > 0 without W_DQ
+    assert b"W_DQ" in L.mla_last_error()
+    assert _query(_dims(), d_cq=0) == mla.MLA_ERR_INVALID_ARG        # W_DQ given with d_cq == 0
+    assert _query(_dims(), ptr=0) == mla.MLA_ERR_INVALID_ARG
+    assert _query(_dims(), ws=(1 << 20) + 16) == mla.MLA_ERR_INVALID_ARG   # workspace not 256-aligned
+    assert _query(_dims(), ws_bytes=100) == mla.MLA_ERR_WORKSPACE
+    assert _query(_dims(), ptr=0) == mla.MLA_ERR_INVALID_ARG
+    L2 = mla.lib()
+    p = ctypes.c_void_p(16 * 4096)
+    bad = ctypes.c_void_p(16 * 4096 + 8)
+    d = _dims()
+    assert L2.mla_query_project(ctypes.byref(d), 4, 512, bad, p, p, p, p, p, ctypes.c_void_p(1 << 20), 1 << 30,
+                                None) == mla.MLA_ERR_INVALID_ARG   # h misaligned
+
+
+def test_output_project_rejects_bad_arguments_before_launching():
+    L = mla.lib()
+    p = ctypes.c_void_p(16 * 4096)
+    ws = ctypes.c_void_p(1 << 20)
+    d = _dims()
+    assert L.mla_output_project(None, 4, p, p, p, ws, 1 << 30, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_output_project(ctypes.byref(d), 0, p, p, p, ws, 1 << 30, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_output_project(ctypes.byref(d), 4, None, p, p, ws, 1 << 30, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_output_project(ctypes.byref(d), 4, p, p, ctypes.c_void_p(16 * 4096 + 4), ws, 1 << 30,
+                                None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_output_project(ctypes.byref(d), 4, p, p, p, ws, 10, None) == mla.MLA_ERR_WORKSPACE
+    assert L.mla_output_project(ctypes.byref(_dims(d_h=64)), 4, p, p, p, ws, 1 << 30, None) == \
+        mla.MLA_ERR_UNSUPPORTED
 
 
 # ---- the split arithmetic the decode and combine kernels share
