@@ -11,8 +11,10 @@ workload (own weights, queries and cache) whose total size exceeds it.
 
 Prints one JSON line.  `value` is decode tokens/s (B sequences per step);
 `roofline` is computed for the split-KV attention kernel from its algorithmic
-bytes and its HIP-event duration measured in the timed region; `cpu_baseline`
-times the fp64 CPU oracle on a bounded sample of the same workload.
+bytes and its HIP-event duration measured in the timed region; `projections`
+times the query path (W^DQ, W^UQ, W^QR) and the output projection W^O, which
+sit outside the step, at the same batch sizes; `cpu_baseline` times the fp64
+CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -77,6 +79,57 @@ def measured_copy_gbps(torch) -> float:
     return 2 * n / (best * 1e-3) / 1e9
 
 
+def measure_projections(torch, mla, B: int, n_h: int = 128, d_model: int = 5120, d_cq: int = 1536, reps: int = 20):
+    """The weight-streaming projections around the attention at batch B
+    (DeepSeek-V2 sizes; d_cq = 1536, a choice: the pages give no query rank):
+    mla_query_project (W^DQ, W^UQ, W^QR) and mla_output_project (W^O), each
+    timed with fence-free HIP events per call over three rotating weight sets
+    (about 1 GB, past the Infinity Cache).  Algorithmic bytes = weights +
+    activations in and out."""
+    import seeded_inputs as si
+    dims = mla.Dims(n_h=n_h, d_model=d_model)
+    bf = torch.bfloat16
+
+    def w(seed, name, rows, cols):
+        return mla.pack_weight(dims, si.normal(si.stream_key(seed, name), (rows, cols), cols ** -0.5, bf, "cuda"))
+
+    sets = []
+    for i in range(3):
+        seed = 4242 + i
+        sets.append(dict(h=si.normal(si.stream_key(seed, "h"), (B, d_model), 1.0, bf, "cuda"),
+                         W_DQ=w(seed, "W_DQ", d_cq, d_model), W_UQ=w(seed, "W_UQ", n_h * 128, d_cq),
+                         W_QR=w(seed, "W_QR", n_h * 64, d_model), W_O=w(seed, "W_O", d_model, n_h * 128),
+                         o=si.normal(si.stream_key(seed, "o"), (B, n_h, 128), 1.0, torch.float32, "cuda")))
+    q_C = torch.empty((B, n_h, 128), dtype=bf, device="cuda")
+    q_R = torch.empty((B, n_h, 64), dtype=bf, device="cuda")
+    u = torch.empty((B, d_model), dtype=torch.float32, device="cuda")
+    wq = mla.query_project_workspace(dims, B, d_cq)
+    wo = mla.output_project_workspace(dims, B)
+    q_bytes = 2 * (d_cq * d_model + n_h * 128 * d_cq + n_h * 64 * d_model) + 2 * B * d_model + 2 * B * n_h * 192
+    o_bytes = 2 * d_model * n_h * 128 + 4 * B * n_h * 128 + 4 * B * d_model
+    out = {}
+    for name, fn, nbytes in (
+            ("query_project", lambda x: mla.query_project(dims, x["h"], x["W_DQ"], x["W_UQ"], x["W_QR"], q_C, q_R, wq),
+             q_bytes),
+            ("output_project", lambda x: mla.output_project(dims, x["o"], x["W_O"], u, wo), o_bytes)):
+        for i in range(6):
+            fn(sets[i % 3])
+        torch.cuda.synchronize()
+        evs = [(mla.HipEvent(), mla.HipEvent()) for _ in range(reps)]
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            fn(sets[i % 3])
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.median([1e3 * a.elapsed_ms(b) for a, b in evs]))
+        gbps = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"B": B, "us_p50": round(us, 2), "alg_MB": round(nbytes / 1e6, 1), "GBps": round(gbps, 1),
+                     "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wl, seconds: float):
     """The fp64 oracle (absorbed form) doing the same per-sequence work as a
     step -- append the newest token, then decode -- on a bounded sample."""
@@ -126,6 +179,9 @@ def main():
     ap.add_argument("--impl", type=int, default=0, help="0 = MFMA attention kernel, 1 = VALU reference kernel")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-projections", action="store_true", help="skip the query / output projection timings")
+    ap.add_argument("--projections-only", default="",
+                    help="comma-separated batch sizes: only time the query / output projections at them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM "
                          "byte counters of rocprofv3)")
@@ -147,6 +203,10 @@ def main():
         return
     import workloads as W
     import compressed_kv_cache_mla_amd as mla
+    if args.projections_only:
+        print(json.dumps({f"B{b}": measure_projections(torch, mla, int(b))
+                          for b in args.projections_only.split(",")}), flush=True)
+        return
 
     def measure(name, steps, warmup):
         """Build rotating copies of a workload, run warmup + timed steps;
@@ -243,6 +303,10 @@ def main():
             "mfma_frac": round(a2["attn_flops"] / (k2 * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "hbm_frac_of_measured_copy": round(a2["attn_bytes"] / (k2 * 1e-6) / 1e9 / copy_gbps, 4),
             "copies_rotated": c2, **d2}
+    if not args.no_projections:
+        # rows past the attention step: the query path and W^O, at the batches reported above
+        res["projections"] = {f"B{b}": measure_projections(torch, mla, b) for b in
+                              sorted({B, res.get("target_shape", {}).get("B", B)})}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -59,6 +59,112 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmArgs g, GemmOut o) {
   gemm_finish_tile<MT>(n_blk, m_blk, g, epi, &flag);
 }
 
+// Wide workgroup for products with more than 16 rows: 16*NT columns x 16*MT
+// rows (MT = 2 or 4, X packed), 4 waves over quarters of the K chunk.  Per
+// K-step a wave loads MT activation and NT weight fragments (1 KB each) and
+// runs MT*NT MFMAs, so that each activation fragment serves NT weight tiles
+// (activation bytes per weight byte MT/NT instead of MT).  The four waves'
+// sums are added in LDS in the order ((w3 + w2) + w1) + w0 into
+// red[16MT][16NT + 1].
+template <int MT, int NT, int KB>
+__device__ __forceinline__ void gemm_accumulate_wide(int n_blk, int kc, int m_blk, const GemmArgs& g, float* red) {
+  constexpr int LD = 16 * NT + 1;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n0 = n_blk * 16 * NT;
+  const int K = g.K;
+  int beg;
+  const int seg = gemm_segment(g, n0, &beg);
+  const int kchunk = K / g.S, kw = kchunk / 4, nks = kw / 32;
+  const int64_t kbase = (int64_t)kc * kchunk + wave * kw;
+  const int64_t tile = (int64_t)(K >> 5) * 512;   // elements from one 16-row block to the next
+  const bf16* wp = gemm_weight(g, seg) + ((int64_t)((n0 - beg) >> 4) * (K >> 5) + (kbase >> 5)) * 512 + lane * 8;
+  const bf16* xp = (const bf16*)g.X + ((int64_t)(m_blk * MT) * (K >> 5) + (kbase >> 5)) * 512 + lane * 8;
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int c = 0; c < NT; ++c) acc[t][c] = f32x4{0, 0, 0, 0};
+  for (int b0 = 0; b0 < nks; b0 += KB) {
+    bf16x8 wv[NT][KB], xv[MT][KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+      if (b0 + i < nks) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) wv[c][i] = *(const bf16x8*)(wp + c * tile + 512 * (b0 + i));
+#pragma unroll
+        for (int t = 0; t < MT; ++t) xv[t][i] = *(const bf16x8*)(xp + t * tile + 512 * (b0 + i));
+      }
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+      if (b0 + i < nks) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int c = 0; c < NT; ++c)
+            acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[t][i], wv[c][i], acc[t][c], 0, 0, 0);
+      }
+  }
+  // C layout: lane holds column 16c + lane%16, rows 16t + 4*(lane/16) + i
+  for (int w = 3; w >= 0; --w) {
+    if (wave == w) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float* p = red + (16 * t + 4 * (lane >> 4) + i) * LD + 16 * c + (lane & 15);
+            *p = w == 3 ? acc[t][c][i] : acc[t][c][i] + *p;
+          }
+    }
+    __syncthreads();
+  }
+}
+
+// Grid: S * (N / (16 NT)) * ceil(M / (16 MT)) workgroups, ordered as for
+// gemm_bf16_kernel.  S > 1: chunk sums at system scope and the in-launch
+// finish by the tile's last workgroup, as in gemm_finish_tile.
+template <int MT, int NT, typename YT>
+__global__ void __launch_bounds__(256) gemm_wide_kernel(GemmArgs g, GemmOut o) {
+  constexpr int ROWS = 16 * MT, COLS = 16 * NT, PAIRS = 8 * NT, LD = COLS + 1;
+  __shared__ float red[ROWS * LD];
+  __shared__ int flag;
+  const int ntw = g.N / COLS;
+  const int bid = blockIdx.x, tid = threadIdx.x;
+  const int kc = bid % g.S, n_blk = (bid / g.S) % ntw, m_blk = bid / (g.S * ntw);
+  gemm_accumulate_wide<MT, NT, GW_KB>(n_blk, kc, m_blk, g, red);
+  if (g.S == 1) {
+    for (int q = tid; q < ROWS * PAIRS; q += 256) {
+      const int r = q / PAIRS, cp = q % PAIRS;
+      const int m = m_blk * ROWS + r;
+      if (m < g.M) gemm_store_pair<YT>(g, o, m, n_blk * PAIRS + cp, red[r * LD + 2 * cp], red[r * LD + 2 * cp + 1]);
+    }
+    return;
+  }
+  for (int q = tid; q < ROWS * COLS; q += 256) {
+    const int r = q / COLS, c = q % COLS;
+    const int m = m_blk * ROWS + r;
+    if (m < g.M)
+      __hip_atomic_store(g.part + ((int64_t)kc * g.M + m) * g.N + n_blk * COLS + c, red[r * LD + c], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's sum stores are complete
+  __syncthreads();
+  int32_t* cnt = g.counters + (int64_t)m_blk * ntw + n_blk;
+  if (tid == 0) flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g.S - 1;
+  __syncthreads();
+  if (!flag) return;
+  for (int q = tid; q < ROWS * PAIRS; q += 256) {
+    const int r = q / PAIRS, cp = q % PAIRS;
+    const int m = m_blk * ROWS + r;
+    if (m < g.M) {
+      const float2 x = gemm_sum_pair<true>(m, n_blk * PAIRS + cp, g);
+      gemm_store_pair<YT>(g, o, m, n_blk * PAIRS + cp, x.x, x.y);
+    }
+  }
+  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // fp32: wave w of workgroup b computes output (m, n) = divmod(4b + w, N) from
 // row-major X and packed W; the 64 lanes take every 64th k and the lane sums
 // are added by a butterfly.
@@ -94,11 +200,19 @@ __global__ void __launch_bounds__(256) pack_kernel(const TI* __restrict__ src, i
   const int64_t kb = K >> 5;
   const int64_t r = (b / kb) * 16 + (l & 15);
   const int64_t c = (b % kb) * 32 + (l >> 4) * 8;
-  TO v[8];
+  // 8 consecutive source elements (16 or 32 aligned bytes) -> 8 consecutive outputs
+  typedef __attribute__((ext_vector_type(8))) TI vin_t;
+  typedef __attribute__((ext_vector_type(8))) TO vout_t;
+  vout_t v;
+  if (r < rows) {
+    const vin_t x = *(const vin_t*)(src + r * ld + c);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = r < rows ? (TO)src[r * ld + c + i] : (TO)0.f;
+    for (int i = 0; i < 8; ++i) v[i] = (TO)x[i];
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dst[q * 8 + i] = v[i];
+    for (int i = 0; i < 8; ++i) v[i] = (TO)0.f;
+  }
+  *(vout_t*)(dst + q * 8) = v;
 }
 
 template <int MT, int XM, typename YT>
@@ -106,34 +220,33 @@ void launch_bf16(const GemmArgs& g, const GemmOut& o, int64_t grid, hipStream_t 
   gemm_bf16_kernel<MT, XM, YT><<<dim3((unsigned)grid), 256, 0, s>>>(g, o);
 }
 
-// Row-major activations only occur with at most GK_ROWS_MAX rows, i.e. MT = 1.
-template <int MT>
-void launch_mt(const GemmArgs& g, const GemmOut& o, int64_t grid, bool x_f32, bool y_f32, hipStream_t s) {
+template <int MT, typename YT>
+void launch_wide(const GemmArgs& g, const GemmOut& o, int64_t grid, hipStream_t s) {
+  gemm_wide_kernel<MT, GW_NT, YT><<<dim3((unsigned)grid), 256, 0, s>>>(g, o);
+}
+
+// One 16-row tile: narrow kernel, row-major activations up to GK_ROWS_MAX rows.
+void launch_narrow(const GemmArgs& g, const GemmOut& o, int64_t grid, bool x_f32, bool y_f32, hipStream_t s) {
   static_assert(GK_ROWS_MAX <= 16, "row-major activations are instantiated for one 16-row tile");
-  const bool packed = gemm_x_packed(g.M);
-  if constexpr (MT == 1) {
-    if (!packed) {
-      if (y_f32 && x_f32) launch_bf16<1, GK_X_ROWS_F32, float>(g, o, grid, s);
-      else if (y_f32) launch_bf16<1, GK_X_ROWS, float>(g, o, grid, s);
-      else if (x_f32) launch_bf16<1, GK_X_ROWS_F32, bf16>(g, o, grid, s);
-      else launch_bf16<1, GK_X_ROWS, bf16>(g, o, grid, s);
-      return;
-    }
-  }
-  if (y_f32)
-    launch_bf16<MT, GK_X_PACKED, float>(g, o, grid, s);
-  else
-    launch_bf16<MT, GK_X_PACKED, bf16>(g, o, grid, s);
+  if (gemm_x_packed(g.M)) {
+    if (y_f32) launch_bf16<1, GK_X_PACKED, float>(g, o, grid, s);
+    else launch_bf16<1, GK_X_PACKED, bf16>(g, o, grid, s);
+  } else if (y_f32 && x_f32) launch_bf16<1, GK_X_ROWS_F32, float>(g, o, grid, s);
+  else if (y_f32) launch_bf16<1, GK_X_ROWS, float>(g, o, grid, s);
+  else if (x_f32) launch_bf16<1, GK_X_ROWS_F32, bf16>(g, o, grid, s);
+  else launch_bf16<1, GK_X_ROWS, bf16>(g, o, grid, s);
 }
 
 }  // namespace
 
 int gemm_pick_splits(int32_t M, int32_t N, int32_t K) {
-  const int rows = 16 * gemm_mt(M);
-  const int64_t tiles = (int64_t)(N / 16) * ((M + rows - 1) / rows);
-  if (tiles >= GK_UNSPLIT_TILES) return 1;
+  const int mt = gemm_mt(M), nt = gemm_nt(M);
+  // work in units of 16-column tiles
+  const int64_t units = (int64_t)(N / (16 * nt)) * ((M + 16 * mt - 1) / (16 * mt)) * nt;
+  if (units >= GK_UNSPLIT_TILES) return 1;
+  const int64_t target = nt == 1 ? GK_TARGET_WG : 2 * GK_TARGET_WG;
   int S = 1;
-  while (S < GK_S_MAX && tiles * S < GK_TARGET_WG && K % (2 * S * 128) == 0) S *= 2;
+  while (S < GK_S_MAX && units * S < target && K % (2 * S * 128) == 0) S *= 2;
   return S;
 }
 
@@ -146,17 +259,21 @@ hipError_t launch_gemm(const GemmArgs& g, const GemmOut& o, bool f32_weights, bo
     gemm_f32_kernel<<<dim3((unsigned)((waves + 3) / 4)), 256, 0, s>>>(g, o);
     return hipGetLastError();
   }
-  const int mt = gemm_mt(g.M);
-  const int64_t tiles = (int64_t)(g.N / 16) * ((g.M + 16 * mt - 1) / (16 * mt));
-  if (g.S < 1 || g.S > GK_S_MAX || g.K % (g.S * 128) != 0 || (g.S > 1 && tiles > SPLITK_COUNTERS))
+  const int mt = gemm_mt(g.M), nt = gemm_nt(g.M);
+  const int cols = 16 * nt;
+  for (int i = 0; i < GK_SEG; ++i)
+    if (g.seg_end[i] % cols != 0) return hipErrorInvalidValue;
+  const int64_t tiles = (int64_t)(g.N / cols) * ((g.M + 16 * mt - 1) / (16 * mt));
+  if (g.N % cols != 0 || g.S < 1 || g.S > GK_S_MAX || g.K % (g.S * 128) != 0 ||
+      (g.S > 1 && tiles > SPLITK_COUNTERS) || (mt > 1 && !gemm_x_packed(g.M)))
     return hipErrorInvalidValue;
   const int64_t grid = (int64_t)g.S * tiles;
   if (mt == 1)
-    launch_mt<1>(g, o, grid, x_f32, y_f32, s);
+    launch_narrow(g, o, grid, x_f32, y_f32, s);
   else if (mt == 2)
-    launch_mt<2>(g, o, grid, x_f32, y_f32, s);
+    y_f32 ? launch_wide<2, float>(g, o, grid, s) : launch_wide<2, bf16>(g, o, grid, s);
   else
-    launch_mt<4>(g, o, grid, x_f32, y_f32, s);
+    y_f32 ? launch_wide<4, float>(g, o, grid, s) : launch_wide<4, bf16>(g, o, grid, s);
   return hipGetLastError();
 }
 

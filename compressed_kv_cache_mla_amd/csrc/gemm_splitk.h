@@ -292,6 +292,10 @@ struct GemmOut {
 
 // Rows per workgroup (16 * MT) of a product with M rows.
 inline int gemm_mt(int32_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
+// 16-column tiles per wave (wide kernel above 16 rows, gemm.hip).
+constexpr int GW_NT = 4;
+constexpr int GW_KB = 2;
+inline int gemm_nt(int32_t M) { return gemm_mt(M) == 1 ? 1 : GW_NT; }
 // Activations are read row-major (each row broadcast to the lanes of a
 // tile) up to this many rows and packed above it.
 constexpr int GK_ROWS_MAX = 8;
@@ -299,9 +303,11 @@ inline bool gemm_x_packed(int32_t M) { return M > GK_ROWS_MAX; }
 // Rows of a packed activation buffer.
 inline int64_t gemm_rows_padded(int32_t M) { return ((int64_t)M + 63) / 64 * 64; }
 
-// K chunks for an [M, N, K] product: 1 from GK_UNSPLIT_TILES tiles on, else
-// the least power of two that gives GK_TARGET_WG workgroups (at most
-// GK_S_MAX, and K % (S * 128) == 0).
+// K chunks for an [M, N, K] product, counted in 16-column tile units
+// (workgroups x 16-column tiles per wave): 1 from GK_UNSPLIT_TILES units on,
+// else the least power of two that reaches GK_TARGET_WG units (twice that for
+// the wide kernel), at most GK_S_MAX, with K % (S * 128) == 0.  A split
+// product must have at most SPLITK_COUNTERS (16*NT)-column tiles.
 int gemm_pick_splits(int32_t M, int32_t N, int32_t K);
 // Bytes of the chunk sums of a split product (0 when S == 1).
 size_t gemm_part_bytes(int32_t M, int32_t N, int32_t S);

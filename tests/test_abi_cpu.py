@@ -154,16 +154,21 @@ def _splits_rows(M):
     return 16 if M <= 16 else 32 if M <= 32 else 64
 
 
+def _splits_cols(M):
+    return 16 if M <= 16 else 64           # four 16-column tiles per wave above 16 rows
+
+
 def _splits(M, N, K):
-    """K chunks of a bf16 projection: none from 512 tiles on, else double
-    while the grid has fewer than 1024 workgroups, up to 16, while 128 * 2S
-    divides K (16, 32 or 64 rows per workgroup)."""
-    rows = _splits_rows(M)
-    tiles = (N // 16) * ((M + rows - 1) // rows)
-    if tiles >= 512:                       # two tiles per CU: not split
+    """K chunks of a bf16 projection, counted in 16-column tile units: none
+    from 512 units on, else double while below 1024 units (2048 for the
+    64-column tiles), up to 16, while 128 * 2S divides K."""
+    rows, cols = _splits_rows(M), _splits_cols(M)
+    units = (N // cols) * ((M + rows - 1) // rows) * (cols // 16)
+    if units >= 512:
         return 1
+    target = 1024 if cols == 16 else 2048
     S = 1
-    while S < 16 and tiles * S < 1024 and K % (2 * S * 128) == 0:
+    while S < 16 and units * S < target and K % (2 * S * 128) == 0:
         S *= 2
     return S
 
@@ -194,8 +199,8 @@ def test_split_products_fit_the_tile_counters():
     for M in (1, 7, 16, 17, 32, 33, 64, 100, 500):
         for N, K in ((9728, 5120), (16384, 1536), (5120, 16384), (576, 5120), (1280, 1024), (2048, 256)):
             S = _splits(M, N, K)
-            rows = _splits_rows(M)
-            assert S == 1 or (N // 16) * ((M + rows - 1) // rows) <= 1024
+            rows, cols = _splits_rows(M), _splits_cols(M)
+            assert S == 1 or (N // cols) * ((M + rows - 1) // rows) <= 1024
 
 
 def test_output_project_workspace_size():
