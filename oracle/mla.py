@@ -238,6 +238,22 @@ def attend_absorbed(q_C, q_R, pos_q, c_KV, k_R, W_UK, W_UV, base: float, scale: 
     return out, lse
 
 
+def attend_causal_chunk(q_C, q_R, pos, c_KV, k_R, W_UK, W_UV, base: float, scale: float, reconstruct: bool = False):
+    """A chunk of new tokens of one sequence, each attending causally: token t
+    (query q_C[t], q_R[t] at position pos[t]) attends to cached rows
+    0 .. pos[t] of the sequence, earlier tokens of the same chunk included
+    ([V2-arch] ch.2 §1: each token attends to the tokens before it and itself).
+    c_KV [n, d_c], k_R [n, d_hR] hold every row up to max(pos); returns
+    out [T, n_h, d_h], lse [T, n_h]."""
+    attend = attend_reconstruct if reconstruct else attend_absorbed
+    outs, lses = [], []
+    for t, p in enumerate(np.asarray(pos)):
+        o, l = attend(q_C[t], q_R[t], p, c_KV[:p + 1], k_R[:p + 1], W_UK, W_UV, base, scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
 def softmax_scale(d_h: int, d_hR: int) -> float:
     """1/sqrt(d_h + d_h^R): q and k are the concatenations of width d_h + d_h^R."""
     return 1.0 / np.sqrt(d_h + d_hR)

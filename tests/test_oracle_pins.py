@@ -16,7 +16,10 @@
   the product matrix W^UQ W^DQ formed first, against the full-rank path when
   W^DQ is the identity, and by the rank bound it implies;
 * the output projection W^O by head selectors, the sum of heads, and the
-  absorption of W^UV into W^O (ch.2 §2).
+  absorption of W^UV into W^O (ch.2 §2);
+* a causal chunk of new tokens against torch's scaled_dot_product_attention
+  with an explicit causal mask over materialised q, k, v, and by the
+  no-future-leak invariant.
 
 The last tests plant typical mistakes in copies of the oracle's functions and
 check that the pins above catch each of them.
@@ -461,3 +464,68 @@ def test_projection_pins_catch_planted_mistakes(kind):
         assert np.allclose(oracle.output_project(o, W_O), o[:, i] @ W_O[:, i * d_h:(i + 1) * d_h].T)
         caught |= not np.allclose(proj(o, W_O), o[:, i] @ W_O[:, i * d_h:(i + 1) * d_h].T)
     assert caught
+
+
+# ----------------------------------------------------------------------------- causal chunk (prefill)
+def _torch_chunk(P, L):
+    """The last T = n - L tokens as queries, each attending causally to all
+    earlier tokens and itself, through torch SDPA with an explicit boolean
+    mask over materialised per-head q, k, v (float64, CPU)."""
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))  # noqa: E731
+    n_h, d_h, d_hR, n = P["n_h"], P["d_h"], P["d_hR"], P["n"]
+    h = t(P["h"])
+    pos = torch.arange(n, dtype=torch.float64)
+
+    def rot(x, p):
+        d = x.shape[-1]
+        theta = BASE ** (-torch.arange(0, d, 2, dtype=torch.float64) / d)
+        z = torch.view_as_complex(x.reshape(*x.shape[:-1], d // 2, 2).contiguous())
+        z = z * torch.polar(torch.ones_like(theta), p[..., None] * theta)
+        return torch.view_as_real(z).reshape(x.shape)
+
+    c = h @ t(P["W_DKV"]).T
+    kC = torch.einsum("hdc,nc->hnd", t(P["W_UK"]).reshape(n_h, d_h, -1), c)
+    v = torch.einsum("hdc,nc->hnd", t(P["W_UV"]).reshape(n_h, d_h, -1), c)
+    kR = rot(h @ t(P["W_KR"]).T, pos)
+    k = torch.cat([kC, kR.unsqueeze(0).expand(n_h, n, d_hR)], dim=-1)
+    hq = h[L:]
+    qC = (hq @ t(P["W_UQ"]).T).reshape(-1, n_h, d_h).transpose(0, 1)
+    qR = rot((hq @ t(P["W_QR"]).T).reshape(-1, n_h, d_hR), pos[L:, None].expand(-1, n_h)).transpose(0, 1)
+    q = torch.cat([qC, qR], dim=-1)                                    # [n_h, T, E]
+    mask = torch.arange(n)[None, :] <= torch.arange(L, n)[:, None]     # [T, n]: key j visible to query i
+    out = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None], attn_mask=mask)[0]
+    return out.transpose(0, 1).numpy()                                 # [T, n_h, d_h]
+
+
+@pytest.mark.parametrize("reconstruct", [False, True])
+def test_causal_chunk_matches_torch_sdpa_with_a_causal_mask(reconstruct):
+    P = _problem(np.random.default_rng(30), n_h=3, d_h=8, d_c=12, d_hR=6, d_model=20, n=14)
+    L = 9
+    n = P["n"]
+    c, kR = oracle.down_project(P["h"], P["W_DKV"], P["W_KR"], np.arange(n), BASE)
+    qs = [oracle.query_project(P["h"][i], P["W_UQ"], P["W_QR"], P["n_h"]) for i in range(L, n)]
+    q_C, q_R = np.stack([a for a, _ in qs]), np.stack([b for _, b in qs])
+    out, lse = oracle.attend_causal_chunk(q_C, q_R, np.arange(L, n), c, kR, P["W_UK"], P["W_UV"], BASE,
+                                          oracle.softmax_scale(P["d_h"], P["d_hR"]), reconstruct=reconstruct)
+    assert out.shape == (n - L, P["n_h"], P["d_h"]) and lse.shape == (n - L, P["n_h"])
+    assert _rel(out, _torch_chunk(P, L)) < 1e-12
+
+
+def test_causal_chunk_has_no_future_leak():
+    """Rows after a token's position never change its output; its output is
+    the single-token decode over its own prefix."""
+    rng = np.random.default_rng(31)
+    n_h, d_h, d_c, d_hR, n, T = 4, 16, 32, 8, 20, 6
+    q_C, q_R = rng.standard_normal((T, n_h, d_h)), rng.standard_normal((T, n_h, d_hR))
+    c, kR = rng.standard_normal((n, d_c)), rng.standard_normal((n, d_hR))
+    W_UK, W_UV = rng.standard_normal((n_h * d_h, d_c)), rng.standard_normal((n_h * d_h, d_c))
+    pos = np.arange(n - T, n)
+    a, la = oracle.attend_causal_chunk(q_C, q_R, pos, c, kR, W_UK, W_UV, BASE, 0.2)
+    c2, kR2 = c.copy(), kR.copy()
+    c2[n - 2:] += 5.0
+    kR2[n - 2:] -= 3.0
+    b, lb = oracle.attend_causal_chunk(q_C, q_R, pos, c2, kR2, W_UK, W_UV, BASE, 0.2)
+    assert np.array_equal(a[:T - 2], b[:T - 2]) and np.array_equal(la[:T - 2], lb[:T - 2])
+    assert _rel(b[T - 1], a[T - 1]) > 1e-3                  # the last tokens do see the changed rows
+    o, l = oracle.attend_absorbed(q_C[2], q_R[2], pos[2], c[:pos[2] + 1], kR[:pos[2] + 1], W_UK, W_UV, BASE, 0.2)
+    assert np.array_equal(o, a[2]) and np.array_equal(l, la[2])
