@@ -29,6 +29,7 @@ EXPORTED = ("mla_cache_append", "mla_cache_append_ws", "mla_cache_append_workspa
             "mla_decode_step_workspace_size", "mla_decode_step",
             "mla_pack_weight", "mla_query_project_workspace_size", "mla_query_project",
             "mla_output_project_workspace_size", "mla_output_project",
+            "mla_prefill_workspace_size", "mla_prefill",
             "mla_read_error_flags", "mla_last_error", "mla_device_cu_count")
 
 
@@ -115,6 +116,11 @@ def lib() -> ctypes.CDLL:
         L.mla_output_project_workspace_size.restype = sz
         L.mla_output_project.argtypes = [pdims, i32, vp, vp, vp, vp, sz, vp]
         L.mla_output_project.restype = ctypes.c_int
+        L.mla_prefill_workspace_size.argtypes = [pdims, i32, i32, i32]
+        L.mla_prefill_workspace_size.restype = sz
+        L.mla_prefill.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32, i32, vp,
+                                  vp, vp, sz, i32, vp]
+        L.mla_prefill.restype = ctypes.c_int
         L.mla_read_error_flags.argtypes = [vp, ctypes.POINTER(i32), vp]
         L.mla_read_error_flags.restype = ctypes.c_int
         L.mla_last_error.argtypes = []
@@ -320,6 +326,30 @@ def output_project(dims: Dims, o, W_O, u, workspace, stream=None):
     d = dims.c()
     _check(lib().mla_output_project(ctypes.byref(d), B, _ptr(o), _ptr(W_O), _ptr(u), _ptr(workspace),
                                     workspace.numel(), _stream(stream)))
+
+
+def prefill_workspace_size(dims: Dims, T: int, max_pages: int, n_splits: int = 0) -> int:
+    d = dims.c()
+    return int(lib().mla_prefill_workspace_size(ctypes.byref(d), T, max_pages, n_splits))
+
+
+def prefill(dims: Dims, h, W_DKV, W_KR, q_C, q_R, seq_id, pos, W_UK, W_UV, c_KV, k_R, row_stride: int,
+            num_pages: int, page_table, out, lse=None, workspace=None, n_splits: int = 0, stream=None):
+    """mla_prefill: append T new tokens (token t: sequence seq_id[t], position
+    pos[t]) and let each attend causally over its sequence; writes out
+    [T, n_h, d_h] (fp32) and optionally lse [T, n_h].  Returns the workspace
+    (which holds the error flags)."""
+    T = h.shape[0]
+    num_seqs, max_pages = page_table.shape
+    if workspace is None:
+        workspace = torch.empty(prefill_workspace_size(dims, T, max_pages, n_splits), dtype=torch.uint8,
+                                device=h.device)
+    d = dims.c()
+    _check(lib().mla_prefill(ctypes.byref(d), T, _ptr(h), _ptr(W_DKV), _ptr(W_KR), _ptr(q_C), _ptr(q_R),
+                             _ptr(seq_id), _ptr(pos), _ptr(W_UK), _ptr(W_UV), _ptr(c_KV), _ptr(k_R), row_stride,
+                             num_pages, _ptr(page_table), num_seqs, max_pages, _ptr(out), _ptr(lse), _ptr(workspace),
+                             workspace.numel(), n_splits, _stream(stream)))
+    return workspace
 
 
 def read_error_flags(workspace_or_flag, stream=None) -> int:

@@ -152,7 +152,7 @@ static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, 
                               int64_t row_stride, int32_t num_pages, const int32_t* page_table, int32_t max_pages,
                               const int32_t* seq_lens, float* out, float* lse, void* workspace, size_t ws_bytes,
                               int32_t n_splits, const mla_decode_opts* opts, const StepAppendIn* step,
-                              void* stream) {
+                              void* stream, bool merge_append_flags = false) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
@@ -228,7 +228,8 @@ static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, 
   }
   if (e == hipSuccess && opts && opts->ev_stop) e = hipEventRecord((hipEvent_t)opts->ev_stop, s);
   if (e == hipSuccess)
-    e = mla::launch_combine(*dims, B, prefix, n_splits, part_ml, part_o, W_UV, out, lse, step ? flags : nullptr, s);
+    e = mla::launch_combine(*dims, B, prefix, n_splits, part_ml, part_o, W_UV, out, lse,
+                            step || merge_append_flags ? flags : nullptr, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -463,6 +464,66 @@ mla_status mla_pack_weight(const mla_dims* dims, int32_t rows, int32_t K, const 
   hipError_t e = mla::launch_pack(W, K, rows, rows, K, f32, false, W_packed, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "pack launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+// Chunked prefill workspace: the decode's for T queries, then the queries'
+// page-table rows [T, max_pages] and lengths [T].
+struct PrefillWs {
+  size_t q_pt, q_len, total;
+};
+
+static PrefillWs prefill_ws_layout(const mla_dims& d, int32_t T, int32_t max_pages, int32_t n_splits) {
+  PrefillWs w;
+  w.q_pt = mla::decode_ws_layout(T, d.n_h, n_splits, elt_size(&d)).total;
+  w.q_len = w.q_pt + mla::align256((size_t)T * max_pages * 4);
+  w.total = w.q_len + mla::align256((size_t)T * 4);
+  return w;
+}
+
+size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t T, int32_t max_pages, int32_t n_splits) {
+  if (check_dims(dims) != MLA_OK || T < 1 || T > (1 << 20) || max_pages < 1) return 0;
+  if (n_splits <= 0) n_splits = default_splits();
+  return prefill_ws_layout(*dims, T, max_pages, n_splits).total;
+}
+
+mla_status mla_prefill(const mla_dims* dims, int32_t T, const void* h, const void* W_DKV, const void* W_KR,
+                       const void* q_C, const void* q_R, const int32_t* seq_id, const int32_t* pos, const void* W_UK,
+                       const void* W_UV, void* c_KV, void* k_R, int64_t row_stride, int32_t num_pages,
+                       const int32_t* page_table, int32_t num_seqs, int32_t max_pages, float* out, float* lse,
+                       void* workspace, size_t ws_bytes, int32_t n_splits, void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (T < 1 || T > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "T=%d out of range", T);
+  // every check of the decode that follows is made here too, before anything is launched
+  if (!h || !W_DKV || !W_KR || !seq_id || !pos || !page_table || !workspace || !q_C || !q_R || !W_UK || !W_UV ||
+      !out)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(h) || !aligned16(W_DKV) || !aligned16(W_KR) || !aligned16(q_C) || !aligned16(q_R) ||
+      !aligned16(W_UK) || !aligned16(W_UV) || !aligned16(out))
+    return fail(MLA_ERR_INVALID_ARG, "h / weights / q_C / q_R / out not 16-byte aligned");
+  if (num_seqs < 1 || max_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_seqs and max_pages must be >= 1");
+  if (((uintptr_t)workspace & 255) != 0) return fail(MLA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if (n_splits <= 0) n_splits = default_splits();
+  if (n_splits > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d too large", n_splits);
+  st = check_pool(dims, c_KV, k_R, row_stride, num_pages);
+  if (st != MLA_OK) return st;
+  if ((int64_t)T * max_pages * dims->page_size >= ((int64_t)1 << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "T*max_pages*page_size >= 2^31 tokens");
+  const PrefillWs L = prefill_ws_layout(*dims, T, max_pages, n_splits);
+  if (ws_bytes < L.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  char* ws = (char*)workspace;
+  int32_t* q_pt = (int32_t*)(ws + L.q_pt);
+  int32_t* q_len = (int32_t*)(ws + L.q_len);
+  hipStream_t s = (hipStream_t)stream;
+  // append errors go to flag word 1 (cleared first), which the combine folds into word 0
+  hipError_t e = mla::launch_prefill_queries(T, seq_id, pos, page_table, num_seqs, max_pages, dims->page_size, q_pt,
+                                             q_len, (int32_t*)ws + 1, s);
+  if (e == hipSuccess)
+    e = mla::launch_append(*dims, T, h, W_DKV, W_KR, seq_id, pos, page_table, num_seqs, max_pages, c_KV, k_R,
+                           row_stride, num_pages, (int32_t*)ws + 1, nullptr, 0, s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return decode_impl(dims, T, q_C, q_R, pos, W_UK, W_UV, c_KV, k_R, row_stride, num_pages, q_pt, max_pages, q_len,
+                     out, lse, workspace, L.q_pt, n_splits, nullptr, nullptr, stream, true);
 }
 
 mla_status mla_read_error_flags(void* workspace_or_flag, int32_t* flags, void* stream) {

@@ -228,6 +228,11 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
                          int32_t num_seqs, int32_t max_pages, void* c_KV, void* k_R, int64_t row_stride,
                          int32_t num_pages, int32_t* err_flag, void* ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_plan(const PlanArgs& pa, hipStream_t s);
+// Chunked prefill: per-query page-table rows and lengths, and a cleared
+// append flag word (prefill.hip).
+hipError_t launch_prefill_queries(int32_t T, const int32_t* seq_id, const int32_t* pos, const int32_t* page_table,
+                                  int32_t num_seqs, int32_t max_pages, int32_t page_size, int32_t* q_pt,
+                                  int32_t* q_len, int32_t* append_flag, hipStream_t s);
 // Query absorption; for bf16 the decode plan runs in the same launch (then
 // launch_plan is not called).
 hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,

@@ -297,6 +297,40 @@ mla_status mla_output_project(const mla_dims* dims, int32_t B, const float* o, c
                               void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * mla_prefill_workspace_size -- bytes of device workspace mla_prefill needs
+ * for a chunk of T tokens, page-table rows of max_pages entries and n_splits
+ * (0 = default); 0 for invalid arguments.
+ *
+ * mla_prefill -- a chunk of T new tokens, any mix of sequences (chunked
+ * prefill, or several decode tokens per sequence).  Token t belongs to
+ * sequence seq_id[t] at position pos[t]; all T rows are first appended to the
+ * latent cache as mla_cache_append would (liang.world ch.2 §2 eq. for c_t^KV;
+ * tuntang.top MLA section, k_t formula); then token t attends causally to rows
+ * 0 .. pos[t] of its sequence, earlier tokens of the same chunk included
+ * (liang.world ch.2 §1: a token attends to the tokens before it and itself),
+ * exactly as mla_decode with one query per new token.
+ *   h            [T, d_model]      dtype   device
+ *   W_DKV, W_KR  as for mla_cache_append
+ *   q_C, q_R     [T, n_h, d_h], [T, n_h, d_hR] dtype device (q_R not rotated)
+ *   seq_id, pos  [T] int32         device  sequence and position of each token
+ *   W_UK, W_UV   as for mla_decode
+ *   c_KV, k_R, row_stride, num_pages, page_table [num_seqs, max_pages]: the pool
+ *   out          [T, n_h, d_h] fp32, lse [T, n_h] fp32 or NULL
+ *   workspace    ws_bytes >= mla_prefill_workspace_size(dims, T, max_pages, n_splits),
+ *                256-byte aligned device memory; holds the error flags.
+ * A token with a bad sequence id or position is not appended, its output is
+ * empty (out = 0, lse = -inf) and MLA_FLAG_BAD_SEQ_ID / BAD_POSITION /
+ * BAD_SEQ_LEN are raised (mla_read_error_flags).  Deterministic for fixed
+ * inputs and n_splits.
+ */
+size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t T, int32_t max_pages, int32_t n_splits);
+mla_status mla_prefill(const mla_dims* dims, int32_t T, const void* h, const void* W_DKV, const void* W_KR,
+                       const void* q_C, const void* q_R, const int32_t* seq_id, const int32_t* pos, const void* W_UK,
+                       const void* W_UV, void* c_KV, void* k_R, int64_t row_stride, int32_t num_pages,
+                       const int32_t* page_table, int32_t num_seqs, int32_t max_pages, float* out, float* lse,
+                       void* workspace, size_t ws_bytes, int32_t n_splits, void* stream);
+
+/*
  * mla_read_error_flags -- wait for `stream`, then copy the device error flags
  * of a decode workspace (or an append err_flag word) to *flags and clear them.
  */

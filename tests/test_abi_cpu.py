@@ -319,3 +319,34 @@ def test_append_workspace_size():
     assert L.mla_cache_append_workspace_size(ctypes.byref(d), 65) == 0           # decode-step sizes only
     assert L.mla_cache_append_workspace_size(ctypes.byref(_dims(dtype=mla.MLA_FP32)), 32) == 0
     assert L.mla_cache_append_workspace_size(ctypes.byref(_dims(d_model=1536)), 32) == 0
+
+
+def test_prefill_rejects_bad_arguments_before_launching():
+    L = mla.lib()
+    p = ctypes.c_void_p(16 * 4096)
+    ws = ctypes.c_void_p(1 << 20)
+    d = _dims()
+
+    def call(dims=d, T=4, ptr=p, stride=576, ws_bytes=1 << 30, work=ws, num_seqs=2, max_pages=4):
+        return L.mla_prefill(ctypes.byref(dims) if dims is not None else None, T, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                             ptr, ptr, ptr, ptr, stride, 10, ptr, num_seqs, max_pages, ptr, None, work, ws_bytes, 8,
+                             None)
+    assert call(None) == mla.MLA_ERR_INVALID_ARG
+    assert call(_dims(d_c=256)) == mla.MLA_ERR_UNSUPPORTED
+    assert call(T=0) == mla.MLA_ERR_INVALID_ARG
+    assert call(ptr=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(ptr=ctypes.c_void_p(16 * 4096 + 2)) == mla.MLA_ERR_INVALID_ARG
+    assert call(stride=500) == mla.MLA_ERR_INVALID_ARG
+    assert call(num_seqs=0) == mla.MLA_ERR_INVALID_ARG
+    assert call(work=ctypes.c_void_p((1 << 20) + 64)) == mla.MLA_ERR_INVALID_ARG
+    assert call(ws_bytes=1000) == mla.MLA_ERR_WORKSPACE
+
+
+def test_prefill_workspace_is_the_decode_layout_plus_query_tables():
+    L = mla.lib()
+    d = _dims()
+    for T, max_pages in ((1, 1), (17, 5), (512, 70)):
+        dec = L.mla_decode_workspace_size(ctypes.byref(d), T, 64)
+        pre = L.mla_prefill_workspace_size(ctypes.byref(d), T, max_pages, 64)
+        assert pre == dec + _a256(T * max_pages * 4) + _a256(T * 4)
+    assert L.mla_prefill_workspace_size(ctypes.byref(d), 0, 4, 64) == 0
