@@ -13,8 +13,9 @@ Prints one JSON line.  `value` is decode tokens/s (B sequences per step);
 `roofline` is computed for the split-KV attention kernel from its algorithmic
 bytes and its HIP-event duration measured in the timed region; `projections`
 times the query path (W^DQ, W^UQ, W^QR) and the output projection W^O, which
-sit outside the step, at the same batch sizes; `cpu_baseline` times the fp64
-CPU oracle on a bounded sample of the same workload.
+sit outside the step, at the same batch sizes; `prefill` times chunked
+prefill (new tokens attending causally over their sequences); `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode tokens/s + latent-cache GB/s (% of HBM/MFMA roofline), 1 GPU"
+PREFILL_CONFIGS = [(1, 4096, 512), (8, 2048, 64)]     # (sequences, prior tokens, new tokens per sequence)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 COUNTERS = os.path.join(ROOT, "profiles", "decode_attention_counters.json")
@@ -130,6 +132,60 @@ def measure_projections(torch, mla, B: int, n_h: int = 128, d_model: int = 5120,
     return out
 
 
+def measure_prefill(torch, mla, B: int, L: int, T: int, n_h: int = 128, d_model: int = 5120, reps: int = 10):
+    """Chunked prefill (mla_prefill) of T new tokens per sequence after an
+    L-token prior, B sequences, DeepSeek-V2 sizes, 64-token pages in order.
+    Each call appends the chunk again at the same positions (same values) and
+    runs the causal attention; timed with fence-free HIP events per call.
+    Algorithmic flops: the attention's n_h * (2*576 + 2*512) per (query,
+    visible row) pair, plus the append (2 * d_model * 576 per token),
+    absorption and W^UV (2 * 2 * n_h * 128 * 512 per token)."""
+    import seeded_inputs as si
+    bf = torch.bfloat16
+    ps = 64
+    dims = mla.Dims(n_h=n_h, d_model=d_model, page_size=ps)
+    n = L + T
+    max_pages = (n + ps - 1) // ps
+    num_pages = B * max_pages
+    pt = torch.arange(num_pages, dtype=torch.int32, device="cuda").reshape(B, max_pages)
+    pool = torch.empty((num_pages * ps, 576), dtype=bf, device="cuda")
+    key = lambda name: si.stream_key(4321, name)  # noqa: E731
+    W_DKV = si.normal(key("W_DKV"), (512, d_model), d_model ** -0.5, bf, "cuda")
+    W_KR = si.normal(key("W_KR"), (64, d_model), d_model ** -0.5, bf, "cuda")
+    W_UK = si.normal(key("W_UK"), (n_h * 128, 512), 512 ** -0.5, bf, "cuda")
+    W_UV = si.normal(key("W_UV"), (n_h * 128, 512), 512 ** -0.5, bf, "cuda")
+    seq = torch.arange(B, dtype=torch.int32, device="cuda").repeat_interleave(n)
+    pos = torch.arange(n, dtype=torch.int32, device="cuda").repeat(B)
+    h = si.normal(key("h"), (B * n, d_model), 1.0, bf, "cuda")
+    mla.cache_append(dims, h, W_DKV, W_KR, pos, pt, pool[:, :512], pool[:, 512:], 576, num_pages, seq_id=seq)
+    last = (torch.arange(B * n, device="cuda") % n) >= L
+    c_h, c_seq, c_pos = h[last].contiguous(), seq[last].contiguous(), pos[last].contiguous()
+    q_C = si.normal(key("q_C"), (B * T, n_h, 128), 1.0, bf, "cuda")
+    q_R = si.normal(key("q_R"), (B * T, n_h, 64), 1.0, bf, "cuda")
+    out = torch.empty((B * T, n_h, 128), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(mla.prefill_workspace_size(dims, B * T, max_pages), dtype=torch.uint8, device="cuda")
+
+    def call():
+        mla.prefill(dims, c_h, W_DKV, W_KR, q_C, q_R, c_seq, c_pos, W_UK, W_UV, pool[:, :512], pool[:, 512:], 576,
+                    num_pages, pt, out, workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    evs = [(mla.HipEvent(), mla.HipEvent()) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.median([1e3 * a.elapsed_ms(b) for a, b in evs]))
+    pairs = B * (T * L + T * (T + 1) // 2)
+    flops = pairs * n_h * (2 * 576 + 2 * 512) + B * T * (2 * d_model * 576 + 4 * n_h * 128 * 512)
+    tf = flops / (us * 1e-6) / 1e12
+    return {"B": B, "prior_tokens": L, "chunk_tokens": T, "us_p50": round(us, 1),
+            "tokens_per_s": round(B * T / (us * 1e-6), 1), "TFLOPs": round(tf, 1),
+            "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
 def cpu_baseline(wl, seconds: float):
     """The fp64 oracle (absorbed form) doing the same per-sequence work as a
     step -- append the newest token, then decode -- on a bounded sample."""
@@ -180,6 +236,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-projections", action="store_true", help="skip the query / output projection timings")
+    ap.add_argument("--prefill-only", action="store_true", help="only time the chunked prefill configurations")
     ap.add_argument("--projections-only", default="",
                     help="comma-separated batch sizes: only time the query / output projections at them")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -203,6 +260,9 @@ def main():
         return
     import workloads as W
     import compressed_kv_cache_mla_amd as mla
+    if args.prefill_only:
+        print(json.dumps({"prefill": [measure_prefill(torch, mla, *cfg) for cfg in PREFILL_CONFIGS]}), flush=True)
+        return
     if args.projections_only:
         print(json.dumps({f"B{b}": measure_projections(torch, mla, int(b))
                           for b in args.projections_only.split(",")}), flush=True)
@@ -307,6 +367,9 @@ def main():
         # rows past the attention step: the query path and W^O, at the batches reported above
         res["projections"] = {f"B{b}": measure_projections(torch, mla, b) for b in
                               sorted({B, res.get("target_shape", {}).get("B", B)})}
+    if not args.no_projections:
+        # the chunked-prefill row: new tokens attending causally over their sequences
+        res["prefill"] = [measure_prefill(torch, mla, *cfg) for cfg in PREFILL_CONFIGS]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
     print(json.dumps(res), flush=True)
