@@ -30,6 +30,7 @@ EXPORTED = ("mla_cache_append", "mla_cache_append_ws", "mla_cache_append_workspa
             "mla_pack_weight", "mla_query_project_workspace_size", "mla_query_project",
             "mla_output_project_workspace_size", "mla_output_project",
             "mla_prefill_workspace_size", "mla_prefill",
+            "mla_decode_layer_workspace_size", "mla_decode_layer",
             "mla_read_error_flags", "mla_last_error", "mla_device_cu_count")
 
 
@@ -121,6 +122,11 @@ def lib() -> ctypes.CDLL:
         L.mla_prefill.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32, i32, vp,
                                   vp, vp, sz, i32, vp]
         L.mla_prefill.restype = ctypes.c_int
+        L.mla_decode_layer_workspace_size.argtypes = [pdims, i32, i32, i32]
+        L.mla_decode_layer_workspace_size.restype = sz
+        L.mla_decode_layer.argtypes = [pdims, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp,
+                                       i32, vp, vp, vp, vp, sz, i32, ctypes.POINTER(mla_decode_opts), vp]
+        L.mla_decode_layer.restype = ctypes.c_int
         L.mla_read_error_flags.argtypes = [vp, ctypes.POINTER(i32), vp]
         L.mla_read_error_flags.restype = ctypes.c_int
         L.mla_last_error.argtypes = []
@@ -350,6 +356,35 @@ def prefill(dims: Dims, h, W_DKV, W_KR, q_C, q_R, seq_id, pos, W_UK, W_UV, c_KV,
                              num_pages, _ptr(page_table), num_seqs, max_pages, _ptr(out), _ptr(lse), _ptr(workspace),
                              workspace.numel(), n_splits, _stream(stream)))
     return workspace
+
+
+def decode_layer_workspace_size(dims: Dims, B: int, d_cq: int, n_splits: int = 0) -> int:
+    d = dims.c()
+    return int(lib().mla_decode_layer_workspace_size(ctypes.byref(d), B, d_cq, n_splits))
+
+
+def decode_layer_workspace(dims: Dims, B: int, d_cq: int, n_splits: int = 0, device="cuda"):
+    """A zero-filled workspace for decode_layer (the library needs it zeroed once)."""
+    return torch.zeros(decode_layer_workspace_size(dims, B, d_cq, n_splits), dtype=torch.uint8, device=device)
+
+
+def decode_layer(dims: Dims, h, W_DKV, W_KR, W_DQ, W_UQ, W_QR, W_UK, W_UV, W_O, pos_q, c_KV, k_R, row_stride: int,
+                 num_pages: int, page_table, seq_lens, u, lse, workspace, n_splits: int = 0, stream=None,
+                 ev_start=None, ev_stop=None, impl: int = 0):
+    """mla_decode_layer: query projection, decode step (append + attention +
+    combine + W^UV) and output projection for one new token per sequence;
+    writes u [B, d_model] (fp32).  W_DQ, W_UQ, W_QR, W_O packed (pack_weight);
+    W_DQ None means no query down-projection."""
+    B = h.shape[0]
+    d_cq = 0 if W_DQ is None else W_DQ.shape[0]
+    max_pages = page_table.shape[1]
+    d = dims.c()
+    o = mla_decode_opts(_event_handle(ev_start), _event_handle(ev_stop), impl)
+    _check(lib().mla_decode_layer(ctypes.byref(d), B, d_cq, _ptr(h), _ptr(W_DKV), _ptr(W_KR), _ptr(W_DQ), _ptr(W_UQ),
+                                  _ptr(W_QR), _ptr(W_UK), _ptr(W_UV), _ptr(W_O), _ptr(pos_q), _ptr(c_KV), _ptr(k_R),
+                                  row_stride, num_pages, _ptr(page_table), max_pages, _ptr(seq_lens), _ptr(u),
+                                  _ptr(lse), _ptr(workspace), workspace.numel(), n_splits, ctypes.byref(o),
+                                  _stream(stream)))
 
 
 def read_error_flags(workspace_or_flag, stream=None) -> int:

@@ -526,6 +526,67 @@ mla_status mla_prefill(const mla_dims* dims, int32_t T, const void* h, const voi
                      out, lse, workspace, L.q_pt, n_splits, nullptr, nullptr, stream, true);
 }
 
+// Whole-layer decode workspace: the decode step's (first, so that its error
+// flags sit at offset 0) | query projection | q_C | q_R | o | output projection.
+struct LayerWs {
+  size_t q, qc, qr, o, out, total;
+};
+
+static LayerWs layer_ws_layout(const mla_dims& d, int32_t B, int32_t d_cq, int32_t n_splits) {
+  const size_t elt = elt_size(&d);
+  LayerWs w;
+  size_t off = mla::decode_ws_layout(B, d.n_h, n_splits, (int)elt, true).total;
+  w.q = off;   off += mla::align256(query_plan(d, B, d_cq).total);
+  w.qc = off;  off += mla::align256((size_t)B * d.n_h * mla::D_H * elt);
+  w.qr = off;  off += mla::align256((size_t)B * d.n_h * mla::D_R * elt);
+  w.o = off;   off += mla::align256((size_t)B * d.n_h * mla::D_H * 4);
+  w.out = off; off += mla::align256(output_plan(d, B).total);
+  w.total = off;
+  return w;
+}
+
+size_t mla_decode_layer_workspace_size(const mla_dims* dims, int32_t B, int32_t d_cq, int32_t n_splits) {
+  if (check_query_dims(dims, B, d_cq) != MLA_OK) return 0;
+  if (n_splits <= 0) n_splits = default_splits();
+  return layer_ws_layout(*dims, B, d_cq, n_splits).total;
+}
+
+mla_status mla_decode_layer(const mla_dims* dims, int32_t B, int32_t d_cq, const void* h, const void* W_DKV,
+                            const void* W_KR, const void* W_DQ, const void* W_UQ, const void* W_QR, const void* W_UK,
+                            const void* W_UV, const void* W_O, const int32_t* pos_q, void* c_KV, void* k_R,
+                            int64_t row_stride, int32_t num_pages, const int32_t* page_table, int32_t max_pages,
+                            const int32_t* seq_lens, float* u, float* lse, void* workspace, size_t ws_bytes,
+                            int32_t n_splits, const mla_decode_opts* opts, void* stream) {
+  // every check of the three parts is made here, before anything is launched
+  mla_status st = check_query_dims(dims, B, d_cq);
+  if (st != MLA_OK) return st;
+  if (!h || !W_DKV || !W_KR || !W_UQ || !W_QR || !W_UK || !W_UV || !W_O || !pos_q || !page_table || !seq_lens ||
+      !u || !workspace || (d_cq > 0) != (W_DQ != nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "null pointer argument (W_DQ must be given exactly when d_cq > 0)");
+  if (!aligned16(h) || !aligned16(W_DKV) || !aligned16(W_KR) || (W_DQ && !aligned16(W_DQ)) || !aligned16(W_UQ) ||
+      !aligned16(W_QR) || !aligned16(W_UK) || !aligned16(W_UV) || !aligned16(W_O) || !aligned16(u))
+    return fail(MLA_ERR_INVALID_ARG, "h / weights / u not 16-byte aligned");
+  if (((uintptr_t)workspace & 255) != 0) return fail(MLA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  st = check_pool(dims, c_KV, k_R, row_stride, num_pages);
+  if (st != MLA_OK) return st;
+  if (max_pages < 1 || (int64_t)B * max_pages * dims->page_size >= ((int64_t)1 << 31))
+    return fail(MLA_ERR_INVALID_ARG, "max_pages=%d out of range", max_pages);
+  if (opts && opts->impl != 0 && opts->impl != 1) return fail(MLA_ERR_INVALID_ARG, "opts->impl=%d", opts->impl);
+  if (n_splits <= 0) n_splits = default_splits();
+  if (n_splits > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d too large", n_splits);
+  const LayerWs L = layer_ws_layout(*dims, B, d_cq, n_splits);
+  if (ws_bytes < L.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  char* ws = (char*)workspace;
+  st = mla_query_project(dims, B, d_cq, h, W_DQ, W_UQ, W_QR, ws + L.qc, ws + L.qr, ws + L.q, L.qc - L.q, stream);
+  if (st == MLA_OK)
+    st = mla_decode_step(dims, B, h, W_DKV, W_KR, ws + L.qc, ws + L.qr, pos_q, W_UK, W_UV, c_KV, k_R, row_stride,
+                         num_pages, page_table, max_pages, seq_lens, (float*)(ws + L.o), lse, workspace, L.q, n_splits,
+                         opts, stream);
+  if (st == MLA_OK)
+    st = mla_output_project(dims, B, (const float*)(ws + L.o), W_O, u, ws + L.out, L.total - L.out, stream);
+  return st;
+}
+
 mla_status mla_read_error_flags(void* workspace_or_flag, int32_t* flags, void* stream) {
   if (!workspace_or_flag || !flags) return fail(MLA_ERR_INVALID_ARG, "null pointer");
   hipStream_t s = (hipStream_t)stream;

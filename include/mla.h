@@ -331,6 +331,37 @@ mla_status mla_prefill(const mla_dims* dims, int32_t T, const void* h, const voi
                        void* workspace, size_t ws_bytes, int32_t n_splits, void* stream);
 
 /*
+ * mla_decode_layer_workspace_size -- bytes of device workspace
+ * mla_decode_layer needs for batch B, query rank d_cq and n_splits (0 =
+ * default); 0 for invalid arguments.
+ *
+ * mla_decode_layer -- one MLA attention layer for one decode token per
+ * sequence, from the token states h to the layer output u: the query path
+ * (mla_query_project), the decode step (mla_decode_step: append of the token's
+ * latent row, absorption, attention over the cache, combine + W^UV) and the
+ * output projection (mla_output_project), on the same stream and with the
+ * same results as those three calls.
+ *   h            [B, d_model]     dtype   device  state of each sequence's new token
+ *   W_DKV, W_KR  row-major, as for mla_cache_append
+ *   W_DQ, W_UQ, W_QR   packed, as for mla_query_project (W_DQ NULL iff d_cq == 0)
+ *   W_UK, W_UV   row-major, as for mla_decode
+ *   W_O          packed, as for mla_output_project
+ *   pos_q, c_KV, k_R, row_stride, num_pages, page_table, max_pages, seq_lens, opts:
+ *                as for mla_decode_step (the new token is written at pos_q[b])
+ *   u            [B, d_model] fp32 device, written;  lse [B, n_h] fp32 or NULL
+ *   workspace    ws_bytes >= mla_decode_layer_workspace_size(dims, B, d_cq, n_splits),
+ *                256-byte aligned, ZERO-FILLED ONCE (split-K counters); its
+ *                first word holds the error flags (mla_read_error_flags).
+ */
+size_t mla_decode_layer_workspace_size(const mla_dims* dims, int32_t B, int32_t d_cq, int32_t n_splits);
+mla_status mla_decode_layer(const mla_dims* dims, int32_t B, int32_t d_cq, const void* h, const void* W_DKV,
+                            const void* W_KR, const void* W_DQ, const void* W_UQ, const void* W_QR, const void* W_UK,
+                            const void* W_UV, const void* W_O, const int32_t* pos_q, void* c_KV, void* k_R,
+                            int64_t row_stride, int32_t num_pages, const int32_t* page_table, int32_t max_pages,
+                            const int32_t* seq_lens, float* u, float* lse, void* workspace, size_t ws_bytes,
+                            int32_t n_splits, const mla_decode_opts* opts, void* stream);
+
+/*
  * mla_read_error_flags -- wait for `stream`, then copy the device error flags
  * of a decode workspace (or an append err_flag word) to *flags and clear them.
  */

@@ -350,3 +350,36 @@ def test_prefill_workspace_is_the_decode_layout_plus_query_tables():
         pre = L.mla_prefill_workspace_size(ctypes.byref(d), T, max_pages, 64)
         assert pre == dec + _a256(T * max_pages * 4) + _a256(T * 4)
     assert L.mla_prefill_workspace_size(ctypes.byref(d), 0, 4, 64) == 0
+
+
+def test_decode_layer_workspace_is_its_parts():
+    L = mla.lib()
+    d = _dims()
+    for B, d_cq in ((1, 1536), (32, 1536), (64, 0)):
+        step = L.mla_decode_step_workspace_size(ctypes.byref(d), B, 256)
+        q = L.mla_query_project_workspace_size(ctypes.byref(d), B, d_cq)
+        o = L.mla_output_project_workspace_size(ctypes.byref(d), B)
+        want = step + _a256(q) + _a256(B * 128 * 128 * 2) + _a256(B * 128 * 64 * 2) + _a256(B * 128 * 128 * 4) + \
+            _a256(o)
+        assert L.mla_decode_layer_workspace_size(ctypes.byref(d), B, d_cq, 256) == want
+    assert L.mla_decode_layer_workspace_size(ctypes.byref(d), 4, 100, 256) == 0
+
+
+def test_decode_layer_rejects_bad_arguments_before_launching():
+    L = mla.lib()
+    p = ctypes.c_void_p(16 * 4096)
+    ws = ctypes.c_void_p(1 << 20)
+
+    def call(dims=None, B=4, d_cq=512, wdq=p, ptr=p, ws_bytes=1 << 30, work=ws, stride=576):
+        dd = _dims() if dims is None else dims
+        return L.mla_decode_layer(ctypes.byref(dd), B, d_cq, ptr, ptr, ptr, wdq, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                                  stride, 10, ptr, 4, ptr, ptr, None, work, ws_bytes, 8, None, None)
+    assert call(_dims(d_c=256)) == mla.MLA_ERR_UNSUPPORTED
+    assert call(B=0) == mla.MLA_ERR_INVALID_ARG
+    assert call(wdq=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(d_cq=0) == mla.MLA_ERR_INVALID_ARG
+    assert call(ptr=None) == mla.MLA_ERR_INVALID_ARG
+    assert call(ptr=ctypes.c_void_p(16 * 4096 + 2)) == mla.MLA_ERR_INVALID_ARG
+    assert call(stride=500) == mla.MLA_ERR_INVALID_ARG
+    assert call(work=ctypes.c_void_p((1 << 20) + 16)) == mla.MLA_ERR_INVALID_ARG
+    assert call(ws_bytes=4096) == mla.MLA_ERR_WORKSPACE

@@ -1,0 +1,81 @@
+"""GPU parity of the whole decode layer (mla_decode_layer): query projection,
+decode step and output projection from the new tokens' states h to u.
+
+Checked two ways: bit for bit against the three entry points called one after
+the other (mla_query_project, mla_decode_step, mla_output_project), and
+against the fp64 oracle chained the same way -- oracle.query_project_lowrank,
+the absorbed attention over the oracle's own cache rows, oracle.output_project
+-- on sampled sequences, within the bf16 bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+import workloads as W
+from cases import oracle_cache, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _proj_weights(seed, n_h, d_model, d_cq, device):
+    g = lambda name, r, c: si.normal(si.stream_key(seed, name), (r, c), c ** -0.5, torch.bfloat16, device)  # noqa
+    return dict(W_DQ=g("W_DQ", d_cq, d_model) if d_cq else None,
+                W_UQ=g("W_UQ", n_h * 128, d_cq or d_model), W_QR=g("W_QR", n_h * 64, d_model),
+                W_O=g("W_O", d_model, n_h * 128))
+
+
+@pytest.mark.parametrize("B,d_model,d_cq,lens", [(5, 1024, 512, (40, 700)), (40, 1024, 0, (20, 300))])
+def test_decode_layer_equals_its_parts_and_the_oracle(B, d_model, d_cq, lens):
+    import compressed_kv_cache_mla_amd as mla
+    cfg = W.scaled(W.CONFIGS["b64_ragged"], name=f"layer_b{B}_q{d_cq}", d_model=d_model, B=B, lens=lens,
+                   seed=1300 + B + d_cq)
+    _say(f"case {cfg.name}")
+    wl = W.Workload(cfg, n_splits=37)
+    dims, n_h = wl.dims, cfg.n_h
+    P = _proj_weights(cfg.seed, n_h, d_model, d_cq, "cuda")
+    Pp = {k: (None if v is None else mla.pack_weight(dims, v)) for k, v in P.items()}
+    h = wl._newest_token_states()
+    u = torch.full((B, d_model), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, n_h), dtype=torch.float32, device="cuda")
+    ws = mla.decode_layer_workspace(dims, B, d_cq, 37)
+    for call in range(2):
+        mla.decode_layer(dims, h, wl.W_DKV, wl.W_KR, Pp["W_DQ"], Pp["W_UQ"], Pp["W_QR"], wl.W_UK, wl.W_UV, Pp["W_O"],
+                         wl.pos_q, wl.c_KV, wl.k_R, wl.row_stride, wl.num_pages, wl.page_table, wl.seq_lens, u, lse,
+                         ws, n_splits=37)
+        torch.cuda.synchronize()
+        assert mla.read_error_flags(ws) == 0
+    # the three parts, one after the other, on workspaces of their own
+    q_C = torch.empty((B, n_h, 128), dtype=torch.bfloat16, device="cuda")
+    q_R = torch.empty((B, n_h, 64), dtype=torch.bfloat16, device="cuda")
+    mla.query_project(dims, h, Pp["W_DQ"], Pp["W_UQ"], Pp["W_QR"], q_C, q_R,
+                      mla.query_project_workspace(dims, B, d_cq))
+    out = torch.empty((B, n_h, 128), dtype=torch.float32, device="cuda")
+    lse2 = torch.empty_like(lse)
+    mla.decode_step(dims, h, wl.W_DKV, wl.W_KR, q_C, q_R, wl.pos_q, wl.W_UK, wl.W_UV, wl.c_KV, wl.k_R,
+                    wl.row_stride, wl.num_pages, wl.page_table, wl.seq_lens, out, lse2,
+                    mla.decode_step_workspace(dims, B, 37), 37)
+    u2 = torch.empty_like(u)
+    mla.output_project(dims, out, Pp["W_O"], u2, mla.output_project_workspace(dims, B))
+    torch.cuda.synchronize()
+    assert torch.equal(u, u2) and torch.equal(lse, lse2)
+    # the oracle, chained
+    f = {k: (None if v is None else v.double().cpu().numpy()) for k, v in P.items()}
+    got = u.double().cpu().numpy()
+    for b in sorted({0, B - 1, B // 2}):
+        d = wl.oracle_inputs(b)
+        c, kR = oracle_cache(wl, d)
+        h_b = d["h"][d["n"] - 1]
+        if d_cq:
+            qc, qr = oracle.query_project_lowrank(h_b, f["W_DQ"], f["W_UQ"], f["W_QR"], n_h)
+        else:
+            qc, qr = oracle.query_project(h_b, f["W_UQ"], f["W_QR"], n_h)
+        o, _ = oracle.attend_absorbed(qc, qr, d["pos_q"], c, kR, d["W_UK"], d["W_UV"], dims.rope_base, dims.scale)
+        ref = oracle.output_project(o, f["W_O"])
+        e = rel_err(got[b], ref)
+        assert e <= 1e-2, f"sequence {b}: rel err {e:.3e}"
