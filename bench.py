@@ -14,7 +14,8 @@ Prints one JSON line.  `value` is decode tokens/s (B sequences per step);
 bytes and its HIP-event duration measured in the timed region; `projections`
 times the query path (W^DQ, W^UQ, W^QR) and the output projection W^O, which
 sit outside the step, at the same batch sizes; `prefill` times chunked
-prefill (new tokens attending causally over their sequences); `cpu_baseline`
+prefill (new tokens attending causally over their sequences); `layer` times
+the whole attention layer (query path + step + W^O, h -> u); `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -132,6 +133,48 @@ def measure_projections(torch, mla, B: int, n_h: int = 128, d_model: int = 5120,
     return out
 
 
+def measure_layer(torch, mla, W, name: str, d_cq: int = 1536, reps: int = 20, copies: int = 2):
+    """One whole MLA attention layer per decode token (mla_decode_layer: query
+    projection, decode step, output projection, h -> u) on a workload, over
+    rotating copies with their own weights; HIP events per call, median."""
+    import seeded_inputs as si
+    cfg = W.CONFIGS[name]
+    wls = [W.Workload(cfg, layer=i) for i in range(copies)]
+    dims, nh, dm, B = wls[0].dims, cfg.n_h, cfg.d_model, cfg.B
+    runs = []
+    for i, wl in enumerate(wls):
+        key = lambda nm: si.stream_key(cfg.seed + 77, nm, i)  # noqa: E731
+        pw = lambda nm, r, c: mla.pack_weight(dims, si.normal(key(nm), (r, c), c ** -0.5, torch.bfloat16, "cuda"))  # noqa
+        P = dict(W_DQ=pw("W_DQ", d_cq, dm), W_UQ=pw("W_UQ", nh * 128, d_cq), W_QR=pw("W_QR", nh * 64, dm),
+                 W_O=pw("W_O", dm, nh * 128))
+        u = torch.empty((B, dm), dtype=torch.float32, device="cuda")
+        ws = mla.decode_layer_workspace(dims, B, d_cq)
+        h = wl._newest_token_states()
+
+        def call(wl=wl, P=P, u=u, ws=ws, h=h):
+            mla.decode_layer(dims, h, wl.W_DKV, wl.W_KR, P["W_DQ"], P["W_UQ"], P["W_QR"], wl.W_UK, wl.W_UV, P["W_O"],
+                             wl.pos_q, wl.c_KV, wl.k_R, wl.row_stride, wl.num_pages, wl.page_table, wl.seq_lens, u,
+                             wl.lse, ws)
+        runs.append(call)
+    for i in range(4):
+        runs[i % copies]()
+    torch.cuda.synchronize()
+    evs = [(mla.HipEvent(), mla.HipEvent()) for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        runs[i % copies]()
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.median([1e3 * a.elapsed_ms(b) for a, b in evs]))
+    alg = algorithmic(wls[0])
+    nbytes = alg["step_bytes"] + 2 * (d_cq * dm + nh * 128 * d_cq + nh * 64 * dm + dm * nh * 128) + 4 * B * dm
+    del wls, runs
+    torch.cuda.empty_cache()
+    return {"workload": name, "B": B, "d_cq": d_cq, "us_p50": round(us, 1), "tokens_per_s": round(B / (us * 1e-6), 1),
+            "alg_MB": round(nbytes / 1e6, 1), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def measure_prefill(torch, mla, B: int, L: int, T: int, n_h: int = 128, d_model: int = 5120, reps: int = 10):
     """Chunked prefill (mla_prefill) of T new tokens per sequence after an
     L-token prior, B sequences, DeepSeek-V2 sizes, 64-token pages in order.
@@ -237,6 +280,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-projections", action="store_true", help="skip the query / output projection timings")
     ap.add_argument("--prefill-only", action="store_true", help="only time the chunked prefill configurations")
+    ap.add_argument("--layer-only", default="", help="comma-separated workloads: only time the whole decode layer")
     ap.add_argument("--projections-only", default="",
                     help="comma-separated batch sizes: only time the query / output projections at them")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -260,6 +304,9 @@ def main():
         return
     import workloads as W
     import compressed_kv_cache_mla_amd as mla
+    if args.layer_only:
+        print(json.dumps({"layer": [measure_layer(torch, mla, W, n) for n in args.layer_only.split(",")]}), flush=True)
+        return
     if args.prefill_only:
         print(json.dumps({"prefill": [measure_prefill(torch, mla, *cfg) for cfg in PREFILL_CONFIGS]}), flush=True)
         return
@@ -370,6 +417,9 @@ def main():
     if not args.no_projections:
         # the chunked-prefill row: new tokens attending causally over their sequences
         res["prefill"] = [measure_prefill(torch, mla, *cfg) for cfg in PREFILL_CONFIGS]
+        # the whole attention layer (query path + decode step + W^O) at the step's workloads
+        res["layer"] = [measure_layer(torch, mla, W, n) for n in
+                        dict.fromkeys([cfg.name, res.get("target_shape", {}).get("workload", cfg.name)])]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
     print(json.dumps(res), flush=True)
