@@ -311,12 +311,13 @@ inline int64_t gemm_rows_padded(int32_t M) { return ((int64_t)M + 63) / 64 * 64;
 int gemm_pick_splits(int32_t M, int32_t N, int32_t K);
 // Bytes of the chunk sums of a split product (0 when S == 1).
 size_t gemm_part_bytes(int32_t M, int32_t N, int32_t S);
-// One launch of the product with packed weights.  f32_weights: fp32 X (rows),
-// W (packed fp32) and Y (VALU kernel; g.S is ignored).  Otherwise bf16 W; X
-// packed bf16 when gemm_x_packed(M), else rows of fp32 (x_f32) or bf16; Y
-// fp32 (y_f32) or bf16; with g.S > 1, g.part holds gemm_part_bytes(M, N, S)
-// bytes and g.counters SPLITK_COUNTERS zeros (every completed launch leaves
-// them at zero); a split product must have at most SPLITK_COUNTERS tiles.
+// The product with packed weights.  f32_weights: fp32 X (rows), W (packed
+// fp32) and Y (VALU kernel; g.S is ignored).  Otherwise bf16 W; X packed bf16
+// when gemm_x_packed(M), else rows of fp32 (x_f32) or bf16; Y fp32 (y_f32) or
+// bf16; with g.S > 1, g.part holds gemm_part_bytes(M, N, S) bytes, and up to
+// 16 rows (one launch, in-launch finish) g.counters SPLITK_COUNTERS zeros
+// (every completed launch leaves them at zero; at most SPLITK_COUNTERS tiles);
+// above 16 rows a second launch adds the chunks.
 hipError_t launch_gemm(const GemmArgs& g, const GemmOut& o, bool f32_weights, bool x_f32, bool y_f32, hipStream_t s);
 // Packs rows x K of a row-major matrix (row stride ld elements) into dst
 // (packed layout, rows_padded rows; rows past `rows` are zero).  Element
