@@ -12,6 +12,8 @@
 // W^UK's row index.  fp32 (VALU): workgroup (head h, 32 sequences), W^UK_h
 // (128 x 512) streamed through LDS in 32-row chunks; each thread owns 2 latent
 // columns for the 32 sequences, q^C comes from LDS.  bf16: the MFMA kernel below.
+#include <algorithm>
+
 #include "absorb_mfma.h"
 
 namespace mla {
@@ -80,13 +82,14 @@ __global__ void __launch_bounds__(256) absorb_mfma_kernel(int32_t B, int32_t n_h
                                                           const bf16* __restrict__ q_R,
                                                           const int32_t* __restrict__ pos_q,
                                                           const bf16* __restrict__ W_UK, float qscale,
-                                                          RopeTab rope, bf16* __restrict__ qabs, PlanArgs pa) {
+                                                          RopeTab rope, bf16* __restrict__ qabs, PlanArgs pa,
+                                                          int32_t nby) {
   __shared__ __attribute__((aligned(1024))) char wl[D_H * 256];
   if (blockIdx.x == 4 * n_h) {
     if (blockIdx.y == 0) plan_block<256>(pa, (int32_t*)wl, D_H * 256 / 4 - 256);
     return;
   }
-  absorb_mfma_block(blockIdx.x, blockIdx.y, B, n_h, q_C, q_R, pos_q, W_UK, qscale, rope, qabs, wl);
+  absorb_mfma_block(blockIdx.x, blockIdx.y, nby, B, n_h, q_C, q_R, pos_q, W_UK, qscale, rope, qabs, wl);
 }
 
 }  // namespace
@@ -101,9 +104,13 @@ hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const vo
     absorb_kernel<float><<<grid, 256, 0, s>>>(B, d.n_h, (const float*)q_C, (const float*)q_R, pos_q,
                                               (const float*)W_UK, qscale, rope_table(d.rope_base), (float*)qabs);
   } else {
-    dim3 g2(4 * d.n_h + 1, (B + 63) / 64);
+    // blocks of 64 sequences per workgroup: one, unless the grid would exceed
+    // ~1024 workgroups; then each W^UK block serves several (long batches)
+    const int32_t nblocks = (B + 63) / 64;
+    const int32_t nby = std::max<int32_t>(1, (int32_t)((int64_t)nblocks * 4 * d.n_h / 1024));
+    dim3 g2(4 * d.n_h + 1, (nblocks + nby - 1) / nby);
     absorb_mfma_kernel<<<g2, 256, 0, s>>>(B, d.n_h, (const bf16*)q_C, (const bf16*)q_R, pos_q, (const bf16*)W_UK,
-                                         qscale, rope_table(d.rope_base), (bf16*)qabs, pa);
+                                         qscale, rope_table(d.rope_base), (bf16*)qabs, pa, nby);
   }
   return hipGetLastError();
 }

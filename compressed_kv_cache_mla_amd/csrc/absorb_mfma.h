@@ -10,18 +10,20 @@
 
 namespace mla {
 
-// Workgroup (head h, latent columns 128q .. 128q+127, 64 sequences), 4 waves.
+// Workgroup (head h, latent columns 128q .. 128q+127, nby blocks of 64
+// sequences: blocks by*nby .. by*nby + nby - 1), 4 waves.
 // q~^T[c][b] = sum_d W^UK_h[d][c] q^C[b][d] as v_mfma_f32_32x32x16_bf16 with
 // M = latent column c, N = sequence, K = d.  The W^UK_h column block (128 rows
-// x 256 B = 32 KB) is copied to LDS with global_load_lds, 4 rows of 256 B per
-// copy instruction; 16-byte chunk c16 of row d sits at chunk c16 ^ 4*(d & 3),
-// which keeps the transposed reads (ds_read_b64_tr_b16, 4 rows x 4 chunks per
-// half-wave) bank-conflict free.  Wave w produces columns 128q + 32w .. +31.
-// The last workgroup of the grid runs the decode plan instead.
+// x 256 B = 32 KB) is copied to LDS once, with global_load_lds, 4 rows of
+// 256 B per copy instruction; 16-byte chunk c16 of row d sits at chunk
+// c16 ^ 4*(d & 3), which keeps the transposed reads (ds_read_b64_tr_b16, 4
+// rows x 4 chunks per half-wave) bank-conflict free.  Wave w produces columns
+// 128q + 32w .. +31.  With more than one block (long batches: prefill), the
+// W^UK block serves all of them.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-__device__ __forceinline__ void absorb_mfma_block(int bx, int by, int32_t B, int32_t n_h,
+__device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32_t B, int32_t n_h,
                                                   const bf16* __restrict__ q_C, const bf16* __restrict__ q_R,
                                                   const int32_t* __restrict__ pos_q, const bf16* __restrict__ W_UK,
                                                   float qscale, const RopeTab& rope, bf16* __restrict__ qabs,
@@ -29,8 +31,6 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int32_t B, int
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = bx >> 2, cq = bx & 3;
-  const int b0 = by * 64;
-  const int nb = min(64, B - b0);
   // W^UK_h[:, 128cq .. 128cq+127] -> LDS (2048 chunks of 16 B; 8 copy instructions per wave)
   const char* wsrc = (const char*)(W_UK + (int64_t)h * D_H * D_C) + 256 * cq;
 #pragma unroll
@@ -45,15 +45,12 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int32_t B, int
   // (lane & 31), d = 16*ks + 8*(lane >> 5).  The second block (sequences
   // 32..63) is loaded after the first block's MFMAs have read their operands.
   bf16x8 qf[8];
-  auto load_qf = [&](int nblk) {
+  auto load_qf = [&](int b0, int nblk) {
     const int b = min(b0 + 32 * nblk + (lane & 31), B - 1);
     const bf16* qp = q_C + ((int64_t)b * n_h + h) * D_H + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
   };
-  load_qf(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   // transposed-read source address: row d = 16ks + 8*(lane>>5) + 4rr + ((lane&15)>>2),
   // local columns 32w + 16*((lane>>4)&1) + 4*(lane&3)
   const int t_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
@@ -82,7 +79,7 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int32_t B, int
     return acc;
   };
   // C layout: lane -> sequence (lane & 31) of the block, latent rows (r/4)*8 + 4*(lane>>5) + r%4
-  auto store_block = [&](const f32x16& acc, int nblk) {
+  auto store_block = [&](const f32x16& acc, int b0, int nb, int nblk) {
     const int bb = 32 * nblk + (lane & 31);
     if (bb < nb) {
       bf16* dst = qabs + ((int64_t)(b0 + bb) * n_h + h) * D_K + 128 * cq + 32 * wave + 4 * (lane >> 5);
@@ -97,24 +94,32 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int32_t B, int
       }
     }
   };
-  {
-    const f32x16 acc0 = block_product();
-    if (nb > 32) load_qf(1);
-    store_block(acc0, 0);
-  }
-  if (nb > 32) store_block(block_product(), 1);
-  // RoPE half (32 pairs per sequence), by the column-quarter-0 workgroups
-  if (cq == 0) {
-    for (int i = tid; i < nb * (D_R / 2); i += 256) {
-      const int bb = i / (D_R / 2), k = i % (D_R / 2);
-      const int b = b0 + bb;
-      const bf16* src = q_R + ((int64_t)b * n_h + h) * D_R;
-      const float x0 = (float)src[2 * k], x1 = (float)src[2 * k + 1];
-      float cs, sn;
-      rope_cos_sin(pos_q[b], k, rope, &cs, &sn);
-      bf16* dst = qabs + ((int64_t)b * n_h + h) * D_K + D_C;
-      dst[2 * k] = (bf16)((x0 * cs - x1 * sn) * qscale);
-      dst[2 * k + 1] = (bf16)((x0 * sn + x1 * cs) * qscale);
+  for (int j = 0; j < nby; ++j) {
+    const int b0 = (by * nby + j) * 64;
+    if (b0 >= B) break;
+    const int nb = min(64, B - b0);
+    load_qf(b0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (j == 0) __syncthreads();   // the W^UK block has landed (it is only read from here on)
+    {
+      const f32x16 acc0 = block_product();
+      if (nb > 32) load_qf(b0, 1);
+      store_block(acc0, b0, nb, 0);
+    }
+    if (nb > 32) store_block(block_product(), b0, nb, 1);
+    // RoPE half (32 pairs per sequence), by the column-quarter-0 workgroups
+    if (cq == 0) {
+      for (int i = tid; i < nb * (D_R / 2); i += 256) {
+        const int bb = i / (D_R / 2), k = i % (D_R / 2);
+        const int b = b0 + bb;
+        const bf16* src = q_R + ((int64_t)b * n_h + h) * D_R;
+        const float x0 = (float)src[2 * k], x1 = (float)src[2 * k + 1];
+        float cs, sn;
+        rope_cos_sin(pos_q[b], k, rope, &cs, &sn);
+        bf16* dst = qabs + ((int64_t)b * n_h + h) * D_K + D_C;
+        dst[2 * k] = (bf16)((x0 * cs - x1 * sn) * qscale);
+        dst[2 * k + 1] = (bf16)((x0 * sn + x1 * cs) * qscale);
+      }
     }
   }
 }

@@ -60,7 +60,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) s
   }
   bid -= a.n_app;
   const int nx = 4 * a.n_h;
-  absorb_mfma_block(bid % nx, bid / nx, a.B, a.n_h, a.q_C, a.q_R, a.pos_q, a.W_UK, a.qscale, a.dst.rope, a.qabs,
+  absorb_mfma_block(bid % nx, bid / nx, 1, a.B, a.n_h, a.q_C, a.q_R, a.pos_q, a.W_UK, a.qscale, a.dst.rope, a.qabs,
                     smem);
 }
 

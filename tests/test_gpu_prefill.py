@@ -168,6 +168,16 @@ def test_prefill_deepseek_sizes_sampled():
     c.check()
 
 
+def test_prefill_long_chunk_shares_the_absorption_weights():
+    """512 new tokens after a 300-token prior (n_h = 128): the absorption then
+    lets each W^UK block serve several 64-token blocks; every token checked."""
+    _say("case prefill 512-token chunk")
+    c = Chunk(81, 128, 1024, torch.bfloat16, [300], [512], 64)
+    c.run()
+    assert c.mla.read_error_flags(c.ws) == 0
+    c.check()
+
+
 def test_prefill_one_token_per_sequence_equals_decode():
     """One new token per sequence is the decode of that token: mla_prefill
     against mla_cache_append + mla_decode on the same inputs (within the bf16
