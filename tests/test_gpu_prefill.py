@@ -207,3 +207,21 @@ def test_prefill_flags_a_bad_sequence_id():
     out = c.out.cpu().numpy()
     assert np.all(out[bad] == 0) and np.all(np.isneginf(c.lse.cpu().numpy()[bad]))
     c.check(seqs=[0])                               # the other sequence is untouched by the bad token
+
+
+def test_prefill_rows_after_a_token_do_not_change_it():
+    """Causality on the GPU: rewriting the pool rows after a token's position
+    (here: the last 10 positions of the sequence) leaves that token's output
+    bit for bit unchanged when the chunk is run again with the later tokens
+    given other states."""
+    _say("case prefill no future leak")
+    c = Chunk(82, 32, 1024, torch.bfloat16, [200], [40], 64, shuffle=False)
+    c.run()
+    before = c.out.clone()
+    # other token states for the last 10 new tokens: their rows (positions 230..239) change
+    c.c_glob = c.c_glob.copy()
+    c.c_glob[-10:] += 100000
+    c.run()
+    after = c.out
+    assert torch.equal(before[:30], after[:30])
+    assert not torch.equal(before[30:], after[30:])

@@ -93,6 +93,7 @@ QUERY_CASES = [
     (8, 1024, 16, 128, torch.bfloat16),       # last row-major batch
     (9, 1024, 16, 128, torch.bfloat16),       # first packed batch (16-row tiles)
     (33, 1024, 16, 256, torch.bfloat16),      # 64-row tiles, one ragged
+    (100, 1024, 16, 256, torch.bfloat16),     # two 64-row blocks, the second ragged
     (1, 1024, 16, 512, torch.float32),
     (6, 1024, 16, 0, torch.float32),
 ]
@@ -146,6 +147,7 @@ OUTPUT_CASES = [
     (37, 1024, 16, torch.bfloat16),           # 64-row tile, ragged
     (8, 1024, 16, torch.bfloat16),            # row-major activations
     (17, 1024, 16, torch.bfloat16),           # 32-row tile
+    (130, 1024, 16, torch.bfloat16),          # three 64-row blocks, the last ragged
     (3, 1024, 16, torch.float32),
 ]
 
