@@ -253,12 +253,13 @@ __global__ void __launch_bounds__(64 * SMALL_W) append_bf16_small_kernel(
 // Decode-step append with a workspace: split over d_model (append_splitk.h),
 // chunk sums in the workspace, then one pass that adds them in a fixed order,
 // applies RoPE and stores the rows (deterministic, no float atomics).
+template <int MT>
 __global__ void __launch_bounds__(256) append_splitk_kernel(int32_t T_rows, int32_t d_model,
                                                             const bf16* __restrict__ h,
                                                             const bf16* __restrict__ W_DKV,
                                                             const bf16* __restrict__ W_KR, float* __restrict__ part) {
-  __shared__ float red[SK_RED_FLOATS];
-  append_splitk_block(blockIdx.x, blockIdx.y, blockIdx.z, T_rows, d_model, h, W_DKV, W_KR, part, red);
+  __shared__ float red[gk_red_floats(MT)];
+  append_splitk_block<false, MT>(blockIdx.x, blockIdx.y, blockIdx.z, T_rows, d_model, h, W_DKV, W_KR, part, red);
 }
 
 __global__ void __launch_bounds__(256) append_finish_kernel(int32_t T_rows, int32_t d_model,
@@ -281,9 +282,14 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
                          int32_t num_pages, int32_t* err_flag, void* ws, size_t ws_bytes, hipStream_t s) {
   const size_t need = append_workspace_bytes(d, T);
   if (ws && need > 0 && ws_bytes >= need) {
-    dim3 g1(D_K / 16, SK_SPLIT, (T + SK_TOK - 1) / SK_TOK);
-    append_splitk_kernel<<<g1, 256, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV, (const bf16*)W_KR,
-                                           (float*)ws);
+    const int rows = 16 * append_mt(T);
+    dim3 g1(D_K / 16, SK_SPLIT, (T + rows - 1) / rows);
+    if (append_mt(T) == 4)
+      append_splitk_kernel<4><<<g1, 256, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV,
+                                                (const bf16*)W_KR, (float*)ws);
+    else
+      append_splitk_kernel<2><<<g1, 256, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV,
+                                                (const bf16*)W_KR, (float*)ws);
     const int64_t n = (int64_t)T * (D_K / 2);
     const AppendDst a{seq_id, pos, page_table, num_seqs, max_pages, d.page_size, num_pages, (bf16*)c_KV,
                       (bf16*)k_R, row_stride, rope_table(d.rope_base), err_flag};

@@ -21,8 +21,14 @@
 namespace mla {
 
 constexpr int SK_SPLIT = APPEND_SK_SPLIT;   // d_model chunks
-constexpr int SK_TOK = GK_TOK;              // tokens per workgroup
+constexpr int SK_TOK = GK_TOK;              // tokens per workgroup up to 32 tokens
 constexpr int SK_RED_FLOATS = GK_RED_FLOATS;
+// Token rows per workgroup: 32 (MT = 2) up to 32 tokens, 64 (MT = 4) above,
+// so that a 33..64-token batch reads the weights once.
+inline int append_mt(int32_t T) { return T > 32 ? 4 : 2; }
+// K-steps per load batch for MT row tiles (the 64-row form keeps its loads
+// within the fused step's register budget).
+__host__ __device__ constexpr int append_kb(int MT) { return MT == 4 ? 2 : GK_KB; }
 
 // Where and how the finished rows are stored.
 struct AppendDst {
@@ -58,13 +64,15 @@ __device__ __forceinline__ GemmArgs append_gemm(int32_t T_rows, int32_t d_model,
   return g;
 }
 
-// Chunk sums of workgroup (col_blk, kc, tok_blk); red: SK_RED_FLOATS floats of LDS.
-template <bool COHERENT = false>
+// Chunk sums of workgroup (col_blk, kc, tok_blk) of 16*MT token rows; red:
+// gk_red_floats(MT) floats of LDS.
+template <bool COHERENT = false, int MT = 2>
 __device__ __forceinline__ void append_splitk_block(int col_blk, int kc, int tok_blk, int32_t T_rows,
                                                     int32_t d_model, const bf16* __restrict__ h,
                                                     const bf16* __restrict__ W_DKV, const bf16* __restrict__ W_KR,
                                                     float* __restrict__ part, float* red) {
-  gemm_chunk<COHERENT>(col_blk, kc, tok_blk, append_gemm(T_rows, d_model, h, W_DKV, W_KR, part, nullptr), red);
+  gemm_chunk<COHERENT, MT, GK_X_ROWS, false, append_kb(MT)>(
+      col_blk, kc, tok_blk, append_gemm(T_rows, d_model, h, W_DKV, W_KR, part, nullptr), red);
 }
 
 // Store of a finished column pair (columns 2cp, 2cp+1) of token t: RoPE on
@@ -107,12 +115,13 @@ __device__ __forceinline__ void append_finish_pair(int32_t T_rows, int32_t d_mod
 
 // In-launch finish of tile (col_blk, tok_blk) by the last of its SK_SPLIT
 // workgroups (gemm_finish_tile), right after append_splitk_block<true>.
+template <int MT = 2>
 __device__ __forceinline__ void append_splitk_finish_tile(int col_blk, int tok_blk, int32_t T_rows, int32_t d_model,
                                                           float* part, int32_t* counters, const AppendDst& a,
                                                           int* lds_flag) {
   const GemmArgs g = append_gemm(T_rows, d_model, nullptr, nullptr, nullptr, part, counters);
-  gemm_finish_tile(col_blk, tok_blk, g, [&](int m, int cp, float x0, float x1) { append_store_pair(m, cp, x0, x1, a); },
-                   lds_flag);
+  gemm_finish_tile<MT>(col_blk, tok_blk, g,
+                       [&](int m, int cp, float x0, float x1) { append_store_pair(m, cp, x0, x1, a); }, lds_flag);
 }
 
 }  // namespace mla

@@ -26,7 +26,7 @@ struct StepPrepArgs {
   float* app_part;
   int32_t* app_cnt;
   AppendDst dst;
-  int32_t n_app;        // append workgroups: SK_SPLIT * (D_K / 16) * ceil(B / SK_TOK)
+  int32_t n_app;        // append workgroups: SK_SPLIT * (D_K / 16) * ceil(B / (16 * append_mt(B)))
   int32_t d_model;
   // absorb
   const bf16* q_C;
@@ -38,10 +38,13 @@ struct StepPrepArgs {
   int32_t B, n_h;
 };
 
+// AMT: 16-row tiles per append workgroup (append_mt).
+template <int AMT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) step_prep_kernel(StepPrepArgs a) {
   // absorb's W^UK block (32 KB, so that five workgroups fit in a CU's LDS);
-  // the append uses its first SK_RED_FLOATS floats and one int after them
+  // the append uses its first gk_red_floats(AMT) floats and one int after them
   __shared__ __attribute__((aligned(1024))) char smem[D_H * 256];
+  static_assert(gk_red_floats(4) * 4 + 4 <= D_H * 256, "append reduction fits the absorb block");
   int bid = blockIdx.x;
   if (bid == 0) {
     plan_block<256>(a.pa, (int32_t*)smem, D_H * 256 / 4 - 256);
@@ -53,9 +56,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) s
     const int kc = bid % SK_SPLIT;
     const int col_blk = (bid / SK_SPLIT) % (D_K / 16);
     const int tok_blk = bid / (SK_SPLIT * (D_K / 16));
-    append_splitk_block<true>(col_blk, kc, tok_blk, a.B, a.d_model, a.h_new, a.W_DKV, a.W_KR, a.app_part, (float*)smem);
-    append_splitk_finish_tile(col_blk, tok_blk, a.B, a.d_model, a.app_part, a.app_cnt, a.dst,
-                              (int*)(smem + SK_RED_FLOATS * 4));
+    append_splitk_block<true, AMT>(col_blk, kc, tok_blk, a.B, a.d_model, a.h_new, a.W_DKV, a.W_KR, a.app_part,
+                                   (float*)smem);
+    append_splitk_finish_tile<AMT>(col_blk, tok_blk, a.B, a.d_model, a.app_part, a.app_cnt, a.dst,
+                                   (int*)(smem + gk_red_floats(AMT) * 4));
     return;
   }
   bid -= a.n_app;
@@ -83,7 +87,8 @@ hipError_t launch_step_prep(const mla_dims& d, int32_t B, const void* h_new, con
   a.app_part = app_part;
   a.app_cnt = app_cnt;
   a.dst = dst;
-  a.n_app = SK_SPLIT * (D_K / 16) * ((B + SK_TOK - 1) / SK_TOK);
+  const int rows = 16 * append_mt(B);
+  a.n_app = SK_SPLIT * (D_K / 16) * ((B + rows - 1) / rows);
   a.d_model = d.d_model;
   a.q_C = (const bf16*)q_C;
   a.q_R = (const bf16*)q_R;
@@ -95,7 +100,10 @@ hipError_t launch_step_prep(const mla_dims& d, int32_t B, const void* h_new, con
   a.n_h = d.n_h;
   const int64_t n_abs = (int64_t)4 * d.n_h * ((B + 63) / 64);
   const int64_t grid = 1 + (int64_t)a.n_app + n_abs;
-  step_prep_kernel<<<dim3((unsigned)grid), 256, 0, s>>>(a);
+  if (append_mt(B) == 4)
+    step_prep_kernel<4><<<dim3((unsigned)grid), 256, 0, s>>>(a);
+  else
+    step_prep_kernel<2><<<dim3((unsigned)grid), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -145,7 +145,7 @@ def test_bf16_rising_scores_rescale(n_h):
         assert np.max(np.abs(res[k][1] - res[1][1])) < 1e-3 * np.max(np.abs(res[1][1]))
 
 
-@pytest.mark.parametrize("d_model,B", [(1024, 7), (1024, 20), (512, 7)])
+@pytest.mark.parametrize("d_model,B", [(1024, 7), (1024, 20), (1024, 40), (512, 7)])
 def test_decode_step_equals_append_then_decode(d_model, B):
     # mla_decode_step (one launch for append + absorption + plan when d_model is
     # a multiple of 1024, separate launches otherwise) against the same inputs
