@@ -106,8 +106,8 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32
       if (nb > 32) load_qf(b0, 1);
       store_block(acc0, b0, nb, 0);
     }
-    if (nb > 32) store_block(block_product(), b0, nb, 1);
-    // RoPE half (32 pairs per sequence), by the column-quarter-0 workgroups
+    // RoPE half (32 pairs per sequence), by the column-quarter-0 workgroups,
+    // while the second block's query loads are in flight
     if (cq == 0) {
       for (int i = tid; i < nb * (D_R / 2); i += 256) {
         const int bb = i / (D_R / 2), k = i % (D_R / 2);
@@ -121,6 +121,7 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32
         dst[2 * k + 1] = (bf16)((x0 * sn + x1 * cs) * qscale);
       }
     }
+    if (nb > 32) store_block(block_product(), b0, nb, 1);
   }
 }
 
