@@ -216,10 +216,12 @@ class HipEvent:
         return float(ms.value)
 
     def __del__(self):
-        hip = type(self)._hip      # the class, not the module global (gone at interpreter exit)
-        if self.handle and hip is not None:
-            hip.hipEventDestroy(self.handle)
-            self.handle = ctypes.c_void_p()
+        # only the class and the instance are used: module globals (ctypes
+        # included) may already be gone at interpreter exit
+        hip, handle = type(self)._hip, getattr(self, "handle", None)
+        if handle and hip is not None:
+            hip.hipEventDestroy(handle)
+        self.handle = None
 
 
 def _event_handle(ev):
