@@ -82,7 +82,9 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32
   auto store_block = [&](const f32x16& acc, int b0, int nb, int nblk) {
     const int bb = 32 * nblk + (lane & 31);
     if (bb < nb) {
-      bf16* dst = qabs + ((int64_t)(b0 + bb) * n_h + h) * D_K + 128 * cq + 32 * wave + 4 * (lane >> 5);
+      // 4 consecutive latent dims (a multiple of 4 first) share one 8-dim chunk of the q~ layout
+      bf16* qb = qabs + (int64_t)(b0 + bb) * n_h * D_K;
+      const int d0 = 128 * cq + 32 * wave + 4 * (lane >> 5);
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 o;
@@ -90,7 +92,7 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32
         o[1] = (bf16)(acc[4 * r4 + 1] * qscale);
         o[2] = (bf16)(acc[4 * r4 + 2] * qscale);
         o[3] = (bf16)(acc[4 * r4 + 3] * qscale);
-        *(bf16x4*)(dst + 8 * r4) = o;
+        *(bf16x4*)(qb + qabs_offset(n_h, true, h, d0 + 8 * r4)) = o;
       }
     }
   };
@@ -116,9 +118,10 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32
         const float x0 = (float)src[2 * k], x1 = (float)src[2 * k + 1];
         float cs, sn;
         rope_cos_sin(pos_q[b], k, rope, &cs, &sn);
-        bf16* dst = qabs + ((int64_t)b * n_h + h) * D_K + D_C;
-        dst[2 * k] = (bf16)((x0 * cs - x1 * sn) * qscale);
-        dst[2 * k + 1] = (bf16)((x0 * sn + x1 * cs) * qscale);
+        bf16x2 o;
+        o[0] = (bf16)((x0 * cs - x1 * sn) * qscale);
+        o[1] = (bf16)((x0 * sn + x1 * cs) * qscale);
+        *(bf16x2*)(qabs + (int64_t)b * n_h * D_K + qabs_offset(n_h, true, h, D_C + 2 * k)) = o;
       }
     }
     if (nb > 32) store_block(block_product(), b0, nb, 1);

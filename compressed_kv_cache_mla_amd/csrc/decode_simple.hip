@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(256) decode_simple_kernel(
     const int64_t slot = (int64_t)blockIdx.x + b;
     for (int h = 0; h < n_h; ++h) {
       __syncthreads();
-      for (int k = tid; k < D_K; k += 256) qs[k] = to_f32(qabs[((int64_t)b * n_h + h) * D_K + k]);
+      for (int k = tid; k < D_K; k += 256) qs[k] = to_f32(qabs[(int64_t)b * n_h * D_K + qabs_offset(n_h, sizeof(T) == 2, h, k)]);
       __syncthreads();
       float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
       for (int cs = t0; cs < t1; cs += 256) {

@@ -17,8 +17,6 @@
 namespace mla {
 namespace {
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-
 // Finished column pair (2cp, 2cp+1) of row m: stored to its segment's output.
 template <typename YT>
 __device__ __forceinline__ void gemm_store_pair(const GemmArgs& g, const GemmOut& o, int m, int cp, float x0,

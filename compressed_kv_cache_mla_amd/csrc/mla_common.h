@@ -13,6 +13,7 @@ namespace mla {
 typedef __bf16 bf16;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -64,6 +65,23 @@ __device__ __forceinline__ void rope_cos_sin(int32_t pos, int k, const RopeTab& 
   const double n = rint(a * 0.15915494309189535);   // a / (2 pi), rounded
   const float r = (float)fma(-n, 6.283185307179586, a);
   sincosf(r, s, c);
+}
+
+// Element offset of (head h, dim d) in one sequence's block of the absorbed
+// queries q~ ([n_h x 576] elements).  bf16 with n_h % 32 == 0: the order in
+// which the attention kernel (decode_mfma.hip) loads them, so that each of
+// its load instructions reads 1 KB in one piece:
+//  * dims 0..447: 1 KB blocks ((h/16) * 14 + d/32), lane l of a block holding
+//    head 16*(h/16) + l%16, dims 32*(d/32) + 8*(l/16) .. +7 (the B operand of
+//    a 16x16x32 MFMA);
+//  * dims 448..575, after all heads' first part: for each 32-head group,
+//    32 x 16 chunks of 8 dims in head order, chunk c of head h at position
+//    c ^ (h % 16) (the layout the kernel keeps them in, in LDS).
+// Otherwise (fp32, or n_h not a multiple of 32) rows of 576 in head order.
+__host__ __device__ __forceinline__ int64_t qabs_offset(int32_t n_h, bool frag, int h, int d) {
+  if (!frag || n_h % 32 != 0) return (int64_t)h * D_K + d;
+  if (d < 448) return (int64_t)(h >> 4) * 7168 + (d >> 5) * 512 + ((((d >> 3) & 3) << 4) + (h & 15)) * 8 + (d & 7);
+  return (int64_t)n_h * 448 + (h >> 5) * 4096 + (((h & 31) << 4) + (((d - 448) >> 3) ^ (h & 15))) * 8 + (d & 7);
 }
 
 // Ints per split record (see plan_block).
