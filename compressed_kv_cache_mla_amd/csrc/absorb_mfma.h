@@ -96,11 +96,47 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32
       }
     }
   };
+  // RoPE half (32 pairs per sequence), shared by the 4 column-quarter
+  // workgroups of the head (pairs 512q .. 512q+511 of a 64-sequence block,
+  // two per thread): its operands are loaded with the block's first query
+  // fragments, so that their latency passes with that of the W^UK copy, and
+  // it is computed and stored after the first 32 sequences' product.
+  constexpr int RJ = 64 * (D_R / 2) / (4 * 256);
+  bf16x2 rx[RJ];
+  int32_t rpos[RJ];
+  auto load_rope = [&](int b0, int nb) {
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      const int i = tid + 256 * (RJ * cq + j);
+      if (i < nb * (D_R / 2)) {
+        const int b = b0 + i / (D_R / 2), k = i % (D_R / 2);
+        rx[j] = *(const bf16x2*)(q_R + ((int64_t)b * n_h + h) * D_R + 2 * k);
+        rpos[j] = pos_q[b];
+      }
+    }
+  };
+  auto store_rope = [&](int b0, int nb) {
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      const int i = tid + 256 * (RJ * cq + j);
+      if (i < nb * (D_R / 2)) {
+        const int b = b0 + i / (D_R / 2), k = i % (D_R / 2);
+        const float x0 = (float)rx[j][0], x1 = (float)rx[j][1];
+        float cs, sn;
+        rope_cos_sin(rpos[j], k, rope, &cs, &sn);
+        bf16x2 o;
+        o[0] = (bf16)((x0 * cs - x1 * sn) * qscale);
+        o[1] = (bf16)((x0 * sn + x1 * cs) * qscale);
+        *(bf16x2*)(qabs + (int64_t)b * n_h * D_K + qabs_offset(n_h, true, h, D_C + 2 * k)) = o;
+      }
+    }
+  };
   for (int j = 0; j < nby; ++j) {
     const int b0 = (by * nby + j) * 64;
     if (b0 >= B) break;
     const int nb = min(64, B - b0);
     load_qf(b0, 0);
+    load_rope(b0, nb);
     __builtin_amdgcn_s_waitcnt(0);
     if (j == 0) __syncthreads();   // the W^UK block has landed (it is only read from here on)
     {
@@ -108,22 +144,8 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32
       if (nb > 32) load_qf(b0, 1);
       store_block(acc0, b0, nb, 0);
     }
-    // RoPE half (32 pairs per sequence), by the column-quarter-0 workgroups,
     // while the second block's query loads are in flight
-    if (cq == 0) {
-      for (int i = tid; i < nb * (D_R / 2); i += 256) {
-        const int bb = i / (D_R / 2), k = i % (D_R / 2);
-        const int b = b0 + bb;
-        const bf16* src = q_R + ((int64_t)b * n_h + h) * D_R;
-        const float x0 = (float)src[2 * k], x1 = (float)src[2 * k + 1];
-        float cs, sn;
-        rope_cos_sin(pos_q[b], k, rope, &cs, &sn);
-        bf16x2 o;
-        o[0] = (bf16)((x0 * cs - x1 * sn) * qscale);
-        o[1] = (bf16)((x0 * sn + x1 * cs) * qscale);
-        *(bf16x2*)(qabs + (int64_t)b * n_h * D_K + qabs_offset(n_h, true, h, D_C + 2 * k)) = o;
-      }
-    }
+    store_rope(b0, nb);
     if (nb > 32) store_block(block_product(), b0, nb, 1);
   }
 }
