@@ -1,6 +1,7 @@
 // Query absorption: q~_i = W^UK_i^T q^C_i and RoPE(q^R_i) at the query
-// position, both scaled by softmax_scale * log2(e), packed as one 576-wide
-// query row per (sequence, head) in the decode workspace.
+// position, both scaled by softmax_scale * log2(e): 576 values per
+// (sequence, head) in the decode workspace, placed by qabs_offset (rows of 576
+// for fp32, the attention kernel's load order for bf16).
 //   "DeepSeek-V2：在“大力出奇迹”的AI军备竞赛中，四两拨千斤" (liang.world), ch.2 §2:
 //   by associativity W^UK is absorbed into the query side, so the score with
 //   k^C_j = W^UK c_j is q^C . W^UK c_j = (W^UK^T q^C) . c_j and keys are never
