@@ -82,7 +82,7 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32
   auto store_block = [&](const f32x16& acc, int b0, int nb, int nblk) {
     const int bb = 32 * nblk + (lane & 31);
     if (bb < nb) {
-      // 4 consecutive latent dims (a multiple of 4 first) share one 8-dim chunk of the q~ layout
+      // 4 consecutive latent dims (a multiple of 4 first) stay consecutive in the q~ layout
       bf16* qb = qabs + (int64_t)(b0 + bb) * n_h * D_K;
       const int d0 = 128 * cq + 32 * wave + 4 * (lane >> 5);
 #pragma unroll

@@ -334,10 +334,10 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   // the sum (its tokens only; the four parts are added when the segment ends).
   float m_ref[2], l_sum[2];
 
-  // q~ is stored in load order (qabs_offset): the 28 fragments of the
-  // register part of the wave's heads are 28 consecutive 1 KB blocks, and the
-  // staged part of its 32 heads is 8 KB in the order ql keeps it (chunk c of
-  // head h at chunk position c ^ (h & 15)), so every load reads 1 KB in one piece.
+  // q~ is grouped for these loads (qabs_offset): the 14 register fragments of
+  // 16 heads are 14 consecutive 1 KB blocks, and the staged dims 448..575 are
+  // 256 B per head, head after head, so every load below covers one whole
+  // 1 KB run.  ql keeps chunk c of head h at chunk position c ^ (h & 15).
   static_assert(KS_REG == 14 && QLB == 256, "the q~ layout of qabs_offset");
   auto load_q = [&](int32_t b) __attribute__((always_inline)) {
     int ln = lane;   // hidden from loop-invariant hoisting
@@ -345,13 +345,15 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
     const bf16* qb = qabs + (int64_t)b * NH * D_K;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const bf16* qp = qb + (2 * wave + hb) * KS_REG * 512 + 8 * ln;
+      const bf16* qp = qb + (2 * wave + hb) * KS_REG * 512 + (ln & 15) * 32 + 8 * (ln >> 4);
 #pragma unroll
       for (int ks = 0; ks < KS_REG; ++ks) q[hb][ks] = *(const bf16x8*)(qp + 512 * ks);
     }
 #pragma unroll
     for (int j = 0; j < 32 * QLB / 1024; ++j) {
-      const bf16* src = qb + NH * 32 * KS_REG + wave * 32 * (QLB / 2) + 512 * j + 8 * ln;
+      const int sigma = 64 * j + ln;
+      const int hl = sigma / (QLB / 16), c = (sigma % (QLB / 16)) ^ (hl & 15);
+      const bf16* src = qb + NH * 32 * KS_REG + (32 * wave + hl) * (QLB / 2) + 8 * c;
       dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(ql + wave * 32 * QLB + j * 1024)));
     }
   };

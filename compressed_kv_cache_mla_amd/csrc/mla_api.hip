@@ -518,9 +518,14 @@ mla_status mla_prefill(const mla_dims* dims, int32_t T, const void* h, const voi
   // append errors go to flag word 1 (cleared first), which the combine folds into word 0
   hipError_t e = mla::launch_prefill_queries(T, seq_id, pos, page_table, num_seqs, max_pages, dims->page_size, q_pt,
                                              q_len, (int32_t*)ws + 1, s);
+  // The append's split path keeps its chunk sums in the decode layout's
+  // partials region, which the attention fills only after the append.
+  const mla::DecodeWs D = mla::decode_ws_layout(T, dims->n_h, n_splits, (int)elt_size(dims));
+  const size_t app_need = mla::append_workspace_bytes(*dims, T);
+  char* app_ws = app_need > 0 && D.app_part - D.part_o >= app_need ? ws + D.part_o : nullptr;
   if (e == hipSuccess)
     e = mla::launch_append(*dims, T, h, W_DKV, W_KR, seq_id, pos, page_table, num_seqs, max_pages, c_KV, k_R,
-                           row_stride, num_pages, (int32_t*)ws + 1, nullptr, 0, s);
+                           row_stride, num_pages, (int32_t*)ws + 1, app_ws, app_ws ? app_need : 0, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return decode_impl(dims, T, q_C, q_R, pos, W_UK, W_UV, c_KV, k_R, row_stride, num_pages, q_pt, max_pages, q_len,
                      out, lse, workspace, L.q_pt, n_splits, nullptr, nullptr, stream, true);

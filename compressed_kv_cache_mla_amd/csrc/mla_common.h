@@ -68,20 +68,20 @@ __device__ __forceinline__ void rope_cos_sin(int32_t pos, int k, const RopeTab& 
 }
 
 // Element offset of (head h, dim d) in one sequence's block of the absorbed
-// queries q~ ([n_h x 576] elements).  bf16 with n_h % 32 == 0: the order in
-// which the attention kernel (decode_mfma.hip) loads them, so that each of
-// its load instructions reads 1 KB in one piece:
-//  * dims 0..447: 1 KB blocks ((h/16) * 14 + d/32), lane l of a block holding
-//    head 16*(h/16) + l%16, dims 32*(d/32) + 8*(l/16) .. +7 (the B operand of
-//    a 16x16x32 MFMA);
-//  * dims 448..575, after all heads' first part: for each 32-head group,
-//    32 x 16 chunks of 8 dims in head order, chunk c of head h at position
-//    c ^ (h % 16) (the layout the kernel keeps them in, in LDS).
+// queries q~ ([n_h x 576] elements).  bf16 with n_h % 32 == 0: grouped so
+// that each of the attention kernel's query loads (decode_mfma.hip) covers
+// one whole 1 KB run, while each head's dims stay in runs of 64 B or more for
+// the absorption's stores:
+//  * dims 0..447: for each 16 heads and each 32 dims, a 1 KB block holding
+//    the 16 heads' 32 dims head after head (the B operands of one K-step of
+//    the 16x16x32 score MFMAs);
+//  * dims 448..575, after all heads' first part: 128 dims per head, head
+//    after head.
 // Otherwise (fp32, or n_h not a multiple of 32) rows of 576 in head order.
 __host__ __device__ __forceinline__ int64_t qabs_offset(int32_t n_h, bool frag, int h, int d) {
   if (!frag || n_h % 32 != 0) return (int64_t)h * D_K + d;
-  if (d < 448) return (int64_t)(h >> 4) * 7168 + (d >> 5) * 512 + ((((d >> 3) & 3) << 4) + (h & 15)) * 8 + (d & 7);
-  return (int64_t)n_h * 448 + (h >> 5) * 4096 + (((h & 31) << 4) + (((d - 448) >> 3) ^ (h & 15))) * 8 + (d & 7);
+  if (d < 448) return (int64_t)(h >> 4) * 7168 + (d >> 5) * 512 + (h & 15) * 32 + (d & 31);
+  return (int64_t)n_h * 448 + h * 128 + (d - 448);
 }
 
 // Ints per split record (see plan_block).
@@ -237,9 +237,11 @@ __device__ __forceinline__ void plan_block(const PlanArgs& pa, int32_t* part, in
 // Launchers (host side), one per kernel family.
 namespace mla {
 // Cache append.  With a workspace of append_workspace_bytes(d, T) bytes (0:
-// no workspace path for these sizes) a decode-step batch (bf16, T <= 64) runs
-// split over d_model in two launches; otherwise one kernel does it.
-constexpr int APPEND_WS_MAX_T = 64;
+// no workspace path for these sizes) a batch of up to APPEND_WS_MAX_T rows
+// (bf16) runs split over d_model in two launches; otherwise one kernel does
+// it.  The split path measured faster from 128 to 1024 rows (33 against 53 us
+// at 512, 61 against 109 us at 1024 on DeepSeek-V2 sizes).
+constexpr int APPEND_WS_MAX_T = 1024;
 size_t append_workspace_bytes(const mla_dims& d, int32_t T);
 hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void* W_DKV, const void* W_KR,
                          const int32_t* seq_id, const int32_t* pos, const int32_t* page_table,

@@ -112,12 +112,12 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t T, const void* h_t, co
 
 /*
  * mla_cache_append_workspace_size -- bytes of device workspace with which
- * mla_cache_append_ws takes its split path for T tokens (bf16, T <= 64,
+ * mla_cache_append_ws takes its split path for T tokens (bf16, T <= 1024,
  * d_model a multiple of 1024); 0 when that path does not apply.
  *
  * mla_cache_append_ws -- mla_cache_append with a caller workspace
  * (256-byte aligned, device memory, contents need no initialisation).  With
- * at least mla_cache_append_workspace_size() bytes, a decode-step batch is
+ * at least mla_cache_append_workspace_size() bytes, the batch is
  * computed split over d_model (fp32 partial sums in the workspace, then one
  * pass that adds them in a fixed order, applies RoPE and stores the rows), so
  * the weight stream is spread over the whole GPU; results are the same

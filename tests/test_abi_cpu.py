@@ -316,7 +316,8 @@ def test_append_workspace_size():
     d = _dims()
     n = L.mla_cache_append_workspace_size(ctypes.byref(d), 32)
     assert n == 8 * 32 * 576 * 4
-    assert L.mla_cache_append_workspace_size(ctypes.byref(d), 65) == 0           # decode-step sizes only
+    assert L.mla_cache_append_workspace_size(ctypes.byref(d), 1024) == 8 * 1024 * 576 * 4
+    assert L.mla_cache_append_workspace_size(ctypes.byref(d), 1025) == 0         # up to 1024 rows
     assert L.mla_cache_append_workspace_size(ctypes.byref(_dims(dtype=mla.MLA_FP32)), 32) == 0
     assert L.mla_cache_append_workspace_size(ctypes.byref(_dims(d_model=1536)), 32) == 0
 

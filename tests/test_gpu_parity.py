@@ -120,6 +120,29 @@ def test_decode_step_append_paths(use_workspace):
     assert last.size == cfg.B
 
 
+@pytest.mark.parametrize("d_model,lens", [(1024, (150, 330)), (5120, (250, 330))])
+def test_cache_append_split_path_many_rows(d_model, lens):
+    # mla_cache_append_ws over every token of the batch at once (several
+    # hundred rows, up to the split path's 1024), against the oracle
+    cfg = W.scaled(W.CONFIGS["b32_l4096"], name=f"append_ws_{d_model}", n_h=32, d_model=d_model, B=3, lens=lens,
+                   seed=43)
+    _say(f"case append split path d_model={d_model}")
+    wl = W.Workload(cfg)
+    T = int(wl.prefix[-1])
+    assert 128 < T <= 1024
+    nws = wl.mla.cache_append_workspace_size(wl.dims, T)
+    assert nws == 8 * T * 576 * 4
+    ws = torch.empty(nws, dtype=torch.uint8, device=wl.device)
+    wl.pool.zero_()
+    seq, pos = wl.token_rows()
+    ids = np.arange(T)
+    wl.mla.cache_append(wl.dims, wl.h_rows(torch.from_numpy(ids).to(wl.device)), wl.W_DKV, wl.W_KR,
+                        torch.from_numpy(pos).to(wl.device), wl.page_table, wl.c_KV, wl.k_R, wl.row_stride,
+                        wl.num_pages, seq_id=torch.from_numpy(seq).to(wl.device), workspace=ws)
+    torch.cuda.synchronize()
+    _check_append(wl, range(cfg.B))
+
+
 @pytest.mark.parametrize("n_h", [32, 128])
 def test_bf16_rising_scores_rescale(n_h):
     # Cache rows grow by powers of two along each sequence (up to 32x), so the
