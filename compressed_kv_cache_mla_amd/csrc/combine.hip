@@ -256,9 +256,14 @@ hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, i
     combine_f32_kernel<<<grid, 256, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const float*)part_o,
                                             (const float*)W_UV, out, lse, merge_flags);
   } else {
-    // 32 sequences per workgroup (W^UV read once per 32) unless that leaves
-    // fewer workgroups than compute units
-    if (B > 16 && d.n_h * ((B + 31) / 32) >= 256) {
+    // the most sequences per workgroup (W^UV is read once per block of them)
+    // that still leave at least two workgroups per compute unit (64, for long
+    // query batches such as prefill chunks) or one (32); else 16
+    if (B > 32 && d.n_h * ((B + 63) / 64) >= 512) {
+      dim3 grid(d.n_h, (B + 63) / 64);
+      combine_mfma_kernel<64><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
+                                                    (const bf16*)W_UV, out, lse, merge_flags);
+    } else if (B > 16 && d.n_h * ((B + 31) / 32) >= 256) {
       dim3 grid(d.n_h, (B + 31) / 32);
       combine_mfma_kernel<32><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
                                                     (const bf16*)W_UV, out, lse, merge_flags);
