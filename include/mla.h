@@ -304,9 +304,10 @@ mla_status mla_output_project(const mla_dims* dims, int32_t B, const float* o, c
  * mla_prefill -- a chunk of T new tokens, any mix of sequences (chunked
  * prefill, or several decode tokens per sequence).  Token t belongs to
  * sequence seq_id[t] at position pos[t]; all T rows are first appended to the
- * latent cache as mla_cache_append_ws would with a large enough workspace
- * (liang.world ch.2 §2 eq. for c_t^KV; tuntang.top MLA section, k_t formula;
- * the split path's chunk sums use part of this workspace); then token t attends causally to rows
+ * latent cache as mla_cache_append would (liang.world ch.2 §2 eq. for c_t^KV;
+ * tuntang.top MLA section, k_t formula), through the split path of
+ * mla_cache_append_ws when the chunk fits it (up to 1024 rows, chunk sums in
+ * part of this workspace; only the fp32 summation order differs); then token t attends causally to rows
  * 0 .. pos[t] of its sequence, earlier tokens of the same chunk included
  * (liang.world ch.2 §1: a token attends to the tokens before it and itself),
  * exactly as mla_decode with one query per new token.
