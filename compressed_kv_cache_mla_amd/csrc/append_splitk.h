@@ -48,6 +48,7 @@ struct AppendDst {
 __device__ __forceinline__ GemmArgs append_gemm(int32_t T_rows, int32_t d_model, const bf16* h, const bf16* W_DKV,
                                                 const bf16* W_KR, float* part, int32_t* counters) {
   GemmArgs g;
+  g.x_rows = 0;
   g.X = h;
   g.ldx = d_model;
   g.W[0] = W_DKV;

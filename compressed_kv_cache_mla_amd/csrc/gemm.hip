@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmArgs g, GemmOut o) {
 // (activation bytes per weight byte MT/NT instead of MT).  The four waves'
 // sums are added in LDS in the order ((w3 + w2) + w1) + w0 into
 // red[16MT][16NT + 1].
-template <int MT, int NT, int KB>
+template <int MT, int NT, int KB, int XM>
 __device__ __forceinline__ void gemm_accumulate_wide(int n_blk, int kc, int m_blk, const GemmArgs& g, float* red) {
   constexpr int LD = 16 * NT + 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -77,6 +77,13 @@ __device__ __forceinline__ void gemm_accumulate_wide(int n_blk, int kc, int m_bl
   const int64_t tile = (int64_t)(K >> 5) * 512;   // elements from one 16-row block to the next
   const bf16* wp = gemm_weight(g, seg) + ((int64_t)((n0 - beg) >> 4) * (K >> 5) + (kbase >> 5)) * 512 + lane * 8;
   const bf16* xp = (const bf16*)g.X + ((int64_t)(m_blk * MT) * (K >> 5) + (kbase >> 5)) * 512 + lane * 8;
+  // row-major X (bf16): lane reads row 16t + lane%16 (rows past M repeat row
+  // M-1), columns 8*(lane/16) .. +7 of each 32-column K-step
+  const bf16* xr[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    xr[t] = (const bf16*)g.X + (int64_t)min(m_blk * 16 * MT + 16 * t + (lane & 15), g.M - 1) * g.ldx + kbase +
+            8 * (lane >> 4);
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
@@ -90,7 +97,9 @@ __device__ __forceinline__ void gemm_accumulate_wide(int n_blk, int kc, int m_bl
 #pragma unroll
         for (int c = 0; c < NT; ++c) wv[c][i] = *(const bf16x8*)(wp + c * tile + 512 * (b0 + i));
 #pragma unroll
-        for (int t = 0; t < MT; ++t) xv[t][i] = *(const bf16x8*)(xp + t * tile + 512 * (b0 + i));
+        for (int t = 0; t < MT; ++t)
+          xv[t][i] = XM == GK_X_PACKED ? *(const bf16x8*)(xp + t * tile + 512 * (b0 + i))
+                                       : *(const bf16x8*)(xr[t] + 32 * (b0 + i));
       }
 #pragma unroll
     for (int i = 0; i < KB; ++i)
@@ -124,14 +133,14 @@ __device__ __forceinline__ void gemm_accumulate_wide(int n_blk, int kc, int m_bl
 // gemm_finish_kernel in a second launch; measured on W^O at 64 rows (8
 // chunks) this is 10% faster than the in-launch finish, whose every workgroup
 // waits for its write-through stores.
-template <int MT, int NT, typename YT>
+template <int MT, int NT, int XM, typename YT>
 __global__ void __launch_bounds__(256) gemm_wide_kernel(GemmArgs g, GemmOut o) {
   constexpr int ROWS = 16 * MT, COLS = 16 * NT, PAIRS = 8 * NT, LD = COLS + 1;
   __shared__ float red[ROWS * LD];
   const int ntw = g.N / COLS;
   const int bid = blockIdx.x, tid = threadIdx.x;
   const int kc = bid % g.S, n_blk = (bid / g.S) % ntw, m_blk = bid / (g.S * ntw);
-  gemm_accumulate_wide<MT, NT, GW_KB>(n_blk, kc, m_blk, g, red);
+  gemm_accumulate_wide<MT, NT, GW_KB, XM>(n_blk, kc, m_blk, g, red);
   if (g.S == 1) {
     for (int q = tid; q < ROWS * PAIRS; q += 256) {
       const int r = q / PAIRS, cp = q % PAIRS;
@@ -215,7 +224,12 @@ void launch_bf16(const GemmArgs& g, const GemmOut& o, int64_t grid, hipStream_t 
 
 template <int MT, typename YT>
 void launch_wide(const GemmArgs& g, const GemmOut& o, int64_t grid, hipStream_t s) {
-  gemm_wide_kernel<MT, GW_NT, YT><<<dim3((unsigned)grid), 256, 0, s>>>(g, o);
+  bool rows = false;
+  if constexpr (MT == 2) {
+    rows = g.x_rows != 0;
+    if (rows) gemm_wide_kernel<MT, GW_NT, GK_X_ROWS, YT><<<dim3((unsigned)grid), 256, 0, s>>>(g, o);
+  }
+  if (!rows) gemm_wide_kernel<MT, GW_NT, GK_X_PACKED, YT><<<dim3((unsigned)grid), 256, 0, s>>>(g, o);
   if (g.S > 1) {
     const int64_t pairs = (int64_t)g.M * (g.N / 2);
     gemm_finish_kernel<YT><<<dim3((unsigned)((pairs + 255) / 256)), 256, 0, s>>>(g, o);
@@ -262,7 +276,8 @@ hipError_t launch_gemm(const GemmArgs& g, const GemmOut& o, bool f32_weights, bo
     if (g.seg_end[i] % cols != 0) return hipErrorInvalidValue;
   const int64_t tiles = (int64_t)(g.N / cols) * ((g.M + 16 * mt - 1) / (16 * mt));
   if (g.N % cols != 0 || g.S < 1 || g.S > GK_S_MAX || g.K % (g.S * 128) != 0 ||
-      (g.S > 1 && tiles > SPLITK_COUNTERS) || (mt > 1 && !gemm_x_packed(g.M)))
+      (g.S > 1 && tiles > SPLITK_COUNTERS) || (mt > 1 && !gemm_x_packed(g.M)) ||
+      (g.x_rows && (x_f32 || !gemm_x_rows_wide(g.M))))
     return hipErrorInvalidValue;
   const int64_t grid = (int64_t)g.S * tiles;
   if (mt == 1)

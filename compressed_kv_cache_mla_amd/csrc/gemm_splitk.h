@@ -67,6 +67,7 @@ struct GemmArgs {
   int32_t S;          // K chunks, <= GK_S_MAX; K % (S * 128) == 0
   float* part;        // [S, M, N] fp32 chunk sums (S > 1)
   int32_t* counters;  // [ceil(M / (16 MT)), N / 16], zero before the first in-launch finish
+  int32_t x_rows;     // wide kernel: bf16 X read row-major (row stride ldx) although M > 8
 };
 
 // Segment of output column n: its first column and its weight matrix.
@@ -300,6 +301,10 @@ inline int gemm_nt(int32_t M) { return gemm_mt(M) == 1 ? 1 : GW_NT; }
 // tile) up to this many rows and packed above it.
 constexpr int GK_ROWS_MAX = 8;
 inline bool gemm_x_packed(int32_t M) { return M > GK_ROWS_MAX; }
+// bf16 activations of 17..32 rows are read row-major by the wide kernel
+// (measured on the query product at 32 rows: 3 us less than packing them in a
+// launch of its own; above 32 rows the packed layout wins).
+inline bool gemm_x_rows_wide(int32_t M) { return M > 16 && M <= 32; }
 // Rows of a packed activation buffer.
 inline int64_t gemm_rows_padded(int32_t M) { return ((int64_t)M + 63) / 64 * 64; }
 

@@ -272,24 +272,27 @@ namespace {
 struct QueryPlan {
   bool lowrank, packed;
   int32_t N1, S1, N2, S2;
+  bool pack_h;   // h packed by a launch of its own (else read row-major, or rows <= 8)
   size_t off_h, off_cq, off_part, total;
 };
 
 // Workspace: split-K tile counters (fixed offset 0), h packed (bf16, more
-// than a few rows), c^Q (packed like h, else row-major), then the chunk sums
+// than a few rows, except 17..32 rows, read row-major), c^Q (packed above a
+// few rows, else row-major), then the chunk sums
 // (shared by the two products, which run one after the other).
 QueryPlan query_plan(const mla_dims& d, int32_t B, int32_t d_cq) {
   QueryPlan p{};
   const bool bf = d.dtype == MLA_BF16;
   p.lowrank = d_cq > 0;
   p.packed = bf && mla::gemm_x_packed(B);
+  p.pack_h = p.packed && !mla::gemm_x_rows_wide(B);
   const int64_t rows = p.packed ? mla::gemm_rows_padded(B) : B;
   p.N1 = (p.lowrank ? d_cq : d.n_h * mla::D_H) + d.n_h * mla::D_R;
   p.S1 = bf ? mla::gemm_pick_splits(B, p.N1, d.d_model) : 1;
   p.N2 = p.lowrank ? d.n_h * mla::D_H : 0;
   p.S2 = bf && p.lowrank ? mla::gemm_pick_splits(B, p.N2, d_cq) : 1;
   p.off_h = mla::SPLITK_COUNTER_BYTES;
-  p.off_cq = p.off_h + (p.packed ? mla::align256((size_t)rows * d.d_model * 2) : 0);
+  p.off_cq = p.off_h + (p.pack_h ? mla::align256((size_t)rows * d.d_model * 2) : 0);
   p.off_part = p.off_cq + (p.lowrank ? mla::align256((size_t)rows * d_cq * (bf ? 2 : 4)) : 0);
   const size_t part = std::max(mla::gemm_part_bytes(B, p.N1, p.S1), p.lowrank ? mla::gemm_part_bytes(B, p.N2, p.S2) : 0);
   p.total = p.off_part + (bf ? part : 0);
@@ -391,11 +394,12 @@ mla_status mla_query_project(const mla_dims* dims, int32_t B, int32_t d_cq, cons
   const int64_t rows = mla::gemm_rows_padded(B);
   hipError_t e = hipSuccess;
   const void* X1 = h;
-  if (p.packed) {
+  if (p.pack_h) {
     e = mla::launch_pack(h, dims->d_model, B, rows, dims->d_model, false, false, ws + p.off_h, s);
     X1 = ws + p.off_h;
   }
   mla::GemmArgs g = gemm_args(X1, dims->d_model, B, dims->d_model, ws);
+  g.x_rows = p.packed && !p.pack_h;
   mla::GemmOut o{};
   if (p.lowrank)
     gemm_segments(g, o, {{W_DQ, d_cq, c_Q, p.packed ? -(int64_t)d_cq : d_cq}, {W_QR, nr, q_R, nr}});

@@ -175,7 +175,7 @@ def _splits(M, N, K):
 
 @pytest.mark.parametrize("B,d_cq,n_h,d_model", [(32, 1536, 128, 5120), (64, 1536, 128, 5120), (1, 512, 16, 1024),
                                                 (5, 256, 16, 1024), (40, 0, 16, 1024), (300, 1536, 128, 5120),
-                                                (9, 128, 16, 1024)])
+                                                (9, 128, 16, 1024), (17, 256, 16, 1024), (33, 256, 16, 1024)])
 def test_query_project_workspace_size(B, d_cq, n_h, d_model):
     L = mla.lib()
     d = _dims(n_h=n_h, d_model=d_model)
@@ -187,7 +187,7 @@ def test_query_project_workspace_size(B, d_cq, n_h, d_model):
         part = max(part, S2 * B * n_h * 128 * 4 if S2 > 1 else 0)
     packed = B > 8                         # activations packed above 8 rows, padded to 64
     rows = (B + 63) // 64 * 64 if packed else B
-    h = _a256(rows * d_model * 2) if packed else 0
+    h = _a256(rows * d_model * 2) if packed and not 16 < B <= 32 else 0   # 17..32 rows: h read row-major
     cq = _a256(rows * d_cq * 2)
     assert L.mla_query_project_workspace_size(ctypes.byref(d), B, d_cq) == COUNTER_BYTES + h + cq + _a256(part)
     f = _dims(n_h=n_h, d_model=d_model, dtype=mla.MLA_FP32)

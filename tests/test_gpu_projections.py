@@ -10,8 +10,9 @@ Tolerance as for the decode: max|gpu - oracle| / max|oracle| <= 1e-2 (bf16),
 <= 1e-5 (fp32).  Inputs come from the seeded generator, regenerated on the CPU
 for the oracle; weights ~ N(0, 1/fan_in), h ~ N(0, 1), o ~ N(0, 1).  Shapes
 cover the DeepSeek-V2 sizes (n_h = 128, d_model = 5120, d_cq = 1536) at the
-decode batches 32 and 64, split and unsplit products, ragged row blocks, and
-two calls in a row on one workspace (the split-K counters are reset).
+decode batches 32 and 64, split and unsplit products, ragged row blocks, row-major and packed
+activations, and two calls in a row on one workspace (the split-K counters
+are reset).
 """
 import numpy as np
 import pytest
@@ -92,6 +93,7 @@ QUERY_CASES = [
     (3, 1024, 16, 128, torch.bfloat16),
     (8, 1024, 16, 128, torch.bfloat16),       # last row-major batch
     (9, 1024, 16, 128, torch.bfloat16),       # first packed batch (16-row tiles)
+    (20, 1024, 16, 256, torch.bfloat16),      # 32-row tile, h read row-major (rows past 20 repeat row 19)
     (33, 1024, 16, 256, torch.bfloat16),      # 64-row tiles, one ragged
     (100, 1024, 16, 256, torch.bfloat16),     # two 64-row blocks, the second ragged
     (1, 1024, 16, 512, torch.float32),
