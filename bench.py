@@ -288,7 +288,7 @@ def main():
                          "byte counters of rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not part of it "
+        print("bench.py: the library and this benchmark run on one GPU; multi-GPU runs are not supported "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
