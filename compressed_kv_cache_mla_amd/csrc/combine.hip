@@ -14,7 +14,7 @@
 // bf16 (MFMA): workgroup (head h, 16 sequences), one wave per sequence; the
 // combined latents are rounded to bf16 in LDS and o^T[d][b] = W^UV_h[d][:] .
 // O~[b][:] runs as v_mfma_f32_16x16x32_bf16 (M = d, N = sequence, K = latent).
-#include "mla_common.h"
+#include "gemm_splitk.h"
 
 namespace mla {
 namespace {
@@ -148,7 +148,8 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
                                                             int32_t G, const float* __restrict__ part_ml,
                                                             const bf16* __restrict__ part_o,
                                                             const bf16* __restrict__ W_UV, float* __restrict__ out,
-                                                            float* __restrict__ lse, int32_t* merge_flags) {
+                                                            float* __restrict__ lse, int32_t* merge_flags,
+                                                            bf16* __restrict__ out_packed) {
   constexpr int NBQ = CS / 16;
   constexpr int CB = CB_MAX;
   constexpr bool PRE = CS == 16;   // registers allow the W^UV prefetch with one accumulator block
@@ -242,6 +243,15 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
       f32x4 v = acc[j];
       if (empty_l[bb]) v = f32x4{0.f, 0.f, 0.f, 0.f};
       *(f32x4*)(out + ((int64_t)(b0 + bb) * n_h + h) * D_H + 16 * wave + 4 * (lane >> 4)) = v;
+      if (out_packed) {
+        // the same 4 values rounded to bf16, in the packed activation layout
+        // of the output projection (row b0 + bb, columns h*d_h + ...: 4
+        // consecutive elements of one lane group)
+        bf16x4 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[i] = (bf16)v[i];
+        *(bf16x4*)(out_packed + packed_index(b0 + bb, h * D_H + 16 * wave + 4 * (lane >> 4), (int64_t)n_h * D_H)) = pb;
+      }
     }
   }
 }
@@ -250,7 +260,8 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
 
 hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, int32_t n_splits,
                           const float* part_ml, const void* part_o, const void* W_UV, float* out,
-                          float* lse, int32_t* merge_flags, hipStream_t s) {
+                          float* lse, int32_t* merge_flags, void* out_packed, hipStream_t s) {
+  bf16* op = d.dtype == MLA_BF16 ? (bf16*)out_packed : nullptr;
   if (d.dtype == MLA_FP32) {
     dim3 grid(d.n_h, (B + CB_SEQ - 1) / CB_SEQ);
     combine_f32_kernel<<<grid, 256, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const float*)part_o,
@@ -262,15 +273,15 @@ hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, i
     if (B > 32 && d.n_h * ((B + 63) / 64) >= 512) {
       dim3 grid(d.n_h, (B + 63) / 64);
       combine_mfma_kernel<64><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
-                                                    (const bf16*)W_UV, out, lse, merge_flags);
+                                                    (const bf16*)W_UV, out, lse, merge_flags, op);
     } else if (B > 16 && d.n_h * ((B + 31) / 32) >= 256) {
       dim3 grid(d.n_h, (B + 31) / 32);
       combine_mfma_kernel<32><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
-                                                    (const bf16*)W_UV, out, lse, merge_flags);
+                                                    (const bf16*)W_UV, out, lse, merge_flags, op);
     } else {
       dim3 grid(d.n_h, (B + 15) / 16);
       combine_mfma_kernel<16><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
-                                                    (const bf16*)W_UV, out, lse, merge_flags);
+                                                    (const bf16*)W_UV, out, lse, merge_flags, op);
     }
   }
   return hipGetLastError();

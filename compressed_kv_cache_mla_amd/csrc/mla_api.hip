@@ -145,6 +145,7 @@ struct StepAppendIn {
   const void* h_new;
   const void* W_DKV;
   const void* W_KR;
+  void* o_packed;   // optional: the combine also writes out as the output projection's packed bf16 activations
 };
 
 static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
@@ -229,7 +230,7 @@ static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, 
   if (e == hipSuccess && opts && opts->ev_stop) e = hipEventRecord((hipEvent_t)opts->ev_stop, s);
   if (e == hipSuccess)
     e = mla::launch_combine(*dims, B, prefix, n_splits, part_ml, part_o, W_UV, out, lse,
-                            step || merge_append_flags ? flags : nullptr, s);
+                            step || merge_append_flags ? flags : nullptr, step ? step->o_packed : nullptr, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -255,7 +256,7 @@ mla_status mla_decode_step(const mla_dims* dims, int32_t B, const void* h_new, c
                            const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, float* out,
                            float* lse, void* workspace, size_t ws_bytes, int32_t n_splits,
                            const mla_decode_opts* opts, void* stream) {
-  const StepAppendIn in{h_new, W_DKV, W_KR};
+  const StepAppendIn in{h_new, W_DKV, W_KR, nullptr};
   return decode_impl(dims, B, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride, num_pages, page_table, max_pages,
                      seq_lens, out, lse, workspace, ws_bytes, n_splits, opts, &in, stream);
 }
@@ -425,8 +426,12 @@ size_t mla_output_project_workspace_size(const mla_dims* dims, int32_t B) {
   return output_plan(*dims, B).total;
 }
 
-mla_status mla_output_project(const mla_dims* dims, int32_t B, const float* o, const void* W_O, float* u,
-                              void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// o_prepacked: o's packed bf16 copy is already in the workspace (written by the
+// combine of the decode layer), so the pack launch is skipped.
+static mla_status output_project_impl(const mla_dims* dims, int32_t B, const float* o, const void* W_O, float* u,
+                                      void* workspace, size_t ws_bytes, void* stream, bool o_prepacked) {
   mla_status st = check_query_dims(dims, B, 0);
   if (st != MLA_OK) return st;
   if (!o || !W_O || !u || !workspace) return fail(MLA_ERR_INVALID_ARG, "null pointer among o, W_O, u, workspace");
@@ -442,7 +447,7 @@ mla_status mla_output_project(const mla_dims* dims, int32_t B, const float* o, c
   hipError_t e = hipSuccess;
   const void* X = o;
   if (p.packed) {
-    e = mla::launch_pack(o, K, B, mla::gemm_rows_padded(B), K, true, true, ws + p.off_o, s);
+    if (!o_prepacked) e = mla::launch_pack(o, K, B, mla::gemm_rows_padded(B), K, true, true, ws + p.off_o, s);
     X = ws + p.off_o;
   }
   mla::GemmArgs g = gemm_args(X, K, B, K, ws);
@@ -453,6 +458,13 @@ mla_status mla_output_project(const mla_dims* dims, int32_t B, const float* o, c
   if (e == hipSuccess) e = mla::launch_gemm(g, out, f32, true, true, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "output projection launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+extern "C" {
+
+mla_status mla_output_project(const mla_dims* dims, int32_t B, const float* o, const void* W_O, float* u,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  return output_project_impl(dims, B, o, W_O, u, workspace, ws_bytes, stream, false);
 }
 
 mla_status mla_pack_weight(const mla_dims* dims, int32_t rows, int32_t K, const void* W, void* W_packed,
@@ -587,12 +599,16 @@ mla_status mla_decode_layer(const mla_dims* dims, int32_t B, int32_t d_cq, const
   if (ws_bytes < L.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   char* ws = (char*)workspace;
   st = mla_query_project(dims, B, d_cq, h, W_DQ, W_UQ, W_QR, ws + L.qc, ws + L.qr, ws + L.q, L.qc - L.q, stream);
+  // the step's combine also leaves o packed (bf16) where the output
+  // projection reads it, which saves that projection's pack launch
+  const OutputPlan op = output_plan(*dims, B);
+  const StepAppendIn in{h, W_DKV, W_KR, op.packed ? ws + L.out + op.off_o : nullptr};
   if (st == MLA_OK)
-    st = mla_decode_step(dims, B, h, W_DKV, W_KR, ws + L.qc, ws + L.qr, pos_q, W_UK, W_UV, c_KV, k_R, row_stride,
-                         num_pages, page_table, max_pages, seq_lens, (float*)(ws + L.o), lse, workspace, L.q, n_splits,
-                         opts, stream);
+    st = decode_impl(dims, B, ws + L.qc, ws + L.qr, pos_q, W_UK, W_UV, c_KV, k_R, row_stride, num_pages, page_table,
+                     max_pages, seq_lens, (float*)(ws + L.o), lse, workspace, L.q, n_splits, opts, &in, stream);
   if (st == MLA_OK)
-    st = mla_output_project(dims, B, (const float*)(ws + L.o), W_O, u, ws + L.out, L.total - L.out, stream);
+    st = output_project_impl(dims, B, (const float*)(ws + L.o), W_O, u, ws + L.out, L.total - L.out, stream,
+                             op.packed);
   return st;
 }
 

@@ -280,5 +280,5 @@ hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, co
 // append's flags, to be OR-ed into word 0 and cleared.
 hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, int32_t n_splits,
                           const float* part_ml, const void* part_o, const void* W_UV, float* out,
-                          float* lse, int32_t* merge_flags, hipStream_t s);
+                          float* lse, int32_t* merge_flags, void* out_packed, hipStream_t s);
 }  // namespace mla
