@@ -9,14 +9,19 @@ resident in HBM before timing starts.  To keep the 256 MB Infinity Cache from
 serving repeated reads, steps rotate over several independent copies of the
 workload (own weights, queries and cache) whose total size exceeds it.
 
-Prints one JSON line.  `value` is decode tokens/s (B sequences per step);
+Prints one JSON line.  The headline workload is batch 64 at 8K context
+(b64_l8192); `value` is its decode tokens/s (B sequences per step);
 `roofline` is computed for the split-KV attention kernel from its algorithmic
-bytes and its HIP-event duration measured in the timed region; `projections`
-times the query path (W^DQ, W^UQ, W^QR) and the output projection W^O, which
-sit outside the step, at the same batch sizes; `prefill` times chunked
-prefill (new tokens attending causally over their sequences); `layer` times
-the whole attention layer (query path + step + W^O, h -> u); `cpu_baseline`
-times the fp64 CPU oracle on a bounded sample of the same workload.
+bytes and its HIP-event duration measured in the timed region; `configs`
+repeats the measurement on the other single-layer decode configurations
+(batch 32 at 4K, batch 64 ragged over permuted pages, batch 4 at 128K);
+`l60` times the 60-layer configuration (batch 128 at 8K, every layer's
+append + decode) as one captured HIP graph; `projections` times the query
+path (W^DQ, W^UQ, W^QR) and the output projection W^O, which sit outside the
+step; `prefill` times chunked prefill (new tokens attending causally over
+their sequences); `layer` times the whole attention layer (query path + step
++ W^O, h -> u); `cpu_baseline` times the fp64 CPU oracle on one whole decode
+step of the headline workload.
 """
 from __future__ import annotations
 
@@ -229,39 +234,139 @@ def measure_prefill(torch, mla, B: int, L: int, T: int, n_h: int = 128, d_model:
             "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
 
 
-def cpu_baseline(wl, seconds: float):
-    """The fp64 oracle (absorbed form) doing the same per-sequence work as a
-    step -- append the newest token, then decode -- on a bounded sample."""
-    import numpy as np
-    import oracle
+def _host_threads():
+    """Threads the fp64 oracle's BLAS calls use, and the host's CPU counts."""
     from threadpoolctl import threadpool_info
-    sample = [0, 1]
-    prepared = []
-    for b in sample:
-        d = wl.oracle_inputs(b)
-        n = d["n"]
-        if "h" in d:
-            c, kR = oracle.down_project(d["h"][:n - 1], d["W_DKV"], d["W_KR"], np.arange(n - 1), wl.dims.rope_base)
-            h_new = d["h"][n - 1:]
-        else:
-            c, kR, h_new = d["prior_c"], d["prior_kR"], d["h_new"]
-        prepared.append((d, c, kR, h_new))
-    done, t0 = 0, time.perf_counter()
-    while True:
-        for d, c, kR, h_new in prepared:
-            n = d["n"]
-            c1, k1 = oracle.down_project(h_new, d["W_DKV"], d["W_KR"], np.array([n - 1]), wl.dims.rope_base)
-            oracle.attend_absorbed(d["q_C"], d["q_R"], n - 1, np.concatenate([c, c1]), np.concatenate([kR, k1]),
-                                   d["W_UK"], d["W_UV"], wl.dims.rope_base, wl.dims.scale)
-            done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    n0 = int(wl.n[0])
-    return {"value": done / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 absorbed-form oracle, append + decode of sequences {sample} ({n0} cached tokens, "
-                      f"n_h={wl.cfg.n_h}) repeated {done} times in {el:.1f} s; 1 decode token per sequence"}
+    return threads, os.cpu_count(), len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(W, name: str, seconds: float, step_us_gpu: float | None = None):
+    """The fp64 oracle as it stands, timed on the host on the work of one
+    decode step of workload `name`: for every sequence b, append its newest
+    token (oracle.down_project) and decode it (oracle.attend_absorbed) over
+    n_b cached rows.  Its inputs are one sequence's regenerated seeded inputs
+    (queries, W^DKV, W^KR, W^UK, W^UV, the newest token's h) and n_max
+    seeded N(0, 1) latent rows (numpy PCG64), each sequence of the batch
+    taking the first n_b of them: the oracle's cost depends only on the
+    shapes.  Steps are repeated while the time budget lasts (at least one);
+    value = B / median step time.  reconstruct: the definition (K and V
+    rebuilt per head) on one sequence of the workload for two heads, reported
+    per cached token and head."""
+    import oracle
+    cfg = W.CONFIGS[name]
+    L = cfg.context_lengths()
+    n = (L + 1).astype(np.int64)
+    n_max = int(n.max())
+    wl_cpu = W.Workload.__new__(W.Workload)     # generator side only: no device tensors
+    wl_cpu.cfg, wl_cpu.layer = cfg, 0
+    import torch
+    cpu = torch.device("cpu")
+    f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    W_UK = f64(wl_cpu._W_UK(device=cpu))
+    W_UV = f64(wl_cpu._w("W_UV", cfg.n_h * 128, 512, 512, device=cpu))
+    W_DKV = f64(wl_cpu._w("W_DKV", 512, cfg.d_model, cfg.d_model, device=cpu))
+    W_KR = f64(wl_cpu._w("W_KR", 64, cfg.d_model, cfg.d_model, device=cpu))
+    q_C = f64(wl_cpu._q_rows("q_C", range(cfg.n_h), 128, cpu))
+    q_R = f64(wl_cpu._q_rows("q_R", range(cfg.n_h), 64, cpu))
+    h_new = f64(wl_cpu.h_rows(range(1), device=cpu))
+    rng = np.random.default_rng(cfg.seed)
+    c_all = rng.standard_normal((n_max, 512))
+    k_all = rng.standard_normal((n_max, 64))
+    base, scale = 10000.0, 1.0 / math.sqrt(192.0)
+    threads, nproc, affinity = _host_threads()
+
+    def step():
+        for b in range(cfg.B):
+            nb = int(n[b])
+            c1, k1 = oracle.down_project(h_new, W_DKV, W_KR, np.array([nb - 1]), base)
+            c = c_all[:nb].copy()
+            k = k_all[:nb].copy()
+            c[nb - 1:], k[nb - 1:] = c1, k1
+            oracle.attend_absorbed(q_C, q_R, nb - 1, c, k, W_UK, W_UV, base, scale)
+
+    times, t_end = [], time.perf_counter() + seconds
+    while True:
+        t0 = time.perf_counter()
+        step()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() + times[-1] > t_end or len(times) >= 5:
+            break
+    t_step = float(np.median(times))
+    # the definition: per-head K, V rebuilt from the latent
+    nr = min(n_max, 8193)
+    t0 = time.perf_counter()
+    oracle.attend_reconstruct(q_C, q_R, nr - 1, c_all[:nr], k_all[:nr], W_UK, W_UV, base, scale, heads=[0, 1])
+    t_rec = time.perf_counter() - t0
+    res = {"value": round(cfg.B / t_step, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"fp64 absorbed-form oracle on the whole of one decode step of {name} "
+                     f"(B={cfg.B}, {int(n.sum())} cached tokens, n_h={cfg.n_h}): append of each newest token "
+                     f"then decode; {len(times)} step(s), median {t_step:.2f} s; inputs: one sequence's seeded "
+                     f"queries and weights and {n_max} seeded latent rows shared by the batch",
+           "step_s": round(t_step, 3), "steps_timed": len(times), "host_nproc": nproc, "host_affinity": affinity,
+           "reconstruct": {"us_per_cached_token_per_head": round(1e6 * t_rec / (nr * 2), 3),
+                           "tokens_per_s_all_heads": round(1.0 / (t_rec / 2 * cfg.n_h), 4),
+                           "sample": f"oracle.attend_reconstruct, one sequence of {nr} cached tokens, 2 heads, "
+                                     f"{t_rec:.2f} s; tokens/s extrapolated to n_h={cfg.n_h}"}}
+    if step_us_gpu:
+        res["gpu_over_cpu"] = round(t_step / (step_us_gpu * 1e-6), 1)
+    return res
+
+
+def measure_l60(torch, mla, W, steps: int, warmup: int, n_splits: int = 0):
+    """The 60-layer configuration: B = 128 sequences of 8192 prior tokens, 60
+    layers with their own seeded weights, queries and latent caches (72.5 GB
+    of cache in all), one step = for every layer the append of each
+    sequence's newest token and the decode (mla_decode_step).  The 60 layer
+    steps are captured once in a HIP graph (three kernel launches per layer,
+    no memset nodes) and the graph is replayed; each replay is timed with
+    fence-free HIP events.  value: B / step time."""
+    cfg = W.CONFIGS["l60_b128_l8192"]
+    t0 = time.perf_counter()
+    layers = []
+    for i in range(cfg.layers):
+        wl = W.Workload(W.scaled(cfg, layers=1), layer=i, n_splits=n_splits)
+        wl.step()          # creates the zero-filled step workspace outside the capture
+        layers.append(wl)
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+    alg = [algorithmic(wl) for wl in layers]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for wl in layers:  # one eager pass on the capture stream first
+            wl.step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref_out = layers[-1].out.clone()
+    with torch.cuda.graph(g):
+        for wl in layers:
+            wl.step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(layers[-1].out, ref_out))
+    evs = [(mla.HipEvent(), mla.HipEvent()) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    us = [1e3 * a.elapsed_ms(b) for a, b in evs]
+    t = float(np.median(us))
+    step_bytes = sum(a["step_bytes"] for a in alg)
+    cache = sum(a["cache"] for a in alg)
+    res = {"workload": cfg.name, "B": cfg.B, "layers": cfg.layers, "cached_tokens_per_layer": alg[0]["N"],
+           "us_per_step_p10_p50_p90": [round(float(x), 1) for x in np.percentile(us, [10, 50, 90])],
+           "tokens_per_s": round(cfg.B / (t * 1e-6), 1), "alg_GB_per_step": round(step_bytes / 1e9, 2),
+           "cache_GB": round(cache / 1e9, 2), "step_GBps": round(step_bytes / (t * 1e-6) / 1e9, 1),
+           "step_hbm_frac": round(step_bytes / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+           "graph": "60 layer steps, 180 kernel nodes, captured once", "replay_equals_eager": same,
+           "build_s": round(build_s, 1)}
+    del layers, g
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -269,20 +374,24 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="b32_l4096")
-    ap.add_argument("--target-workload", default="b64_l8192",
-                    help="second workload reported under target_shape ('' to skip)")
+    ap.add_argument("--workload", default="b64_l8192",
+                    help="headline workload (default: batch 64, 8K context, the shape the target is stated on)")
+    ap.add_argument("--configs", default="b32_l4096,b64_ragged,b4_l131072",
+                    help="comma-separated workloads timed the same way under `configs` ('' to skip)")
+    ap.add_argument("--no-l60", action="store_true", help="skip the 60-layer configuration (HIP graph)")
     ap.add_argument("--copies", type=int, default=0, help="workload copies to rotate over (0 = enough to exceed "
                                                          "the 256 MB Infinity Cache twice)")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--impl", type=int, default=0, help="0 = MFMA attention kernel, 1 = VALU reference kernel")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-projections", action="store_true", help="skip the query / output projection timings")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the next rows' timings (query / output projections, prefill, whole layer)")
     ap.add_argument("--prefill-only", action="store_true", help="only time the chunked prefill configurations")
     ap.add_argument("--layer-only", default="", help="comma-separated workloads: only time the whole decode layer")
     ap.add_argument("--projections-only", default="",
                     help="comma-separated batch sizes: only time the query / output projections at them")
+    ap.add_argument("--l60-only", action="store_true", help="only time the 60-layer configuration")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM "
                          "byte counters of rocprofv3)")
@@ -314,10 +423,14 @@ def main():
         print(json.dumps({f"B{b}": measure_projections(torch, mla, int(b))
                           for b in args.projections_only.split(",")}), flush=True)
         return
+    if args.l60_only:
+        print(json.dumps({"l60": measure_l60(torch, mla, W, args.steps, args.warmup, args.splits)}), flush=True)
+        return
 
     def measure(name, steps, warmup):
         """Build rotating copies of a workload, run warmup + timed steps;
-        returns (first workload, copies, ms per step, attention-kernel us, wall s)."""
+        returns (first workload, algorithmic sizes, copies, ms per step,
+        mean attention-kernel us, wall s, percentiles)."""
         cfg = W.CONFIGS[name]
         if cfg.layers > 1:
             cfg = W.scaled(cfg, layers=1)
@@ -363,8 +476,20 @@ def main():
         step_us = [1e3 * sev[i].elapsed_ms(sev[i + 1]) for i in range(steps)]
         dist = {"step_us_p10_p50_p90": [round(float(x), 2) for x in np.percentile(step_us, [10, 50, 90])],
                 "kernel_us_p10_p50_p90": [round(float(x), 2) for x in np.percentile(kern_us, [10, 50, 90])]}
+        del wls
         return (first, alg, copies, t_start.elapsed_time(t_stop) / steps, sum(kern_us) / len(kern_us), wall,
                 dist)
+
+    def counter_traffic(name):
+        """HBM bytes per attention launch from the committed rocprofv3 counter
+        passes, if they were taken on the current kernel source."""
+        if not os.path.exists(COUNTERS) or args.impl != 0:
+            return None
+        cnt = json.load(open(COUNTERS))
+        rec = cnt.get("workloads", {}).get(name)
+        if rec and cnt.get("kernel_source_sha256_16") == kernel_source_hash():
+            return rec["hbm_bytes_per_launch"]
+        return None
 
     first, alg, copies, ms_per_step, kern_us, wall, dist = measure(args.workload, args.steps, args.warmup)
     copy_gbps = measured_copy_gbps(torch)
@@ -372,12 +497,8 @@ def main():
     B = cfg.B
     value = B / (ms_per_step * 1e-3)
     achieved = alg["attn_bytes"] / (kern_us * 1e-6) / 1e9
-    traffic = None
-    if os.path.exists(COUNTERS):
-        cnt = json.load(open(COUNTERS))
-        rec = cnt.get("workloads", {}).get(cfg.name)
-        if rec and cnt.get("kernel_source_sha256_16") == kernel_source_hash() and args.impl == 0:
-            traffic = rec["hbm_bytes_per_launch"]
+    del first
+    torch.cuda.empty_cache()
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -385,11 +506,11 @@ def main():
         "config": {"workload": cfg.name, "B": B, "context_tokens_per_seq": int(cfg.lens) if not isinstance(
             cfg.lens, (tuple, list)) else list(cfg.lens), "cached_tokens": alg["N"], "n_h": cfg.n_h, "d_h": 128,
                    "d_c": 512, "d_hR": 64, "d_model": cfg.d_model, "page_size": cfg.page_size,
-                   "copies_rotated": copies, "n_splits": args.splits or first.mla.cu_count()},
+                   "copies_rotated": copies, "n_splits": args.splits or mla.cu_count()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": counter_traffic(cfg.name),
                      "kernel": "split-KV attention (decode_mfma_kernel)" if args.impl == 0 else "decode_simple_kernel",
-                     "kernel_us": round(kern_us, 2),
+                     "alg_bytes_per_launch": alg["attn_bytes"], "kernel_us": round(kern_us, 2),
                      "mfma_tflops": round(alg["attn_flops"] / (kern_us * 1e-6) / 1e12, 1),
                      "mfma_frac": round(alg["attn_flops"] / (kern_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
                      "measured_copy_GBps": round(copy_gbps, 1),
@@ -400,28 +521,38 @@ def main():
         "step_hbm_frac": round(alg["step_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "wall_s_timed": round(wall, 4),
     }
-    if args.target_workload and args.target_workload != args.workload:
-        # the batch-64 / 8K-context decode shape the performance target is stated on
-        f2, a2, c2, ms2, k2, _, d2 = measure(args.target_workload, max(5, args.steps // 2), args.warmup)
-        res["target_shape"] = {
-            "workload": f2.cfg.name, "B": f2.cfg.B, "cached_tokens": a2["N"], "ms_per_step": round(ms2, 5),
+    print(f"# headline {cfg.name}: {ms_per_step * 1e3:.1f} us per step, attention {kern_us:.1f} us",
+          file=sys.stderr, flush=True)
+    # the other decode configurations, timed the same way
+    confs = {}
+    for name in [n for n in args.configs.split(",") if n and n != args.workload]:
+        f2, a2, c2, ms2, k2, _, d2 = measure(name, max(10, args.steps // 2), args.warmup)
+        confs[name] = {
+            "B": f2.cfg.B, "cached_tokens": a2["N"], "ms_per_step": round(ms2, 5),
             "tokens_per_s": round(f2.cfg.B / (ms2 * 1e-3), 1), "kernel_us": round(k2, 2),
             "hbm_frac": round(a2["attn_bytes"] / (k2 * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "mfma_frac": round(a2["attn_flops"] / (k2 * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "hbm_frac_of_measured_copy": round(a2["attn_bytes"] / (k2 * 1e-6) / 1e9 / copy_gbps, 4),
-            "copies_rotated": c2, **d2}
-    if not args.no_projections:
-        # rows past the attention step: the query path and W^O, at the batches reported above
-        res["projections"] = {f"B{b}": measure_projections(torch, mla, b) for b in
-                              sorted({B, res.get("target_shape", {}).get("B", B)})}
-    if not args.no_projections:
+            "step_hbm_frac": round(a2["step_bytes"] / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": counter_traffic(name), "copies_rotated": c2, **d2}
+        del f2
+        torch.cuda.empty_cache()
+        print(f"# {name}: {ms2 * 1e3:.1f} us per step, attention {k2:.1f} us", file=sys.stderr, flush=True)
+    if confs:
+        res["configs"] = confs
+    if not args.no_l60:
+        res["l60"] = measure_l60(torch, mla, W, max(5, args.steps // 4), 2, args.splits)
+        print(f"# l60: {res['l60']['us_per_step_p10_p50_p90'][1]:.0f} us per 60-layer step", file=sys.stderr,
+              flush=True)
+    if not args.no_extras:
+        # rows past the attention step: the query path and W^O at the headline batch
+        res["projections"] = {f"B{B}": measure_projections(torch, mla, B)}
         # the chunked-prefill row: new tokens attending causally over their sequences
-        res["prefill"] = [measure_prefill(torch, mla, *cfg) for cfg in PREFILL_CONFIGS]
-        # the whole attention layer (query path + decode step + W^O) at the step's workloads
-        res["layer"] = [measure_layer(torch, mla, W, n) for n in
-                        dict.fromkeys([cfg.name, res.get("target_shape", {}).get("workload", cfg.name)])]
+        res["prefill"] = [measure_prefill(torch, mla, *c) for c in PREFILL_CONFIGS]
+        # the whole attention layer (query path + decode step + W^O) at the headline workload
+        res["layer"] = [measure_layer(torch, mla, W, cfg.name)]
+        print("# extras done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(W, cfg.name, args.cpu_seconds, ms_per_step * 1e3)
     print(json.dumps(res), flush=True)
 
 

@@ -258,6 +258,26 @@ __device__ __forceinline__ float2 gemm_sum_pair(int m, int cp, const GemmArgs& g
 // atomic; the one that brings the count to S adds the chunks (system-scope
 // loads) and hands each column pair to epi(m, cp, x0, x1), then puts the
 // counter back to zero for the next launch.
+//
+// Ordering.  The hand-off is ordered by the hardware, not by release/acquire
+// operations (an agent-scope release or acquire on gfx950 writes back or
+// invalidates the whole L2 of the XCD, which made this launch several times
+// slower):
+//  1. the chunk sums are system-scope stores (global_store ... sc0 sc1), which
+//     write through every cache level and are acknowledged by the memory
+//     side, not by the XCD's L2;
+//  2. s_waitcnt vmcnt(0) waits for those acknowledgements (vmcnt counts
+//     stores on gfx9), and the barrier that follows makes every thread's
+//     stores complete before thread 0's counter update;
+//  3. the counter update is an atomic with a returned value; thread 0 uses
+//     that value, through LDS and a second barrier, to decide whether the
+//     workgroup finishes the tile, so no finishing load can issue before the
+//     count that includes all S chunks has been read;
+//  4. the finisher reads the sums with system-scope loads
+//     (global_load ... sc0 sc1), which miss in the L2 and read the memory side
+//     where step 1 left the values.
+// The bitwise tests of the fused decode step against the two-launch path
+// (whose kernel boundary orders everything) check this on the hardware.
 template <int MT = 2, class Epi>
 __device__ __forceinline__ void gemm_finish_tile(int n_blk, int m_blk, const GemmArgs& g, Epi&& epi,
                                                  int* lds_flag) {

@@ -371,9 +371,14 @@ size_t mla_query_project_workspace_size(const mla_dims* dims, int32_t B, int32_t
   return query_plan(*dims, B, d_cq).total;
 }
 
-mla_status mla_query_project(const mla_dims* dims, int32_t B, int32_t d_cq, const void* h, const void* W_DQ,
-                             const void* W_UQ, const void* W_QR, void* q_C, void* q_R, void* workspace,
-                             size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// counters: the split-K tile counters of the two products (SPLITK_COUNTER_BYTES
+// of zeros); the public entry point passes the block at offset 0 of its
+// workspace, the whole layer a block at a fixed offset of its own.
+static mla_status query_project_impl(const mla_dims* dims, int32_t B, int32_t d_cq, const void* h, const void* W_DQ,
+                                     const void* W_UQ, const void* W_QR, void* q_C, void* q_R, void* workspace,
+                                     size_t ws_bytes, void* stream, char* counters) {
   mla_status st = check_query_dims(dims, B, d_cq);
   if (st != MLA_OK) return st;
   if (!h || !W_UQ || !W_QR || !q_C || !q_R || !workspace)
@@ -399,7 +404,7 @@ mla_status mla_query_project(const mla_dims* dims, int32_t B, int32_t d_cq, cons
     e = mla::launch_pack(h, dims->d_model, B, rows, dims->d_model, false, false, ws + p.off_h, s);
     X1 = ws + p.off_h;
   }
-  mla::GemmArgs g = gemm_args(X1, dims->d_model, B, dims->d_model, ws);
+  mla::GemmArgs g = gemm_args(X1, dims->d_model, B, dims->d_model, counters ? counters : ws);
   g.x_rows = p.packed && !p.pack_h;
   mla::GemmOut o{};
   if (p.lowrank)
@@ -410,7 +415,7 @@ mla_status mla_query_project(const mla_dims* dims, int32_t B, int32_t d_cq, cons
   g.part = (float*)(ws + p.off_part);
   if (e == hipSuccess) e = mla::launch_gemm(g, o, f32, f32, f32, s);
   if (e == hipSuccess && p.lowrank) {
-    mla::GemmArgs g2 = gemm_args(c_Q, d_cq, B, d_cq, ws);
+    mla::GemmArgs g2 = gemm_args(c_Q, d_cq, B, d_cq, counters ? counters : ws);
     mla::GemmOut o2{};
     gemm_segments(g2, o2, {{W_UQ, nq, q_C, nq}});
     g2.S = p.S2;
@@ -421,6 +426,14 @@ mla_status mla_query_project(const mla_dims* dims, int32_t B, int32_t d_cq, cons
   return ok();
 }
 
+extern "C" {
+
+mla_status mla_query_project(const mla_dims* dims, int32_t B, int32_t d_cq, const void* h, const void* W_DQ,
+                             const void* W_UQ, const void* W_QR, void* q_C, void* q_R, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  return query_project_impl(dims, B, d_cq, h, W_DQ, W_UQ, W_QR, q_C, q_R, workspace, ws_bytes, stream, nullptr);
+}
+
 size_t mla_output_project_workspace_size(const mla_dims* dims, int32_t B) {
   if (check_query_dims(dims, B, 0) != MLA_OK) return 0;
   return output_plan(*dims, B).total;
@@ -429,9 +442,11 @@ size_t mla_output_project_workspace_size(const mla_dims* dims, int32_t B) {
 }  // extern "C"
 
 // o_prepacked: o's packed bf16 copy is already in the workspace (written by the
-// combine of the decode layer), so the pack launch is skipped.
+// combine of the decode layer), so the pack launch is skipped.  counters: as
+// for query_project_impl (NULL: the block at offset 0 of the workspace).
 static mla_status output_project_impl(const mla_dims* dims, int32_t B, const float* o, const void* W_O, float* u,
-                                      void* workspace, size_t ws_bytes, void* stream, bool o_prepacked) {
+                                      void* workspace, size_t ws_bytes, void* stream, bool o_prepacked,
+                                      char* counters = nullptr) {
   mla_status st = check_query_dims(dims, B, 0);
   if (st != MLA_OK) return st;
   if (!o || !W_O || !u || !workspace) return fail(MLA_ERR_INVALID_ARG, "null pointer among o, W_O, u, workspace");
@@ -450,7 +465,7 @@ static mla_status output_project_impl(const mla_dims* dims, int32_t B, const flo
     if (!o_prepacked) e = mla::launch_pack(o, K, B, mla::gemm_rows_padded(B), K, true, true, ws + p.off_o, s);
     X = ws + p.off_o;
   }
-  mla::GemmArgs g = gemm_args(X, K, B, K, ws);
+  mla::GemmArgs g = gemm_args(X, K, B, K, counters ? counters : ws);
   mla::GemmOut out{};
   gemm_segments(g, out, {{W_O, dims->d_model, u, dims->d_model}});
   g.S = p.S;
@@ -598,7 +613,11 @@ mla_status mla_decode_layer(const mla_dims* dims, int32_t B, int32_t d_cq, const
   const LayerWs L = layer_ws_layout(*dims, B, d_cq, n_splits);
   if (ws_bytes < L.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   char* ws = (char*)workspace;
-  st = mla_query_project(dims, B, d_cq, h, W_DQ, W_UQ, W_QR, ws + L.qc, ws + L.qr, ws + L.q, L.qc - L.q, stream);
+  // the projections' split-K counters sit at fixed offsets of the step's
+  // layout (the rest of the workspace moves with B)
+  const mla::DecodeWs D = mla::decode_ws_layout(B, dims->n_h, n_splits, (int)elt_size(dims), true);
+  st = query_project_impl(dims, B, d_cq, h, W_DQ, W_UQ, W_QR, ws + L.qc, ws + L.qr, ws + L.q, L.qc - L.q, stream,
+                          ws + D.q_cnt);
   // the step's combine also leaves o packed (bf16) where the output
   // projection reads it, which saves that projection's pack launch
   const OutputPlan op = output_plan(*dims, B);
@@ -608,7 +627,7 @@ mla_status mla_decode_layer(const mla_dims* dims, int32_t B, int32_t d_cq, const
                      max_pages, seq_lens, (float*)(ws + L.o), lse, workspace, L.q, n_splits, opts, &in, stream);
   if (st == MLA_OK)
     st = output_project_impl(dims, B, (const float*)(ws + L.o), W_O, u, ws + L.out, L.total - L.out, stream,
-                             op.packed);
+                             op.packed, ws + D.o_cnt);
   return st;
 }
 

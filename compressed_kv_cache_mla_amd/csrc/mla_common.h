@@ -91,11 +91,14 @@ constexpr int SPLIT_REC = 8;
 constexpr int APPEND_SK_SPLIT = 8;
 
 // Decode workspace layout (bytes, each part 256-aligned).  flags: word 0 the
-// decode's error flags, word 1 (decode step only) the append's; then the
-// split-K tile counters (used by the decode step's append).  The decode step
-// adds the split-K append's chunk sums.
+// decode's error flags, word 1 (decode step only) the append's; then three
+// blocks of split-K tile counters at fixed offsets: the decode step's append
+// (app_cnt), and the whole-layer entry point's query and output projections
+// (q_cnt, o_cnt).  Everything after them moves with the batch size; the
+// counters must not, because a workspace is zero-filled once and then reused
+// for any batch size.  The decode step adds the split-K append's chunk sums.
 struct DecodeWs {
-  size_t flags, prefix, splits, qabs, part_ml, part_o, app_part, app_cnt, total;
+  size_t flags, prefix, splits, qabs, part_ml, part_o, app_part, app_cnt, q_cnt, o_cnt, total;
   int32_t n_slots;
 };
 
@@ -103,9 +106,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Tile counters of in-launch split-K reductions.  A product is split only
 // while it has fewer tiles than fill the GPU (1024 workgroups), so 1024
-// counters serve any product; they sit at a fixed offset of every workspace
-// (right after the flags) and each completed launch leaves them at zero, so
-// a workspace zero-filled once stays valid for every batch size and for
+// counters serve any product; each block sits at a fixed offset of its
+// workspace (right after the flags of a decode workspace, at offset 0 of a
+// projection's) and each completed launch leaves them at zero, so a
+// workspace zero-filled once stays valid for every batch size and for
 // consecutive products.
 constexpr int SPLITK_COUNTERS = 1024;
 constexpr size_t SPLITK_COUNTER_BYTES = SPLITK_COUNTERS * 4;
@@ -116,6 +120,8 @@ inline DecodeWs decode_ws_layout(int32_t B, int32_t n_h, int32_t n_splits, int e
   size_t off = 0;
   w.flags = off;   off += 256;
   w.app_cnt = off; off += SPLITK_COUNTER_BYTES;
+  w.q_cnt = off;   off += SPLITK_COUNTER_BYTES;
+  w.o_cnt = off;   off += SPLITK_COUNTER_BYTES;
   w.prefix = off;  off += align256((size_t)(B + 1) * 4);
   w.splits = off;  off += align256((size_t)n_splits * SPLIT_REC * 4);   // per split: see plan_block
   w.qabs = off;    off += align256((size_t)B * n_h * D_K * elt);

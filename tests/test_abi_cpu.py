@@ -136,16 +136,6 @@ def test_decode_step_workspace_holds_the_append_reduction():
 COUNTER_BYTES = 1024 * 4          # split-K tile counters at the start of the workspace
 
 
-def _splits(M, N, K):
-    """K chunks of a bf16 projection: double while the grid has fewer than
-    1024 workgroups, up to 16, while 128 * 2S divides K."""
-    tiles = (N // 16) * ((M + 31) // 32)
-    S = 1
-    while S < 16 and tiles * S < 1024 and K % (2 * S * 128) == 0:
-        S *= 2
-    return S
-
-
 def _a256(x):
     return (x + 255) // 256 * 256
 

@@ -83,3 +83,40 @@ def test_decode_layer_equals_its_parts_and_the_oracle(B, d_model, d_cq, lens, dt
         ref = oracle.output_project(o, f["W_O"])
         e = rel_err(got[b], ref)
         assert e <= (1e-2 if dtype == torch.bfloat16 else 1e-5), f"sequence {b}: rel err {e:.3e}"
+
+
+def test_decode_layer_workspace_reused_at_a_smaller_batch():
+    # One workspace, sized for B = 64, serves a B = 64 call and then a B = 8
+    # call.  At B = 8 the output projection is split over K and finished in
+    # the launch, through tile counters that must sit where the B = 64 call
+    # left zeros (not inside its partials): u must equal, bit for bit, the
+    # same B = 8 call on a fresh workspace.
+    import compressed_kv_cache_mla_amd as mla
+    d_model, d_cq = 1024, 512
+    runs = {}
+    for B in (64, 8):
+        cfg = W.scaled(W.CONFIGS["b64_ragged"], name=f"layer_reuse_b{B}", d_model=d_model, B=B, lens=(20, 300),
+                       seed=1400 + B)
+        wl = W.Workload(cfg)
+        P = _proj_weights(cfg.seed, cfg.n_h, d_model, d_cq, "cuda")
+        runs[B] = (wl, {k: mla.pack_weight(wl.dims, v) for k, v in P.items()})
+    _say("case decode layer workspace B=64 then B=8")
+    dims = runs[64][0].dims
+    shared = mla.decode_layer_workspace(dims, 64, d_cq)
+
+    def call(B, ws):
+        wl, Pp = runs[B]
+        u = torch.full((B, d_model), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, wl.cfg.n_h), dtype=torch.float32, device="cuda")
+        mla.decode_layer(dims, wl._newest_token_states(), wl.W_DKV, wl.W_KR, Pp["W_DQ"], Pp["W_UQ"], Pp["W_QR"],
+                         wl.W_UK, wl.W_UV, Pp["W_O"], wl.pos_q, wl.c_KV, wl.k_R, wl.row_stride, wl.num_pages,
+                         wl.page_table, wl.seq_lens, u, lse, ws)
+        torch.cuda.synchronize()
+        assert mla.read_error_flags(ws) == 0
+        return u, lse
+
+    for B in (64, 8, 64, 8):
+        u, lse = call(B, shared)
+        u_ref, lse_ref = call(B, mla.decode_layer_workspace(dims, B, d_cq))
+        assert torch.isfinite(u).all()
+        assert torch.equal(u, u_ref) and torch.equal(lse, lse_ref), f"B={B} on the reused workspace"

@@ -17,7 +17,15 @@ Conventions (the same as the library's and the oracle's):
   N(0, 1) latents ("direct" mode, used where building the context through
   append would take long, e.g. 60 layers x 128 x 8192 tokens);
 * weights ~ N(0, 1/fan_in); q^C, q^R ~ N(0, 1) (the distribution of W^UQ h and
-  W^QR h under those weights).
+  W^QR h under those weights);
+* "exact query" workloads (tests only) replace W^UK and q^C by values built
+  from the same N(0, 1) draws with comparisons alone: W^UK entries in
+  {0, +-1/4, +-1/2}, mostly 0, and q^C small integers, so that every element of
+  q~ = W^UK^T q^C is a multiple of 1/4 below 64 in magnitude and exact in
+  bf16; q^R is drawn small (N(0, 2^-16)) and the softmax scale is the fp32
+  value of ln 2, whose product with fp32 log2(e) is exactly 1.  The scores
+  the kernel sees are then the oracle's up to fp32 summation and the small
+  RoPE'd q^R part, whatever their size.
 """
 from __future__ import annotations
 
@@ -49,6 +57,7 @@ class Config:
     query: str = "synthetic"     # "synthetic" | "projected" (q from W^UQ, W^QR; tests only)
     growth: int = 0              # direct mode: the row at position p of an n-token sequence is
                                  # scaled by 2^floor(growth * p / n) (scores that keep rising)
+    exact_q: bool = False        # W^UK, q^C with q~ exact in bf16 (see the module docstring)
 
     def context_lengths(self) -> np.ndarray:
         """Prior context L_b per sequence (the decode token comes on top)."""
@@ -83,6 +92,30 @@ def _key(cfg: Config, name: str, layer: int = 0) -> int:
     return si.stream_key(cfg.seed, name, layer)
 
 
+# fp32 ln 2: times fp32 log2(e) it rounds to exactly 1.0 in fp32
+LN2_F32 = float(np.float32(math.log(2.0)))
+
+
+def _steps(x: torch.Tensor, thresholds, unit: float) -> torch.Tensor:
+    """sign(x) * unit * #{t in thresholds : |x| >= t}, by comparisons only, so
+    that the CPU and the GPU map the same draws to the same values."""
+    a = x.abs()
+    k = torch.zeros_like(x, dtype=torch.float32)
+    for t in thresholds:
+        k = k + (a >= t).to(torch.float32)
+    return (torch.sign(x.to(torch.float32)) * k * unit).to(x.dtype)
+
+
+def exact_W_UK(x: torch.Tensor) -> torch.Tensor:
+    """Exact-query W^UK from N(0, 1) draws: 0 for |x| < 1.5, +-1/4 up to 3, +-1/2 beyond."""
+    return _steps(x, (1.5, 3.0), 0.25)
+
+
+def exact_q_C(x: torch.Tensor) -> torch.Tensor:
+    """Exact-query q^C from N(0, 1) draws: integers in [-6, 6]."""
+    return _steps(x, (0.5, 1.0, 1.5, 2.0, 2.5, 3.0), 1.0)
+
+
 class Workload:
     """Device tensors of one configuration (one layer at a time)."""
 
@@ -92,7 +125,8 @@ class Workload:
         self.cfg = cfg
         self.layer = layer
         self.device = torch.device(device)
-        self.dims = mla.Dims(n_h=cfg.n_h, d_model=cfg.d_model, page_size=cfg.page_size, dtype=cfg.dtype)
+        self.dims = mla.Dims(n_h=cfg.n_h, d_model=cfg.d_model, page_size=cfg.page_size, dtype=cfg.dtype,
+                             softmax_scale=LN2_F32 if cfg.exact_q else None)
         self.n_splits = n_splits
         L = cfg.context_lengths()
         self.n = (L + 1).astype(np.int64)                      # cached tokens incl. the decode token
@@ -131,18 +165,33 @@ class Workload:
         return si.normal(_key(self.cfg, name, self.layer), (rows, cols), 1.0 / math.sqrt(fan_in), self.cfg.dtype,
                          device or self.device)
 
+    def _W_UK(self, device=None):
+        c = self.cfg
+        if c.exact_q:
+            return exact_W_UK(si.normal(_key(c, "W_UK", self.layer), (c.n_h * D_H, D_C), 1.0, c.dtype,
+                                        device or self.device))
+        return self._w("W_UK", c.n_h * D_H, D_C, D_C, device=device)
+
+    def _q_rows(self, name, rows, width, device):
+        c = self.cfg
+        if name == "q_C" and c.exact_q:
+            return exact_q_C(si.normal_rows(_key(c, name, self.layer), rows, width, 1.0, c.dtype, device))
+        scale = 1.0 / 256 if (name == "q_R" and c.exact_q) else 1.0
+        return si.normal_rows(_key(c, name, self.layer), rows, width, scale, c.dtype, device)
+
     def _build_weights(self):
         c, dm, nh = self.cfg, self.cfg.d_model, self.cfg.n_h
         self.W_DKV = self._w("W_DKV", D_C, dm, dm)
         self.W_KR = self._w("W_KR", D_R, dm, dm)
-        self.W_UK = self._w("W_UK", nh * D_H, D_C, D_C)
+        self.W_UK = self._W_UK()
         self.W_UV = self._w("W_UV", nh * D_H, D_C, D_C)
 
     def _build_queries(self):
         c = self.cfg
         if c.query == "synthetic":
-            self.q_C = si.normal(_key(c, "q_C", self.layer), (c.B, c.n_h, D_H), 1.0, c.dtype, self.device)
-            self.q_R = si.normal(_key(c, "q_R", self.layer), (c.B, c.n_h, D_R), 1.0, c.dtype, self.device)
+            rows = range(c.B * c.n_h)
+            self.q_C = self._q_rows("q_C", rows, D_H, self.device).reshape(c.B, c.n_h, D_H)
+            self.q_R = self._q_rows("q_R", rows, D_R, self.device).reshape(c.B, c.n_h, D_R)
         else:   # filled in by the caller (set_queries)
             self.q_C = torch.zeros((c.B, c.n_h, D_H), dtype=c.dtype, device=self.device)
             self.q_R = torch.zeros((c.B, c.n_h, D_R), dtype=c.dtype, device=self.device)
@@ -252,9 +301,8 @@ class Workload:
         g0, g1 = int(self.prefix[b]), int(self.prefix[b + 1])
         f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
         cpu = torch.device("cpu")
-        W = {k: f64(self._w(k, *shape, device=cpu)) for k, shape in
-             {"W_UK": (c.n_h * D_H, D_C, D_C), "W_UV": (c.n_h * D_H, D_C, D_C)}.items()}
-        d = dict(W_UK=W["W_UK"], W_UV=W["W_UV"], n=g1 - g0, pos_q=g1 - g0 - 1)
+        d = dict(W_UK=f64(self._W_UK(device=cpu)), W_UV=f64(self._w("W_UV", c.n_h * D_H, D_C, D_C, device=cpu)),
+                 n=g1 - g0, pos_q=g1 - g0 - 1)
         if c.cache_mode == "direct":
             lat = f64(self.latent_rows(range(g0, g1 - 1), device=cpu))
             d["prior_c"], d["prior_kR"] = lat[:, :D_C], lat[:, D_C:]
@@ -264,8 +312,7 @@ class Workload:
         d["W_DKV"] = f64(self._w("W_DKV", D_C, c.d_model, c.d_model, device=cpu))
         d["W_KR"] = f64(self._w("W_KR", D_R, c.d_model, c.d_model, device=cpu))
         if c.query == "synthetic":
-            d["q_C"] = f64(si.normal_rows(_key(c, "q_C", self.layer), range(b * c.n_h, (b + 1) * c.n_h), D_H, 1.0,
-                                          c.dtype, cpu))
-            d["q_R"] = f64(si.normal_rows(_key(c, "q_R", self.layer), range(b * c.n_h, (b + 1) * c.n_h), D_R, 1.0,
-                                          c.dtype, cpu))
+            rows = range(b * c.n_h, (b + 1) * c.n_h)
+            d["q_C"] = f64(self._q_rows("q_C", rows, D_H, cpu))
+            d["q_R"] = f64(self._q_rows("q_R", rows, D_R, cpu))
         return d
