@@ -26,7 +26,7 @@ FLAG_BAD_SEQ_LEN, FLAG_BAD_PAGE, FLAG_BAD_POSITION, FLAG_BAD_SEQ_ID = 1, 2, 4, 8
 
 EXPORTED = ("mla_cache_append", "mla_cache_append_ws", "mla_cache_append_workspace_size",
             "mla_decode_workspace_size", "mla_decode", "mla_decode_ex",
-            "mla_decode_step_workspace_size", "mla_decode_step",
+            "mla_decode_step_workspace_size", "mla_decode_step", "mla_decode_step_noalloc",
             "mla_pack_weight", "mla_query_project_workspace_size", "mla_query_project",
             "mla_output_project_workspace_size", "mla_output_project",
             "mla_prefill_workspace_size", "mla_prefill",
@@ -107,6 +107,9 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_step.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32, vp, vp,
                                       vp, vp, sz, i32, ctypes.POINTER(mla_decode_opts), vp]
         L.mla_decode_step.restype = ctypes.c_int
+        L.mla_decode_step_noalloc.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32,
+                                              vp, vp, vp, vp, vp]
+        L.mla_decode_step_noalloc.restype = ctypes.c_int
         L.mla_pack_weight.argtypes = [pdims, i32, i32, vp, vp, vp]
         L.mla_pack_weight.restype = ctypes.c_int
         L.mla_query_project_workspace_size.argtypes = [pdims, i32, i32]
@@ -281,6 +284,20 @@ def decode_step(dims: Dims, h_new, W_DKV, W_KR, q_C, q_R, pos_q, W_UK, W_UV, c_K
                                  _ptr(pos_q), _ptr(W_UK), _ptr(W_UV), _ptr(c_KV), _ptr(k_R), row_stride, num_pages,
                                  _ptr(page_table), max_pages, _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace),
                                  workspace.numel(), n_splits, ctypes.byref(o), _stream(stream)))
+
+
+def decode_step_noalloc(dims: Dims, h_new, W_DKV, W_KR, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride: int,
+                        num_pages: int, page_table, seq_lens, out, lse=None, err_flags=None, stream=None):
+    """mla_decode_step_noalloc: decode_step without a workspace (the library's
+    own per-GPU scratch array; nothing is allocated).  err_flags: None or a
+    one-element int32 device tensor that receives the step's FLAG_* bits."""
+    B = q_C.shape[0]
+    max_pages = page_table.shape[1]
+    d = dims.c()
+    _check(lib().mla_decode_step_noalloc(ctypes.byref(d), B, _ptr(h_new), _ptr(W_DKV), _ptr(W_KR), _ptr(q_C),
+                                         _ptr(q_R), _ptr(pos_q), _ptr(W_UK), _ptr(W_UV), _ptr(c_KV), _ptr(k_R),
+                                         row_stride, num_pages, _ptr(page_table), max_pages, _ptr(seq_lens),
+                                         _ptr(out), _ptr(lse), _ptr(err_flags), _stream(stream)))
 
 
 def pack_weight(dims: Dims, W, stream=None):

@@ -59,13 +59,16 @@ __device__ __forceinline__ MergeInfo merge_info(int32_t b, int32_t h, int32_t n_
 
 // Decode step: the append's flags (word 1 of the flag area) join the decode's
 // (word 0) once both launches before this one are done; word 1 goes back to 0.
-__device__ __forceinline__ void merge_step_flags(int32_t* flags) {
+// ext (may be NULL): a caller's flag word that also receives the step's flags.
+__device__ __forceinline__ void merge_step_flags(int32_t* flags, int32_t* ext) {
   if (flags && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     const int32_t v = flags[1];
+    int32_t all = flags[0] | v;
     if (v) {
-      atomicOr(flags, v);
+      all = atomicOr(flags, v) | v;
       flags[1] = 0;
     }
+    if (ext && all) atomicOr(ext, all);
   }
 }
 
@@ -73,9 +76,10 @@ __global__ void __launch_bounds__(256) combine_f32_kernel(int32_t B, int32_t n_h
                                                           int32_t G, const float* __restrict__ part_ml,
                                                           const float* __restrict__ part_o,
                                                           const float* __restrict__ W_UV, float* __restrict__ out,
-                                                          float* __restrict__ lse, int32_t* merge_flags) {
+                                                          float* __restrict__ lse, int32_t* merge_flags,
+                                                          int32_t* ext_flags) {
   __shared__ float ol[CB_SEQ][D_C + 4];
-  merge_step_flags(merge_flags);
+  merge_step_flags(merge_flags, ext_flags);
   __shared__ MergeInfo info[CB_SEQ];
   const int tid = threadIdx.x;
   const int h = blockIdx.x;
@@ -149,11 +153,11 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
                                                             const bf16* __restrict__ part_o,
                                                             const bf16* __restrict__ W_UV, float* __restrict__ out,
                                                             float* __restrict__ lse, int32_t* merge_flags,
-                                                            bf16* __restrict__ out_packed) {
+                                                            bf16* __restrict__ out_packed, int32_t* ext_flags) {
   constexpr int NBQ = CS / 16;
   constexpr int CB = CB_MAX;
   constexpr bool PRE = CS == 16;   // registers allow the W^UV prefetch with one accumulator block
-  merge_step_flags(merge_flags);
+  merge_step_flags(merge_flags, ext_flags);
   __shared__ __attribute__((aligned(16))) char ol[CS * D_C * 2];
   __shared__ int empty_l[CS];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -260,12 +264,12 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
 
 hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, int32_t n_splits,
                           const float* part_ml, const void* part_o, const void* W_UV, float* out,
-                          float* lse, int32_t* merge_flags, void* out_packed, hipStream_t s) {
+                          float* lse, int32_t* merge_flags, void* out_packed, hipStream_t s, int32_t* ext_flags) {
   bf16* op = d.dtype == MLA_BF16 ? (bf16*)out_packed : nullptr;
   if (d.dtype == MLA_FP32) {
     dim3 grid(d.n_h, (B + CB_SEQ - 1) / CB_SEQ);
     combine_f32_kernel<<<grid, 256, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const float*)part_o,
-                                            (const float*)W_UV, out, lse, merge_flags);
+                                            (const float*)W_UV, out, lse, merge_flags, ext_flags);
   } else {
     // the most sequences per workgroup (W^UV is read once per block of them)
     // that still leave at least two workgroups per compute unit (64, for long
@@ -273,15 +277,15 @@ hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, i
     if (B > 32 && d.n_h * ((B + 63) / 64) >= 512) {
       dim3 grid(d.n_h, (B + 63) / 64);
       combine_mfma_kernel<64><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
-                                                    (const bf16*)W_UV, out, lse, merge_flags, op);
+                                                    (const bf16*)W_UV, out, lse, merge_flags, op, ext_flags);
     } else if (B > 16 && d.n_h * ((B + 31) / 32) >= 256) {
       dim3 grid(d.n_h, (B + 31) / 32);
       combine_mfma_kernel<32><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
-                                                    (const bf16*)W_UV, out, lse, merge_flags, op);
+                                                    (const bf16*)W_UV, out, lse, merge_flags, op, ext_flags);
     } else {
       dim3 grid(d.n_h, (B + 15) / 16);
       combine_mfma_kernel<16><<<grid, 1024, 0, s>>>(B, d.n_h, prefix, n_splits, part_ml, (const bf16*)part_o,
-                                                    (const bf16*)W_UV, out, lse, merge_flags, op);
+                                                    (const bf16*)W_UV, out, lse, merge_flags, op, ext_flags);
     }
   }
   return hipGetLastError();

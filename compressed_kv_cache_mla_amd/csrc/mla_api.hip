@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <tuple>
 
@@ -153,7 +154,7 @@ static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, 
                               int64_t row_stride, int32_t num_pages, const int32_t* page_table, int32_t max_pages,
                               const int32_t* seq_lens, float* out, float* lse, void* workspace, size_t ws_bytes,
                               int32_t n_splits, const mla_decode_opts* opts, const StepAppendIn* step,
-                              void* stream, bool merge_append_flags = false) {
+                              void* stream, bool merge_append_flags = false, int32_t* ext_flags = nullptr) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
@@ -230,7 +231,8 @@ static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, 
   if (e == hipSuccess && opts && opts->ev_stop) e = hipEventRecord((hipEvent_t)opts->ev_stop, s);
   if (e == hipSuccess)
     e = mla::launch_combine(*dims, B, prefix, n_splits, part_ml, part_o, W_UV, out, lse,
-                            step || merge_append_flags ? flags : nullptr, step ? step->o_packed : nullptr, s);
+                            step || merge_append_flags ? flags : nullptr, step ? step->o_packed : nullptr, s,
+                            ext_flags);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -629,6 +631,85 @@ mla_status mla_decode_layer(const mla_dims* dims, int32_t B, int32_t d_cq, const
     st = output_project_impl(dims, B, (const float*)(ws + L.o), W_O, u, ws + L.out, L.total - L.out, stream,
                              op.packed, ws + D.o_cnt);
   return st;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free decode step
+namespace {
+
+// Scratch of mla_decode_step_noalloc: one decode-step workspace of at most
+// NOALLOC_SCRATCH_BYTES in a file-scope device array (each GPU the library
+// runs on holds its own copy until the process ends).  In host code the name
+// `scratch` is only a host-side stand-in: every host use of the array goes
+// through the device address hipGetSymbolAddress returned for the current
+// device, kept in g_scratch.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)80 << 20;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+char* g_scratch[NOALLOC_MAX_DEVICES] = {};
+
+__global__ void __launch_bounds__(256) zero_words_kernel(int32_t* p, int32_t n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// The current device's scratch.  On the first call on a device its address is
+// looked up (with that device current) and the words that must start at zero
+// -- the flag area and the split-K tile counters, which every completed step
+// leaves at zero again -- are cleared by a fill kernel on stream s.
+mla_status noalloc_scratch(hipStream_t s, char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+    return fail(MLA_ERR_UNSUPPORTED, "device %d: the allocation-free step supports devices 0..%d", dev,
+                NOALLOC_MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    // flags and counters precede everything that depends on the batch size
+    const int32_t words = (int32_t)(mla::decode_ws_layout(1, 1, 1, 2, true).prefix / 4);
+    zero_words_kernel<<<dim3((words + 255) / 256), 256, 0, s>>>((int32_t*)p, words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "scratch clear launch: %s", hipGetErrorString(e));
+    g_scratch[dev] = (char*)p;
+  }
+  *out = g_scratch[dev];
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_step_noalloc(const mla_dims* dims, int32_t B, const void* h_new, const void* W_DKV,
+                                   const void* W_KR, const void* q_C, const void* q_R, const int32_t* pos_q,
+                                   const void* W_UK, const void* W_UV, void* c_KV, void* k_R, int64_t row_stride,
+                                   int32_t num_pages, const int32_t* page_table, int32_t max_pages,
+                                   const int32_t* seq_lens, float* out, float* lse, int32_t* err_flags,
+                                   void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  const int32_t n_splits = default_splits();
+  const size_t need = mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims), true).total;
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_WORKSPACE,
+                "B=%d, n_h=%d needs %zu bytes of scratch; the allocation-free step has %zu (use mla_decode_step)", B,
+                dims->n_h, need, NOALLOC_SCRATCH_BYTES);
+  char* ws = nullptr;
+  st = noalloc_scratch((hipStream_t)stream, &ws);
+  if (st != MLA_OK) return st;
+  const StepAppendIn in{h_new, W_DKV, W_KR, nullptr};
+  return decode_impl(dims, B, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride, num_pages, page_table, max_pages,
+                     seq_lens, out, lse, ws, NOALLOC_SCRATCH_BYTES, n_splits, nullptr, &in, stream, false,
+                     err_flags);
 }
 
 mla_status mla_read_error_flags(void* workspace_or_flag, int32_t* flags, void* stream) {

@@ -283,8 +283,10 @@ hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, co
                               const int32_t* split_rec, int32_t n_splits, float* part_ml, void* part_o,
                               int32_t* flags, hipStream_t s);
 // merge_flags: NULL, or (decode step) the flag area whose word 1 holds the
-// append's flags, to be OR-ed into word 0 and cleared.
+// append's flags, to be OR-ed into word 0 and cleared; ext_flags (NULL, or a
+// caller's device word, with merge_flags given) also receives them.
 hipError_t launch_combine(const mla_dims& d, int32_t B, const int32_t* prefix, int32_t n_splits,
                           const float* part_ml, const void* part_o, const void* W_UV, float* out,
-                          float* lse, int32_t* merge_flags, void* out_packed, hipStream_t s);
+                          float* lse, int32_t* merge_flags, void* out_packed, hipStream_t s,
+                          int32_t* ext_flags = nullptr);
 }  // namespace mla

@@ -228,6 +228,33 @@ mla_status mla_decode_step(const mla_dims* dims, int32_t B, const void* h_new, c
                            int32_t n_splits, const mla_decode_opts* opts, void* stream);
 
 /*
+ * mla_decode_step_noalloc -- mla_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): no workspace argument, and nothing is allocated by
+ * this call or by the library -- the step's scratch is a file-scope device
+ * array of the library, 80 MiB, one copy per GPU, held until the process
+ * ends.  Same kernels, same default split count (the device's CU count) and
+ * bitwise the same results as mla_decode_step with n_splits = 0 and opts =
+ * NULL; the arguments mean what they mean there.
+ *   err_flags  NULL, or one int32 of device memory into which the step ORs
+ *              its MLA_FLAG_* bits (the caller clears it).
+ * Limit: the step's scratch for (B, n_h, CU count) must fit the 80 MiB
+ * (mla_decode_step_workspace_size(dims, B, 0) <= 80 MiB: at n_h = 128 and
+ * 256 CUs, B <= 167); larger batches return MLA_ERR_WORKSPACE (use
+ * mla_decode_step).  The first call on each device looks up the array's
+ * address and clears its counters with a small kernel on `stream`; make that
+ * call outside graph capture.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (several streams or threads) race and
+ * must be ordered by the caller.
+ */
+mla_status mla_decode_step_noalloc(const mla_dims* dims, int32_t B, const void* h_new, const void* W_DKV,
+                                   const void* W_KR, const void* q_C, const void* q_R, const int32_t* pos_q,
+                                   const void* W_UK, const void* W_UV, void* c_KV, void* k_R, int64_t row_stride,
+                                   int32_t num_pages, const int32_t* page_table, int32_t max_pages,
+                                   const int32_t* seq_lens, float* out, float* lse, int32_t* err_flags,
+                                   void* stream);
+
+/*
  * mla_pack_weight -- copy a row-major weight W [rows, K] (dims.dtype) into
  * the packed layout the projection kernels stream (mla_query_project,
  * mla_output_project): blocks of 16 rows x 32 columns, block (rb, ks) at
