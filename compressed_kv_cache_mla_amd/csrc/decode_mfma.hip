@@ -11,6 +11,10 @@
 // One workgroup = NW waves (one per SIMD, occupancy 1) and one contiguous
 // range of the batch's tokens (see split_begin).  All n_h = 32*NW heads of a
 // sequence share each staged tile:
+//  * Within each sequence piece the tiles are visited from a per-split
+//    starting tile on, wrapping around (tile_phase, mla_common.h), so that
+//    the workgroups' concurrent reads do not march through the pool in
+//    lockstep at fixed distances, which crowds HBM channels.
 //  * Tiles of TT = 32 cached rows (36 KB) are copied HBM -> LDS with
 //    global_load_lds (16 B per lane, 1 KB per wave instruction), three
 //    buffers deep: two tiles are in flight while one is computed.  A row is
@@ -49,7 +53,7 @@
 namespace mla {
 namespace {
 
-constexpr int TT = 32;                  // cached rows per tile
+constexpr int TT = DECODE_TT;           // cached rows per tile (32)
 constexpr int NINSTR = TT * 72 / 64;    // 36 copy instructions (blocks of 1 KB) per tile
 constexpr int TILEB = NINSTR * 1024;    // 36,864 bytes per tile buffer (36 windows of 1 KB)
 constexpr int PGOFF = TILEB;            // the tile's two page ids follow its windows
@@ -149,54 +153,76 @@ struct TileDesc {
 // through the constant address space so that uniform reads are scalar loads.
 typedef const __attribute__((address_space(4))) int32_t* cint_t;
 
-// Cursor over the tiles of one workgroup's token range [x, P1).  Tiles never
-// straddle two sequences; within a sequence the page index and offset of the
-// next tile advance by TT (pages hold at least TT rows).
+// Cursor over the tiles of one workgroup's token range [P0, P1) (split
+// `split`).  The range is cut at sequence ends into segments; a segment
+// [sx, se) is cut into K tiles of TT rows from sx on (only tile K-1 can be
+// shorter) and visited from tile tile_phase(split, K) on, wrapping around to
+// tile 0 (mla_common.h).  Tiles never straddle two sequences.  From one tile
+// to the next within a segment the page index and offset advance by TT
+// (pages hold at least TT rows); the wrap goes back to the segment's start.
 struct Cursor {
-  int32_t x, P1, s_beg, s_end, seg_beg;
-  int32_t b, B, pidx, prem, page_size;
-  __device__ void init(cint_t rec, int32_t B_, int32_t P0, int32_t P1_, int32_t ps) {
+  int32_t P1, B, page_size, split;
+  int32_t b, s_beg, s_end;   // sequence of the current segment, its tokens [s_beg, s_end)
+  int32_t sx, se, K, j, k;   // segment [sx, se) of K tiles, j of them handed out, k the next one
+  int32_t pidx, prem;        // page index (in the sequence) and offset of tile k's first row
+  int32_t p_sx, r_sx;        // the same for tile 0
+  bool done;
+  __device__ void segment(int32_t x) {
+    sx = x;
+    se = s_end < P1 ? s_end : P1;
+    K = (se - sx + TT - 1) / TT;
+    j = 0;
+    k = tile_phase(split, K);
+    const int32_t t0 = sx - s_beg, tk = t0 + TT * k;
+    p_sx = t0 / page_size;
+    r_sx = t0 - p_sx * page_size;
+    pidx = tk / page_size;
+    prem = tk - pidx * page_size;
+  }
+  __device__ void init(cint_t rec, int32_t B_, int32_t P0, int32_t P1_, int32_t ps, int32_t w) {
     B = B_;
     P1 = P1_;
-    x = P0;
     page_size = ps;
+    split = w;
     b = rec[0];
     s_beg = rec[1];
     s_end = rec[2];
-    seg_beg = x;
-    const int32_t t0 = x - s_beg;
-    pidx = t0 / ps;
-    prem = t0 - pidx * ps;
+    done = P0 >= P1;
+    if (!done) segment(P0);
   }
   __device__ TileDesc next(cint_t prefix) {
     TileDesc t;
-    if (x >= P1) {
+    if (done) {
       t.b = 0; t.t0 = 0; t.n = 0; t.p0 = 0; t.rem = 0; t.first = 0; t.last = 0;
       return t;
     }
-    const int32_t seg_end = s_end < P1 ? s_end : P1;
+    const int32_t x0 = sx + TT * k;
     t.b = b;
-    t.t0 = x - s_beg;
-    t.n = (seg_end - x) < TT ? (seg_end - x) : TT;
+    t.t0 = x0 - s_beg;
+    t.n = (se - x0) < TT ? (se - x0) : TT;
     t.p0 = pidx;
     t.rem = prem;
-    t.first = (x == seg_beg);
-    x += t.n;
-    t.last = (x == seg_end);
+    t.first = (j == 0);
+    ++j;
+    t.last = (j == K);
     if (t.last) {
-      if (x < P1) {
+      if (se < P1) {
         // move to the next sequence holding tokens (skip empty ones)
         do {
           ++b;
           s_beg = s_end;
           s_end = prefix[b + 1];
-        } while (s_end <= x && b < B - 1);
-        seg_beg = x;
+        } while (s_end <= se && b < B - 1);
+        segment(se);
+      } else {
+        done = true;
       }
-      pidx = 0;
-      prem = 0;
+    } else if (++k == K) {
+      k = 0;
+      pidx = p_sx;
+      prem = r_sx;
     } else {
-      prem += TT;   // a tile that does not end its segment has TT rows
+      prem += TT;
       if (prem >= page_size) {
         prem -= page_size;
         ++pidx;
@@ -269,7 +295,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 
   Cursor cur;
   const cint_t rec = (cint_t)split_rec + SPLIT_REC * split;
-  cur.init(rec, B, P0, P1, page_size);
+  cur.init(rec, B, P0, P1, page_size, split);
   TileDesc t_now = cur.next(cpre);   // tile being computed
   TileDesc t_n1 = cur.next(cpre);    // tile in flight
   TileDesc t_n2 = cur.next(cpre);    // tile whose copy is issued this iteration
@@ -381,19 +407,16 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   m_ref[0] = m_ref[1] = -INFINITY;
   l_sum[0] = l_sum[1] = 0.f;
   // The query loads go first; the pages of the first two tiles come with the
-  // split's plan record (pages p0 .. p0+2 of its first sequence), so both
-  // copies start one memory latency after the record.
+  // split's plan record when both lie in its first segment, so both copies
+  // start one memory latency after the record.
   load_q(t_now.b);
   {
-    const int32_t r0 = rec[3], r1 = rec[4], r2 = rec[5];
-    const int32_t a0 = r0, a1 = (t_now.rem + t_now.n > page_size) ? r1 : r0;
+    const int32_t a0 = rec[3], a1 = rec[4];
     int32_t b0 = 0, b1 = 0;
     if (t_n1.n > 0) {
-      if (t_n1.b == t_now.b) {
-        const int32_t kf = t_n1.p0 - t_now.p0;
-        const int32_t kl = kf + ((t_n1.rem + t_n1.n > page_size) ? 1 : 0);
-        b0 = kf == 0 ? r0 : r1;
-        b1 = kl == 0 ? r0 : (kl == 1 ? r1 : r2);
+      if (!t_now.last) {
+        b0 = rec[5];
+        b1 = rec[6];
       } else {
         b0 = cpt[page_index(t_n1, 0)];
         b1 = cpt[page_index(t_n1, 1)];
