@@ -37,6 +37,18 @@ Readings where the pages are silent (each is listed in the design notes):
 * The output projection W^O [d_model, n_h*d_h] acts on the heads' outputs
   concatenated in head order (``output_project``); the decode attention itself
   returns each head's o_i.
+* Sparse top-k decode ([V3-V4] "DeepSeek 架构精讲：从 V3 到 V4" (cyco.top),
+  §4 V3.2 bullet and §6 self-test question 7): the pages say only that a
+  light "indexer" first picks the few most relevant cached tokens and the
+  attention then looks at those alone.  Reading taken: every cached token j
+  carries a small indexer key k^I_j (d_I wide); a decode query carries H_I
+  indexer heads q^I_h and head weights w_h; the token's relevance is
+  I_j = sum_h w_h * max(0, q^I_h . k^I_j) (``indexer_scores``); the k tokens
+  of largest I_j are kept, equal scores going to the smaller token index
+  (``topk_select``; all tokens when n <= k); the MLA decode attention then
+  runs over the kept rows only (``attend_sparse``).  How k^I, q^I and w are
+  produced is outside the pages and outside this function set: they are
+  inputs.
 
 Everything is numpy float64; matrix products are numpy ``@``.
 """
@@ -257,3 +269,47 @@ def attend_causal_chunk(q_C, q_R, pos, c_KV, k_R, W_UK, W_UV, base: float, scale
 def softmax_scale(d_h: int, d_hR: int) -> float:
     """1/sqrt(d_h + d_h^R): q and k are the concatenations of width d_h + d_h^R."""
     return 1.0 / np.sqrt(d_h + d_hR)
+
+
+# ----------------------------------------------------------------------------
+# Sparse top-k decode ([V3-V4] §4 V3.2 bullet, §6 question 7)
+# ----------------------------------------------------------------------------
+
+
+def indexer_scores(q_I, w_I, k_I) -> np.ndarray:
+    """Relevance of each cached token to one decode query:
+    I_j = sum_h w_h * max(0, q^I_h . k^I_j).
+    q_I [H_I, d_I], w_I [H_I], k_I [n, d_I]; returns [n] (fp64)."""
+    q_I = np.asarray(q_I, dtype=np.float64)
+    w_I = np.asarray(w_I, dtype=np.float64)
+    k_I = np.asarray(k_I, dtype=np.float64)
+    dots = q_I @ k_I.T                                  # [H_I, n]: q^I_h . k^I_j
+    return (w_I[:, None] * np.maximum(dots, 0.0)).sum(axis=0)
+
+
+def topk_select(scores, k: int) -> np.ndarray:
+    """Indices (ascending) of the k largest scores; between equal scores the
+    smaller index is kept first.  All indices when len(scores) <= k."""
+    scores = np.asarray(scores)
+    n = scores.shape[0]
+    if n <= k:
+        return np.arange(n, dtype=np.int64)
+    order = sorted(range(n), key=lambda j: (-scores[j], j))   # largest first, then smaller index
+    return np.array(sorted(order[:k]), dtype=np.int64)
+
+
+def attend_sparse(q_C, q_R, pos_q, c_KV, k_R, W_UK, W_UV, base: float, scale: float, sel):
+    """The absorbed MLA decode over the kept rows only: the softmax runs over
+    j in sel, O~_i = sum_{j in sel} p_j c_j, o_i = W^UV_i O~_i."""
+    sel = np.asarray(sel, dtype=np.int64)
+    c_KV = np.asarray(c_KV)
+    k_R = np.asarray(k_R)
+    return attend_absorbed(q_C, q_R, pos_q, c_KV[sel], k_R[sel], W_UK, W_UV, base, scale)
+
+
+def sparse_decode(q_C, q_R, pos_q, c_KV, k_R, W_UK, W_UV, base: float, scale: float, q_I, w_I, k_I, k: int):
+    """Indexer scores, top-k selection, attention over the kept rows.
+    Returns (out [n_h, d_h], lse [n_h], sel)."""
+    sel = topk_select(indexer_scores(q_I, w_I, k_I), k)
+    out, lse = attend_sparse(q_C, q_R, pos_q, c_KV, k_R, W_UK, W_UV, base, scale, sel)
+    return out, lse, sel
