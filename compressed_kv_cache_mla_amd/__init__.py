@@ -31,6 +31,8 @@ EXPORTED = ("mla_cache_append", "mla_cache_append_ws", "mla_cache_append_workspa
             "mla_output_project_workspace_size", "mla_output_project",
             "mla_prefill_workspace_size", "mla_prefill",
             "mla_decode_layer_workspace_size", "mla_decode_layer",
+            "mla_indexer_select_workspace_size", "mla_indexer_select",
+            "mla_sparse_decode_workspace_size", "mla_sparse_decode",
             "mla_read_error_flags", "mla_last_error", "mla_device_cu_count")
 
 
@@ -130,6 +132,16 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_layer.argtypes = [pdims, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp,
                                        i32, vp, vp, vp, vp, sz, i32, ctypes.POINTER(mla_decode_opts), vp]
         L.mla_decode_layer.restype = ctypes.c_int
+        L.mla_indexer_select_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.mla_indexer_select_workspace_size.restype = sz
+        L.mla_indexer_select.argtypes = [i32, i32, i32, i32, vp, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, vp,
+                                         vp, sz, vp]
+        L.mla_indexer_select.restype = ctypes.c_int
+        L.mla_sparse_decode_workspace_size.argtypes = [pdims, i32, i32, i32, i32]
+        L.mla_sparse_decode_workspace_size.restype = sz
+        L.mla_sparse_decode.argtypes = [pdims, i32, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp, i32, vp, i32, i32, i32,
+                                        vp, vp, vp, i64, vp, vp, vp, vp, sz, i32, ctypes.POINTER(mla_decode_opts), vp]
+        L.mla_sparse_decode.restype = ctypes.c_int
         L.mla_read_error_flags.argtypes = [vp, ctypes.POINTER(i32), vp]
         L.mla_read_error_flags.restype = ctypes.c_int
         L.mla_last_error.argtypes = []
@@ -257,6 +269,57 @@ def decode(dims: Dims, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride: int, 
     else:
         o = mla_decode_opts(_event_handle(ev_start), _event_handle(ev_stop), impl)
         _check(lib().mla_decode_ex(*args, ctypes.byref(o), _stream(stream)))
+    return workspace
+
+
+def indexer_select_workspace_size(B: int, max_pages: int, page_size: int, top_k: int) -> int:
+    return int(lib().mla_indexer_select_workspace_size(B, max_pages, page_size, top_k))
+
+
+def indexer_select(q_I, w_I, k_I, idx_row_stride: int, num_pages: int, page_size: int, page_table, seq_lens,
+                   top_k: int, scores, sel_tok, sel_row, err_flags, workspace=None, stream=None):
+    """mla_indexer_select: the indexer's relevance scores of every cached
+    token (scores [B, max_pages*page_size] fp32) and the top_k kept tokens of
+    each sequence in ascending order with their pool rows (sel_tok, sel_row
+    [B, top_k] int32; entries past min(seq_len, top_k) are left as they
+    were).  err_flags: a device int32 word the kernels OR MLA_FLAG_* into."""
+    B, H_I, d_I = q_I.shape
+    max_pages = page_table.shape[1]
+    if workspace is None:
+        workspace = torch.empty(indexer_select_workspace_size(B, max_pages, page_size, top_k), dtype=torch.uint8,
+                                device=q_I.device)
+    _check(lib().mla_indexer_select(B, H_I, d_I, top_k, _ptr(q_I), _ptr(w_I), _ptr(k_I), idx_row_stride, num_pages,
+                                    page_size, _ptr(page_table), max_pages, _ptr(seq_lens), _ptr(scores),
+                                    _ptr(sel_tok), _ptr(sel_row), _ptr(err_flags), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def sparse_decode_workspace_size(dims: Dims, B: int, max_pages: int, top_k: int, n_splits: int = 0) -> int:
+    d = dims.c()
+    return int(lib().mla_sparse_decode_workspace_size(ctypes.byref(d), B, max_pages, top_k, n_splits))
+
+
+def sparse_decode(dims: Dims, q_C, q_R, pos_q, W_UK, W_UV, c_KV, k_R, row_stride: int, num_pages: int, page_table,
+                  seq_lens, q_I, w_I, k_I, idx_row_stride: int, top_k: int, out, lse=None, sel_tok=None,
+                  workspace=None, n_splits: int = 0, stream=None, ev_start=None, ev_stop=None):
+    """mla_sparse_decode: the indexer picks each sequence's top_k cached
+    tokens, then the MLA decode attends over those rows only.  sel_tok
+    (optional [B, top_k] int32) receives the kept tokens; ev_start / ev_stop
+    are recorded around the gather attention kernel."""
+    B = q_C.shape[0]
+    H_I, d_I = q_I.shape[1], q_I.shape[2]
+    max_pages = page_table.shape[1]
+    if workspace is None:
+        workspace = torch.empty(sparse_decode_workspace_size(dims, B, max_pages, top_k, n_splits), dtype=torch.uint8,
+                                device=q_C.device)
+    d = dims.c()
+    o = mla_decode_opts(_event_handle(ev_start), _event_handle(ev_stop), 0)
+    _check(lib().mla_sparse_decode(ctypes.byref(d), B, _ptr(q_C), _ptr(q_R), _ptr(pos_q), _ptr(W_UK), _ptr(W_UV),
+                                   _ptr(c_KV), _ptr(k_R), row_stride, num_pages, _ptr(page_table), max_pages,
+                                   _ptr(seq_lens), H_I, d_I, top_k, _ptr(q_I), _ptr(w_I), _ptr(k_I), idx_row_stride,
+                                   _ptr(out), _ptr(lse), _ptr(sel_tok), _ptr(workspace), workspace.numel(), n_splits,
+                                   ctypes.byref(o), _stream(stream)))
     return workspace
 
 

@@ -232,20 +232,25 @@ struct Cursor {
   }
 };
 
-template <int NW>
+// GATHER: the sparse decode.  A sequence's "tokens" are then the positions
+// of its kept list, and position i lives in pool row rows[b * rows_stride +
+// i] (rows checked by the selection); a tile's 32 row ids travel like the
+// page ids (into the tile buffer's pad, one iteration ahead).
+template <int NW, bool GATHER>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV, const bf16* __restrict__ k_R,
                    int64_t row_stride, int32_t num_pages, const int32_t* __restrict__ page_table,
                    int32_t max_pages, int32_t page_size, const int32_t* __restrict__ prefix,
                    const int32_t* __restrict__ split_rec, int32_t B, int32_t G, float* __restrict__ part_ml,
-                   bf16* __restrict__ part_o, int32_t* __restrict__ flags) {
+                   bf16* __restrict__ part_o, int32_t* __restrict__ flags, const int32_t* __restrict__ rows,
+                   int32_t rows_stride) {
   constexpr int NH = 32 * NW;
   constexpr int IPW = NINSTR / NW;              // DMA instructions per wave (NW divides 36)
   constexpr int DB = 16 / NW;                   // 32-wide latent blocks per wave in P.V
   constexpr int PIECES = DB / 4;                // 128-column pieces of a wave's latent columns
-  __shared__ __attribute__((aligned(1024))) char kt0[TILEB + 16];
-  __shared__ __attribute__((aligned(1024))) char kt1[TILEB + 16];
-  __shared__ __attribute__((aligned(1024))) char kt2[TILEB + 16];
+  __shared__ __attribute__((aligned(1024))) char kt0[TILEB + 4 * TT];
+  __shared__ __attribute__((aligned(1024))) char kt1[TILEB + 4 * TT];
+  __shared__ __attribute__((aligned(1024))) char kt2[TILEB + 4 * TT];
   __shared__ __attribute__((aligned(1024))) char ql[NH * QLB];   // query dims 448..575, swizzled
   __shared__ __attribute__((aligned(16))) char pl[NH * PSTR];
   __shared__ float alpha_l[NH];
@@ -317,11 +322,18 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
     }
     return pg * page_size + (cross ? off - page_size : off);
   };
-  // The two page ids of a tile go to the pad after block 0 of a tile buffer
-  // (never written by tile copies, never read by the math).
+  // The two page ids of a tile (GATHER: its 32 row ids, positions past the
+  // tile's end repeating its last) go to the pad after the windows of a tile
+  // buffer (never written by tile copies, never read by the math).
   auto issue_page_ids = [&](char* kt, const TileDesc& td) __attribute__((always_inline)) {
-    if (wave == 0 && td.n > 0 && lane < 2)
-      dma4(page_table + page_index(td, lane), __builtin_amdgcn_readfirstlane(lds_addr(kt + PGOFF)));
+    if (GATHER) {
+      if (wave == 0 && td.n > 0 && lane < TT)
+        dma4(rows + (int64_t)td.b * rows_stride + td.t0 + min(lane, td.n - 1),
+             __builtin_amdgcn_readfirstlane(lds_addr(kt + PGOFF)));
+    } else {
+      if (wave == 0 && td.n > 0 && lane < 2)
+        dma4(page_table + page_index(td, lane), __builtin_amdgcn_readfirstlane(lds_addr(kt + PGOFF)));
+    }
   };
   const int64_t stride_b = row_stride * 2;
   // Copy of a tile: wave w fetches row groups w, w + NW, ...; in row group g
@@ -330,12 +342,13 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   // dma_src() forms a lane's source offset for the wave's gi-th row group
   // from the scalar bases (nothing is kept live across the loop); copy
   // instruction I = 9*gi + j of the wave is issued by dma_one().
-  auto dma_src = [&](const TileDesc& td, int gi, int32_t pg0, int32_t pg1) __attribute__((always_inline)) -> int64_t {
+  auto dma_src = [&](const TileDesc& td, int gi, int32_t pg0, int32_t pg1, const char* ids)
+                     __attribute__((always_inline)) -> int64_t {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int g = wave + NW * gi;
     const int m = (ln >> 3) ^ (g & 1);
-    const int64_t row = resolve_row(td, 8 * g + m, pg0, pg1);
+    const int64_t row = GATHER ? *(const int32_t*)(ids + 4 * (8 * g + m)) : resolve_row(td, 8 * g + m, pg0, pg1);
     return row * stride_b + 16 * ((ln & 7) ^ swz(m));
   };
   auto dma_one = [&](char* kt, int I, int64_t off) __attribute__((always_inline)) {
@@ -346,7 +359,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   auto issue_dma = [&](char* kt, const TileDesc& td, int32_t pg0, int32_t pg1) __attribute__((always_inline)) {
 #pragma unroll
     for (int gi = 0; gi < 4 / NW; ++gi) {
-      const int64_t off = dma_src(td, gi, pg0, pg1);
+      const int64_t off = dma_src(td, gi, pg0, pg1, kt + PGOFF);
 #pragma unroll
       for (int j = 0; j < 9; ++j) dma_one(kt, 9 * gi + j, off);
     }
@@ -409,8 +422,17 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
   // The query loads go first; the pages of the first two tiles come with the
   // split's plan record when both lie in its first segment, so both copies
   // start one memory latency after the record.
-  load_q(t_now.b);
-  {
+  if (GATHER) {
+    // the row ids of the first two tiles, then the query and the copies
+    issue_page_ids(kt0, t_now);
+    issue_page_ids(kt1, t_n1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    load_q(t_now.b);
+    issue_dma(kt0, t_now, 0, 0);
+    if (t_n1.n > 0) issue_dma(kt1, t_n1, 0, 0);
+  } else {
+    load_q(t_now.b);
     const int32_t a0 = rec[3], a1 = rec[4];
     int32_t b0 = 0, b1 = 0;
     if (t_n1.n > 0) {
@@ -447,7 +469,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
     {
       const int2 pg = *(const int2*)(kt_issue + PGOFF);
 #pragma unroll
-      for (int gi = 0; gi < 4 / NW; ++gi) doff[gi] = copy ? dma_src(t_n2, gi, pg.x, pg.y) : 0;
+      for (int gi = 0; gi < 4 / NW; ++gi) doff[gi] = copy ? dma_src(t_n2, gi, pg.x, pg.y, kt_issue + PGOFF) : 0;
     }
 
     // ---- scores S^T[token][head] for this wave's 32 heads (2 x 2 blocks of 16x16)
@@ -702,33 +724,37 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 
 }  // namespace
 
+template <int NW, bool GATHER>
+static void launch_nw(dim3 grid, hipStream_t s, const bf16* qabs, const bf16* c_KV, const bf16* k_R,
+                      int64_t row_stride, int32_t num_pages, const int32_t* page_table, int32_t max_pages,
+                      int32_t page_size, const int32_t* prefix, const int32_t* split_rec, int32_t B, int32_t G,
+                      float* part_ml, bf16* part_o, int32_t* flags, const int32_t* rows, int32_t rows_stride) {
+  decode_mfma_kernel<NW, GATHER><<<grid, 64 * NW, 0, s>>>(qabs, c_KV, k_R, row_stride, num_pages, page_table,
+                                                          max_pages, page_size, prefix, split_rec, B, G, part_ml,
+                                                          part_o, flags, rows, rows_stride);
+}
+
 hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                               const void* k_R, int64_t row_stride, int32_t num_pages,
                               const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
                               const int32_t* split_rec, int32_t n_splits, float* part_ml, void* part_o_v,
-                              int32_t* flags, hipStream_t s) {
-  bf16* part_o = (bf16*)part_o_v;
-  const int nw = d.n_h / 32;
-  dim3 grid(n_splits);
-  switch (nw) {
-    case 1:
-      decode_mfma_kernel<1><<<grid, 64, 0, s>>>((const bf16*)qabs, (const bf16*)c_KV, (const bf16*)k_R,
-                                               row_stride, num_pages, page_table, max_pages, d.page_size,
-                                               prefix, split_rec, B, n_splits, part_ml, part_o, flags);
-      break;
-    case 2:
-      decode_mfma_kernel<2><<<grid, 128, 0, s>>>((const bf16*)qabs, (const bf16*)c_KV, (const bf16*)k_R,
-                                                row_stride, num_pages, page_table, max_pages, d.page_size,
-                                                prefix, split_rec, B, n_splits, part_ml, part_o, flags);
-      break;
-    case 4:
-      decode_mfma_kernel<4><<<grid, 256, 0, s>>>((const bf16*)qabs, (const bf16*)c_KV, (const bf16*)k_R,
-                                                row_stride, num_pages, page_table, max_pages, d.page_size,
-                                                prefix, split_rec, B, n_splits, part_ml, part_o, flags);
-      break;
-    default:
-      return hipErrorInvalidValue;
+                              int32_t* flags, hipStream_t s, const int32_t* rows, int32_t rows_stride) {
+  const dim3 grid(n_splits);
+  const bool g = rows != nullptr;
+  const auto q = (const bf16*)qabs;
+  const auto c = (const bf16*)c_KV;
+  const auto k = (const bf16*)k_R;
+  bf16* po = (bf16*)part_o_v;
+#define MLA_LAUNCH_NW(NW, G)                                                                                  \
+  launch_nw<NW, G>(grid, s, q, c, k, row_stride, num_pages, page_table, max_pages, d.page_size, prefix,      \
+                   split_rec, B, n_splits, part_ml, po, flags, rows, rows_stride)
+  switch (d.n_h / 32) {
+    case 1: if (g) MLA_LAUNCH_NW(1, true); else MLA_LAUNCH_NW(1, false); break;
+    case 2: if (g) MLA_LAUNCH_NW(2, true); else MLA_LAUNCH_NW(2, false); break;
+    case 4: if (g) MLA_LAUNCH_NW(4, true); else MLA_LAUNCH_NW(4, false); break;
+    default: return hipErrorInvalidValue;
   }
+#undef MLA_LAUNCH_NW
   return hipGetLastError();
 }
 

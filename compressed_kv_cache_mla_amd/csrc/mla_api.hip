@@ -633,6 +633,139 @@ mla_status mla_decode_layer(const mla_dims* dims, int32_t B, int32_t d_cq, const
   return st;
 }
 
+// ---------------------------------------------------------------- sparse top-k decode
+namespace {
+
+mla_status check_indexer(int32_t H_I, int32_t d_I, int32_t top_k, const void* q_I, const float* w_I, const void* k_I,
+                         int64_t idx_row_stride, int32_t page_size) {
+  if (d_I != 128) return fail(MLA_ERR_UNSUPPORTED, "d_I=%d: the indexer kernel is built for 128", d_I);
+  if (H_I != 16 && H_I != 32 && H_I != 64) return fail(MLA_ERR_UNSUPPORTED, "H_I=%d not in {16, 32, 64}", H_I);
+  if (top_k < 1) return fail(MLA_ERR_INVALID_ARG, "top_k=%d must be >= 1", top_k);
+  if (!q_I || !w_I || !k_I) return fail(MLA_ERR_INVALID_ARG, "q_I / w_I / k_I is NULL");
+  if (!aligned16(q_I) || !aligned16(k_I) || ((uintptr_t)w_I & 3) != 0)
+    return fail(MLA_ERR_INVALID_ARG, "q_I / k_I not 16-byte aligned or w_I not 4-byte aligned");
+  if (idx_row_stride < d_I || (idx_row_stride * 2) % 16 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "idx_row_stride=%lld must be >= d_I and a multiple of 8", (long long)idx_row_stride);
+  if (page_size < 16 || page_size % 16 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "page_size=%d: the indexer needs a multiple of 16", page_size);
+  return MLA_OK;
+}
+
+int32_t sparse_default_splits(int32_t B, int32_t top_k) {
+  const int64_t want = ((int64_t)B * top_k + 127) / 128;   // about four 32-row tiles per split
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(want, default_splits()));
+}
+
+}  // namespace
+
+size_t mla_indexer_select_workspace_size(int32_t B, int32_t max_pages, int32_t page_size, int32_t top_k) {
+  if (B < 1 || max_pages < 1 || page_size < 1 || top_k < 1) return 0;
+  return mla::select_ws_layout(B, max_pages * page_size, top_k, false).total;
+}
+
+mla_status mla_indexer_select(int32_t B, int32_t H_I, int32_t d_I, int32_t top_k, const void* q_I, const float* w_I,
+                              const void* k_I, int64_t idx_row_stride, int32_t num_pages, int32_t page_size,
+                              const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, float* scores,
+                              int32_t* sel_tok, int32_t* sel_row, int32_t* err_flags, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  mla_status st = check_indexer(H_I, d_I, top_k, q_I, w_I, k_I, idx_row_stride, page_size);
+  if (st != MLA_OK) return st;
+  if (!page_table || !seq_lens || !scores || !sel_tok || !sel_row || !err_flags || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
+  if (((uintptr_t)workspace & 255) != 0) return fail(MLA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if (num_pages < 1 || (int64_t)num_pages * page_size >= ((int64_t)1 << 31))
+    return fail(MLA_ERR_INVALID_ARG, "num_pages=%d out of range", num_pages);
+  if (max_pages < 1 || (int64_t)B * max_pages * page_size >= ((int64_t)1 << 31))
+    return fail(MLA_ERR_INVALID_ARG, "max_pages=%d out of range", max_pages);
+  const mla::SelectWs L = mla::select_ws_layout(B, max_pages * page_size, top_k, false);
+  if (ws_bytes < L.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  const hipError_t e = mla::launch_indexer_select(B, H_I, q_I, w_I, k_I, idx_row_stride, num_pages, page_table,
+                                                  max_pages, page_size, seq_lens, top_k, (char*)workspace, L, scores,
+                                                  sel_tok, sel_row, err_flags, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "indexer / selection launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t mla_sparse_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t max_pages, int32_t top_k,
+                                        int32_t n_splits) {
+  if (check_dims(dims) != MLA_OK || B < 1 || max_pages < 1 || top_k < 1) return 0;
+  if (n_splits <= 0) n_splits = sparse_default_splits(B, top_k);
+  const mla::DecodeWs D = mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims));
+  return D.total + mla::select_ws_layout(B, max_pages * dims->page_size, top_k, true).total;
+}
+
+mla_status mla_sparse_decode(const mla_dims* dims, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
+                             const void* W_UK, const void* W_UV, const void* c_KV, const void* k_R,
+                             int64_t row_stride, int32_t num_pages, const int32_t* page_table, int32_t max_pages,
+                             const int32_t* seq_lens, int32_t H_I, int32_t d_I, int32_t top_k, const void* q_I,
+                             const float* w_I, const void* k_I, int64_t idx_row_stride, float* out, float* lse,
+                             int32_t* sel_tok, void* workspace, size_t ws_bytes, int32_t n_splits,
+                             const mla_decode_opts* opts, void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (dims->dtype != MLA_BF16 || (dims->n_h != 32 && dims->n_h != 64 && dims->n_h != 128) || dims->page_size < 32 ||
+      dims->page_size % 32 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "sparse decode needs bf16, n_h in {32, 64, 128} and page_size a multiple of 32");
+  if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  st = check_indexer(H_I, d_I, top_k, q_I, w_I, k_I, idx_row_stride, dims->page_size);
+  if (st != MLA_OK) return st;
+  if (!q_C || !q_R || !pos_q || !W_UK || !W_UV || !page_table || !seq_lens || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(q_C) || !aligned16(q_R) || !aligned16(W_UK) || !aligned16(W_UV) || !aligned16(out))
+    return fail(MLA_ERR_INVALID_ARG, "q_C / q_R / W_UK / W_UV / out not 16-byte aligned");
+  if (((uintptr_t)workspace & 255) != 0) return fail(MLA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  st = check_pool(dims, c_KV, k_R, row_stride, num_pages);
+  if (st != MLA_OK) return st;
+  if (max_pages < 1 || (int64_t)B * max_pages * dims->page_size >= ((int64_t)1 << 31))
+    return fail(MLA_ERR_INVALID_ARG, "max_pages=%d out of range", max_pages);
+  if ((int64_t)B * top_k >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "B*top_k >= 2^31");
+  if (opts && opts->impl != 0) return fail(MLA_ERR_INVALID_ARG, "opts->impl=%d (sparse decode has one kernel)", opts->impl);
+  if (n_splits <= 0) n_splits = sparse_default_splits(B, top_k);
+  if (n_splits > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d too large", n_splits);
+  const mla::DecodeWs D = mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims));
+  const mla::SelectWs S = mla::select_ws_layout(B, max_pages * dims->page_size, top_k, true);
+  if (ws_bytes < D.total + S.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, D.total + S.total);
+
+  char* ws = (char*)workspace;
+  char* sw = ws + D.total;
+  int32_t* flags = (int32_t*)(ws + D.flags);
+  int32_t* sel_row = (int32_t*)(sw + S.sel_row);
+  hipStream_t s = (hipStream_t)stream;
+  mla::PlanArgs pa;
+  pa.seq_lens = seq_lens;
+  pa.B = B;
+  pa.max_tokens = max_pages * dims->page_size;
+  pa.G = n_splits;
+  pa.prefix = (int32_t*)(ws + D.prefix);
+  pa.split_rec = (int32_t*)(ws + D.splits);
+  pa.flags = flags;
+  pa.page_table = page_table;
+  pa.max_pages = max_pages;
+  pa.page_size = dims->page_size;
+  pa.keep = top_k;
+  pa.gather = true;
+  // query absorption and the plan over the kept counts (it clears the flags),
+  // then the indexer and the selection, the gather attention and the combine
+  hipError_t e = mla::launch_absorb(*dims, B, q_C, q_R, pos_q, W_UK, ws + D.qabs, pa, s);
+  if (e == hipSuccess)
+    e = mla::launch_indexer_select(B, H_I, q_I, w_I, k_I, idx_row_stride, num_pages, page_table, max_pages,
+                                   dims->page_size, seq_lens, top_k, sw, S, (float*)(sw + S.scores),
+                                   sel_tok ? sel_tok : (int32_t*)(sw + S.sel_tok), sel_row, flags, s);
+  if (e == hipSuccess && opts && opts->ev_start) e = hipEventRecord((hipEvent_t)opts->ev_start, s);
+  if (e == hipSuccess)
+    e = mla::launch_decode_mfma(*dims, B, ws + D.qabs, c_KV, k_R, row_stride, num_pages, page_table, max_pages,
+                                pa.prefix, pa.split_rec, n_splits, (float*)(ws + D.part_ml), ws + D.part_o, flags, s,
+                                sel_row, top_k);
+  if (e == hipSuccess && opts && opts->ev_stop) e = hipEventRecord((hipEvent_t)opts->ev_stop, s);
+  if (e == hipSuccess)
+    e = mla::launch_combine(*dims, B, pa.prefix, n_splits, (float*)(ws + D.part_ml), ws + D.part_o, W_UV, out, lse,
+                            nullptr, nullptr, s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "sparse decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- allocation-free decode step

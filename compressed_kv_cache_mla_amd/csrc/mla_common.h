@@ -179,6 +179,10 @@ struct PlanArgs {
   int32_t* flags;
   const int32_t* page_table;
   int32_t max_pages, page_size;
+  // Sparse decode: each sequence keeps at most `keep` tokens (the selection's
+  // list positions); the records then carry no page ids (gather = true).
+  int32_t keep = 0x7fffffff;
+  bool gather = false;
 };
 
 // Decode plan, run by one workgroup of NT threads.  part: NT + cap ints of
@@ -210,7 +214,7 @@ __device__ __forceinline__ void plan_block(const PlanArgs& pa, int32_t* part, in
       atomicOr(pa.flags, MLA_FLAG_BAD_SEQ_LEN);
       n = n < 1 ? 0 : max_tokens;
     }
-    local += n;
+    local += min(n, pa.keep);
   }
   part[tid] = local;
   __syncthreads();
@@ -227,6 +231,7 @@ __device__ __forceinline__ void plan_block(const PlanArgs& pa, int32_t* part, in
   for (int b = beg; b < end; ++b) {
     int32_t n = pa.seq_lens[b];
     n = n < 1 ? 0 : (n > max_tokens ? max_tokens : n);
+    n = min(n, pa.keep);
     pa.prefix[b] = run;
     if (in_lds) pl[b] = run;
     run += n;
@@ -252,7 +257,7 @@ __device__ __forceinline__ void plan_block(const PlanArgs& pa, int32_t* part, in
     const int32_t K = (se - P + DECODE_TT - 1) / DECODE_TT;   // 0 for an empty split
     const int32_t* pt = pa.page_table + (int64_t)lo * pa.max_pages;
     int32_t pg[4] = {0, 0, 0, 0};
-    if (K > 0) {
+    if (K > 0 && !pa.gather) {
       const int32_t k0 = tile_phase(w, K);
       const int32_t k1 = k0 + 1 == K ? 0 : k0 + 1;
 #pragma unroll
@@ -309,11 +314,35 @@ hipError_t launch_decode_simple(const mla_dims& d, int32_t B, const void* qabs, 
                                 const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
                                 int32_t n_splits, float* part_ml, void* part_o, int32_t* flags,
                                 hipStream_t s);
+// rows: NULL (contiguous tokens through the page table), or the sparse
+// decode's kept pool rows, rows[b * rows_stride + i] for list position i
+// (the plan then counts list positions, PlanArgs::keep / gather).
 hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                               const void* k_R, int64_t row_stride, int32_t num_pages,
                               const int32_t* page_table, int32_t max_pages, const int32_t* prefix,
                               const int32_t* split_rec, int32_t n_splits, float* part_ml, void* part_o,
-                              int32_t* flags, hipStream_t s);
+                              int32_t* flags, hipStream_t s, const int32_t* rows = nullptr,
+                              int32_t rows_stride = 0);
+
+// Sparse decode selection (sparse.hip): workspace parts, bytes from the
+// start of the selection area.  nchunks: SEL_CH-token chunks per sequence.
+constexpr int SEL_BINS = 2048;   // radix bins per pass
+constexpr int SEL_CH = 4096;     // tokens per selection workgroup
+struct SelectWs {
+  int32_t nchunks;
+  size_t hist, ticket, st, cnt, scores, sel_tok, sel_row, total;
+};
+// outputs: also room for the scores and the kept tokens / rows (else the
+// caller provides them).
+SelectWs select_ws_layout(int32_t B, int32_t max_tokens, int32_t top_k, bool outputs);
+// Indexer scores (into `scores`, [B, max_pages*page_size] fp32) and the kept
+// tokens and pool rows ([B, top_k] each; the first min(n_b, top_k) entries of
+// row b are written).  ws: the selection area laid out by L.
+hipError_t launch_indexer_select(int32_t B, int32_t H_I, const void* q_I, const float* w_I, const void* k_I,
+                                 int64_t idx_stride, int32_t num_pages, const int32_t* page_table, int32_t max_pages,
+                                 int32_t page_size, const int32_t* seq_lens, int32_t top_k, char* ws,
+                                 const SelectWs& L, float* scores, int32_t* sel_tok, int32_t* sel_row,
+                                 int32_t* flags, hipStream_t s);
 // merge_flags: NULL, or (decode step) the flag area whose word 1 holds the
 // append's flags, to be OR-ed into word 0 and cleared; ext_flags (NULL, or a
 // caller's device word, with merge_flags given) also receives them.

@@ -391,6 +391,70 @@ mla_status mla_decode_layer(const mla_dims* dims, int32_t B, int32_t d_cq, const
                             int32_t n_splits, const mla_decode_opts* opts, void* stream);
 
 /*
+ * Sparse top-k decode (reading of "DeepSeek 架构精讲：从 V3 到 V4",
+ * cyco.top, §4 V3.2 bullet and §6 question 7: a light indexer picks the few
+ * most relevant cached tokens, and attention then looks at those alone).
+ * Every cached token j carries an indexer key k^I_j (d_I bf16) in a paged
+ * pool that shares the latent cache's page table; a decode query carries
+ * H_I indexer heads q^I_h (bf16) and weights w_h (fp32).  The relevance is
+ *   I_j = sum_h w_h * max(0, q^I_h . k^I_j)                  (fp32)
+ * and each sequence keeps its top_k tokens of largest I_j, equal scores
+ * going to the smaller token index (all tokens when seq_len <= top_k).  The
+ * selection is exact integer work on order-preserving keys of the fp32
+ * scores, so it is deterministic.  Supported: d_I = 128, H_I in {16, 32,
+ * 64}, page_size a multiple of 16 (of 32 for mla_sparse_decode).
+ *
+ * mla_indexer_select_workspace_size -- bytes of scratch mla_indexer_select
+ * needs; 0 for invalid sizes.
+ *
+ * mla_indexer_select -- scores and selection only.
+ *   q_I        [B, H_I, d_I]   bf16    device
+ *   w_I        [B, H_I]        fp32    device
+ *   k_I        [num_pages*page_size, idx_row_stride] bf16 device, the key of
+ *              token t of sequence b at row page_table[b][t/page_size] *
+ *              page_size + t % page_size
+ *   page_table [B, max_pages] int32, seq_lens [B] int32    device
+ *   scores     [B, max_pages*page_size] fp32 device out: I_j at [b][j] for
+ *              j < seq_len (the rest untouched)
+ *   sel_tok    [B, top_k] int32 device out: the kept tokens, ascending
+ *   sel_row    [B, top_k] int32 device out: their pool rows
+ *              (entries past min(seq_len, top_k) are left untouched)
+ *   err_flags  int32 device word: MLA_FLAG_BAD_PAGE (page clamped) is OR-ed
+ *              in; seq_len outside [1, max_pages*page_size] is clamped
+ *   workspace  ws_bytes >= mla_indexer_select_workspace_size(), 256-byte
+ *              aligned; needs no initialisation.
+ *
+ * mla_sparse_decode_workspace_size -- bytes of device workspace
+ * mla_sparse_decode needs (n_splits 0 = default); 0 for invalid arguments.
+ *
+ * mla_sparse_decode -- the whole sparse decode: query absorption, indexer
+ * scores, selection, split-KV attention over the kept latent rows only
+ * (each split copies the rows of its list positions straight from the pool),
+ * log-sum-exp combine and the W^UV epilogue.  out / lse are those of
+ * mla_decode with the softmax over the kept tokens.  Arguments as for
+ * mla_decode_ex (bf16, n_h in {32, 64, 128}) and mla_indexer_select; sel_tok
+ * (optional, [B, top_k] int32) receives the kept tokens.  n_splits 0 picks
+ * about one split per 128 kept tokens, at most one per CU.  The error flags
+ * sit in the workspace's first word, as for mla_decode.  opts: ev_start /
+ * ev_stop as for mla_decode_ex; impl must be 0.
+ */
+size_t mla_indexer_select_workspace_size(int32_t B, int32_t max_pages, int32_t page_size, int32_t top_k);
+mla_status mla_indexer_select(int32_t B, int32_t H_I, int32_t d_I, int32_t top_k, const void* q_I,
+                              const float* w_I, const void* k_I, int64_t idx_row_stride, int32_t num_pages,
+                              int32_t page_size, const int32_t* page_table, int32_t max_pages,
+                              const int32_t* seq_lens, float* scores, int32_t* sel_tok, int32_t* sel_row,
+                              int32_t* err_flags, void* workspace, size_t ws_bytes, void* stream);
+size_t mla_sparse_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t max_pages, int32_t top_k,
+                                        int32_t n_splits);
+mla_status mla_sparse_decode(const mla_dims* dims, int32_t B, const void* q_C, const void* q_R,
+                             const int32_t* pos_q, const void* W_UK, const void* W_UV, const void* c_KV,
+                             const void* k_R, int64_t row_stride, int32_t num_pages, const int32_t* page_table,
+                             int32_t max_pages, const int32_t* seq_lens, int32_t H_I, int32_t d_I, int32_t top_k,
+                             const void* q_I, const float* w_I, const void* k_I, int64_t idx_row_stride,
+                             float* out, float* lse, int32_t* sel_tok, void* workspace, size_t ws_bytes,
+                             int32_t n_splits, const mla_decode_opts* opts, void* stream);
+
+/*
  * mla_read_error_flags -- wait for `stream`, then copy the device error flags
  * of a decode workspace (or an append err_flag word) to *flags and clear them.
  */

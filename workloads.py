@@ -316,3 +316,62 @@ class Workload:
             d["q_C"] = f64(self._q_rows("q_C", rows, D_H, cpu))
             d["q_R"] = f64(self._q_rows("q_R", rows, D_R, cpu))
         return d
+
+
+# ---------------------------------------------------------------------------- sparse decode inputs
+D_I = 128    # indexer key width
+
+
+def exact_small_ints(x: torch.Tensor) -> torch.Tensor:
+    """Integers in [-3, 3] from N(0, 1) draws, by comparisons only."""
+    return _steps(x, (0.5, 1.25, 2.0), 1.0)
+
+
+class IndexerInputs:
+    """Indexer keys, queries and head weights of the sparse decode for one
+    Workload (same pages and page table).  Keys: one row of D_I per cached
+    token, N(0, 1) from the generator (by global token id), in a pool of its
+    own laid out like the latent pool.  q^I ~ N(0, 1) per (sequence, head);
+    w_h = min(|x| / 4, 1) for x ~ N(0, 1) (non-negative gates).  exact: keys
+    and q^I integers in [-3, 3], w_h multiples of 1/4 in [0, 2]; every score
+    is then exact in fp32 whatever the summation order."""
+
+    def __init__(self, wl: Workload, H_I: int = 64, exact: bool = False, name: str = "idx"):
+        self.wl, self.H_I, self.exact = wl, H_I, exact
+        c = wl.cfg
+        self.key = lambda part: si.stream_key(c.seed, f"{c.name}/{name}/{part}", wl.layer)  # noqa: E731
+        dev = wl.device
+        ps = c.page_size
+        self.pool = torch.zeros((wl.num_pages * ps, D_I), dtype=torch.bfloat16, device=dev)
+        self.row_stride = D_I
+        seq, pos = wl.token_rows()
+        N = seq.size
+        for i in range(0, N, 65536):
+            g = np.arange(i, min(N, i + 65536))
+            rows = torch.from_numpy(wl.pool_rows(seq[g], pos[g])).to(dev)
+            self.pool[rows] = self.key_rows(torch.from_numpy(g).to(dev))
+        self.q_I = self.query_rows(range(c.B * H_I), dev).reshape(c.B, H_I, D_I)
+        self.w_I = self.weight_rows(range(c.B), dev)
+
+    def key_rows(self, rows, device=None):
+        x = si.normal_rows(self.key("k"), rows, D_I, 1.0, torch.float32, device or self.wl.device)
+        return (exact_small_ints(x) if self.exact else x).to(torch.bfloat16)
+
+    def query_rows(self, rows, device):
+        x = si.normal_rows(self.key("q"), rows, D_I, 1.0, torch.float32, device)
+        return (exact_small_ints(x) if self.exact else x).to(torch.bfloat16)
+
+    def weight_rows(self, rows, device):
+        x = si.normal_rows(self.key("w"), rows, self.H_I, 1.0, torch.float32, device).abs()
+        if self.exact:
+            return _steps(x, (0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0), 0.25).to(torch.float32)
+        return torch.clamp(x * 0.25, max=1.0)
+
+    def oracle_inputs(self, b: int) -> dict:
+        """fp64 q^I, w, and the keys of sequence b's tokens 0 .. n_b - 1 (CPU)."""
+        wl, cpu = self.wl, torch.device("cpu")
+        g0, g1 = int(wl.prefix[b]), int(wl.prefix[b + 1])
+        f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+        return dict(q_I=f64(self.query_rows(range(b * self.H_I, (b + 1) * self.H_I), cpu)),
+                    w_I=f64(self.weight_rows(range(b, b + 1), cpu))[0],
+                    k_I=f64(self.key_rows(range(g0, g1), cpu)))
