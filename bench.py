@@ -20,7 +20,9 @@ append + decode) as one captured HIP graph; `projections` times the query
 path (W^DQ, W^UQ, W^QR) and the output projection W^O, which sit outside the
 step; `prefill` times chunked prefill (new tokens attending causally over
 their sequences); `layer` times the whole attention layer (query path + step
-+ W^O, h -> u); `cpu_baseline` times the fp64 CPU oracle on one whole decode
++ W^O, h -> u); `sparse` times the sparse top-k decode (indexer, selection,
+attention over the kept rows) at batch 4 x 128K and batch 64 x 8K with
+top_k = 2048; `cpu_baseline` times the fp64 CPU oracle on one whole decode
 step of the headline workload.
 """
 from __future__ import annotations
@@ -313,6 +315,87 @@ def cpu_baseline(W, name: str, seconds: float, step_us_gpu: float | None = None)
     return res
 
 
+SPARSE_CONFIGS = [("b4_l131072", 2048), ("b64_l8192", 2048)]   # (workload, top_k)
+
+
+def measure_sparse(torch, mla, W, name: str, top_k: int, H_I: int = 64, reps: int = 20, copies: int = 3):
+    """The sparse top-k decode (mla_sparse_decode) on a decode workload: the
+    indexer scores every cached token (H_I heads, 128-wide bf16 keys), each
+    sequence keeps its top_k, and the attention runs over the kept latent
+    rows.  Copies rotate as for the dense steps (the 134 MB of indexer keys of
+    one copy would fit the Infinity Cache).  Each call is timed with fence-free
+    HIP events; the gather attention kernel with the events the library
+    records around it; the selection alone (mla_indexer_select) separately."""
+    cfg = W.CONFIGS[name]
+    t0 = time.perf_counter()
+    wls = [W.Workload(cfg, layer=i) for i in range(copies)]
+    idxs = [W.IndexerInputs(wl, H_I=H_I) for wl in wls]
+    B, dev = cfg.B, wls[0].device
+    wss = [torch.empty(mla.sparse_decode_workspace_size(wl.dims, B, wl.max_pages, top_k), dtype=torch.uint8,
+                       device=dev) for wl in wls]
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+
+    def run(i, ev=(None, None)):
+        wl, ix = wls[i % copies], idxs[i % copies]
+        mla.sparse_decode(wl.dims, wl.q_C, wl.q_R, wl.pos_q, wl.W_UK, wl.W_UV, wl.c_KV, wl.k_R, wl.row_stride,
+                          wl.num_pages, wl.page_table, wl.seq_lens, ix.q_I, ix.w_I, ix.pool, ix.row_stride, top_k,
+                          wl.out, wl.lse, workspace=wss[i % copies], ev_start=ev[0], ev_stop=ev[1])
+
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    sev = [mla.HipEvent() for _ in range(reps + 1)]
+    kev = [(mla.HipEvent(), mla.HipEvent()) for _ in range(reps)]
+    for i in range(reps):
+        sev[i].record()
+        run(i, kev[i])
+    sev[reps].record()
+    torch.cuda.synchronize()
+    step_us = [1e3 * sev[i].elapsed_ms(sev[i + 1]) for i in range(reps)]
+    attn_us = [1e3 * a.elapsed_ms(b) for a, b in kev]
+    # the selection alone
+    max_tokens = wls[0].max_pages * cfg.page_size
+    scores = torch.empty((B, max_tokens), dtype=torch.float32, device=dev)
+    st = torch.empty((B, top_k), dtype=torch.int32, device=dev)
+    sr = torch.empty((B, top_k), dtype=torch.int32, device=dev)
+    fl = torch.zeros(1, dtype=torch.int32, device=dev)
+    sws = torch.empty(mla.indexer_select_workspace_size(B, wls[0].max_pages, cfg.page_size, top_k),
+                      dtype=torch.uint8, device=dev)
+
+    def sel(i):
+        wl, ix = wls[i % copies], idxs[i % copies]
+        mla.indexer_select(ix.q_I, ix.w_I, ix.pool, ix.row_stride, wl.num_pages, cfg.page_size, wl.page_table,
+                           wl.seq_lens, top_k, scores, st, sr, fl, workspace=sws)
+
+    for i in range(3):
+        sel(i)
+    sev2 = [mla.HipEvent() for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    for i in range(reps):
+        sev2[i].record()
+        sel(i)
+    sev2[reps].record()
+    torch.cuda.synchronize()
+    sel_us = [1e3 * sev2[i].elapsed_ms(sev2[i + 1]) for i in range(reps)]
+    N = int(wls[0].prefix[-1])
+    kept = int(np.minimum(wls[0].n, top_k).sum())
+    idx_bytes = N * (128 * 2 + 4)                       # keys in, scores out
+    attn_bytes = kept * 576 * 2 + B * cfg.n_h * (576 * 2 + 512 * 2 + 8)
+    t_step, t_attn, t_sel = (float(np.median(x)) for x in (step_us, attn_us, sel_us))
+    res = {"workload": name, "B": B, "top_k": top_k, "H_I": H_I, "d_I": 128, "cached_tokens": N, "kept_tokens": kept,
+           "us_per_step_p10_p50_p90": [round(float(x), 1) for x in np.percentile(step_us, [10, 50, 90])],
+           "tokens_per_s": round(B / (t_step * 1e-6), 1),
+           "select_us_p50": round(t_sel, 1), "select_GBps": round(idx_bytes / (t_sel * 1e-6) / 1e9, 1),
+           "attention_us_p50": round(t_attn, 1),
+           "attention_GBps": round(attn_bytes / (t_attn * 1e-6) / 1e9, 1),
+           "alg_bytes": {"indexer_keys_and_scores": idx_bytes, "attention": attn_bytes},
+           "copies_rotated": copies, "build_s": round(build_s, 1)}
+    del wls, idxs, wss
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_l60(torch, mla, W, steps: int, warmup: int, n_splits: int = 0):
     """The 60-layer configuration: B = 128 sequences of 8192 prior tokens, 60
     layers with their own seeded weights, queries and latent caches (72.5 GB
@@ -392,6 +475,7 @@ def main():
     ap.add_argument("--projections-only", default="",
                     help="comma-separated batch sizes: only time the query / output projections at them")
     ap.add_argument("--l60-only", action="store_true", help="only time the 60-layer configuration")
+    ap.add_argument("--sparse-only", action="store_true", help="only time the sparse top-k decode configurations")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM "
                          "byte counters of rocprofv3)")
@@ -422,6 +506,9 @@ def main():
     if args.projections_only:
         print(json.dumps({f"B{b}": measure_projections(torch, mla, int(b))
                           for b in args.projections_only.split(",")}), flush=True)
+        return
+    if args.sparse_only:
+        print(json.dumps({"sparse": [measure_sparse(torch, mla, W, n, k) for n, k in SPARSE_CONFIGS]}), flush=True)
         return
     if args.l60_only:
         print(json.dumps({"l60": measure_l60(torch, mla, W, args.steps, args.warmup, args.splits)}), flush=True)
@@ -550,6 +637,8 @@ def main():
         res["prefill"] = [measure_prefill(torch, mla, *c) for c in PREFILL_CONFIGS]
         # the whole attention layer (query path + decode step + W^O) at the headline workload
         res["layer"] = [measure_layer(torch, mla, W, cfg.name)]
+        # the sparse top-k decode row at the long-context and headline shapes
+        res["sparse"] = [measure_sparse(torch, mla, W, n, k) for n, k in SPARSE_CONFIGS]
         print("# extras done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(W, cfg.name, args.cpu_seconds, ms_per_step * 1e3)

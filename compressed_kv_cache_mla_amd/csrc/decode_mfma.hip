@@ -348,7 +348,10 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
     asm volatile("" : "+v"(ln));
     const int g = wave + NW * gi;
     const int m = (ln >> 3) ^ (g & 1);
-    const int64_t row = GATHER ? *(const int32_t*)(ids + 4 * (8 * g + m)) : resolve_row(td, 8 * g + m, pg0, pg1);
+    // GATHER: the ids come from the selection, which only lists checked
+    // rows; the clamp keeps the copy inside the pool whatever they hold
+    const int64_t row = GATHER ? min(max(*(const int32_t*)(ids + 4 * (8 * g + m)), 0), num_pages * page_size - 1)
+                               : resolve_row(td, 8 * g + m, pg0, pg1);
     return row * stride_b + 16 * ((ln & 7) ^ swz(m));
   };
   auto dma_one = [&](char* kt, int I, int64_t off) __attribute__((always_inline)) {

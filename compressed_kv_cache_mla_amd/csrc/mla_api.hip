@@ -673,6 +673,7 @@ mla_status mla_indexer_select(int32_t B, int32_t H_I, int32_t d_I, int32_t top_k
   if (st != MLA_OK) return st;
   if (!page_table || !seq_lens || !scores || !sel_tok || !sel_row || !err_flags || !workspace)
     return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(scores)) return fail(MLA_ERR_INVALID_ARG, "scores not 16-byte aligned");
   if (((uintptr_t)workspace & 255) != 0) return fail(MLA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   if (num_pages < 1 || (int64_t)num_pages * page_size >= ((int64_t)1 << 31))
     return fail(MLA_ERR_INVALID_ARG, "num_pages=%d out of range", num_pages);

@@ -327,10 +327,10 @@ hipError_t launch_decode_mfma(const mla_dims& d, int32_t B, const void* qabs, co
 // Sparse decode selection (sparse.hip): workspace parts, bytes from the
 // start of the selection area.  nchunks: SEL_CH-token chunks per sequence.
 constexpr int SEL_BINS = 2048;   // radix bins per pass
-constexpr int SEL_CH = 4096;     // tokens per selection workgroup
+constexpr int SEL_CH = 16384;    // tokens per selection workgroup (longer sequences: several)
 struct SelectWs {
   int32_t nchunks;
-  size_t hist, ticket, st, cnt, scores, sel_tok, sel_row, total;
+  size_t hist, st, cnt, scores, sel_tok, sel_row, total;
 };
 // outputs: also room for the scores and the kept tokens / rows (else the
 // caller provides them).

@@ -414,8 +414,8 @@ mla_status mla_decode_layer(const mla_dims* dims, int32_t B, int32_t d_cq, const
  *              token t of sequence b at row page_table[b][t/page_size] *
  *              page_size + t % page_size
  *   page_table [B, max_pages] int32, seq_lens [B] int32    device
- *   scores     [B, max_pages*page_size] fp32 device out: I_j at [b][j] for
- *              j < seq_len (the rest untouched)
+ *   scores     [B, max_pages*page_size] fp32 device out, 16-byte aligned:
+ *              I_j at [b][j] for j < seq_len (the rest untouched)
  *   sel_tok    [B, top_k] int32 device out: the kept tokens, ascending
  *   sel_row    [B, top_k] int32 device out: their pool rows
  *              (entries past min(seq_len, top_k) are left untouched)
