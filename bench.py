@@ -52,6 +52,64 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
+COUNTER_WORKLOADS = ("b64_l8192", "b32_l4096", "b64_ragged", "b4_l131072")
+PMC_CMD = ("cd /tmp && timeout -s KILL 120 rocprofv3 --pmc {ctr} --kernel-include-regex {regex} --output-format csv "
+           "-d <out>/{name} -o run -- python3 <repo>/bench.py {args}")
+PMC_BENCH_ARGS = "--no-cpu-baseline --no-extras --no-l60 --configs '' --workload {w} --steps 3 --warmup 1"
+
+
+def write_counters(out_dir: str):
+    """profiles/decode_attention_counters.json from rocprofv3 counter passes
+    already run into out_dir (the commands recorded in the file): the copy
+    calibration of FETCH_SIZE and WRITE_SIZE (a plain 1 GiB device copy) and
+    both counters on the attention kernel of each workload.  Counter values
+    are averaged over the kernel's dispatches."""
+    import csv
+    import glob
+
+    def per_dispatch(name, counter, regex):
+        files = glob.glob(os.path.join(out_dir, name, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter output under {out_dir}/{name}")
+        vals = {}
+        for row in csv.DictReader(open(files[0])):
+            if row["Counter_Name"] == counter and regex in row["Kernel_Name"]:
+                vals[row["Dispatch_Id"]] = vals.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"no {counter} values for {regex} in {files[0]}")
+        return sum(vals.values()) / len(vals), len(vals)
+
+    copy_bytes = 1 << 30
+    cal = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        kib, _ = per_dispatch("copy_" + ctr.split("_")[0].lower(), ctr, "copyBuffer")
+        cal[ctr] = {"copy_bytes": copy_bytes, "counter_kib_per_copy": round(kib, 1),
+                    "bytes_per_counted_kib": round(copy_bytes / kib, 4)}
+    wl = {}
+    for w in COUNTER_WORKLOADS:
+        f, n = per_dispatch(f"{w}_fetch", "FETCH_SIZE", "decode_mfma")
+        wr, _ = per_dispatch(f"{w}_write", "WRITE_SIZE", "decode_mfma")
+        rd = f * cal["FETCH_SIZE"]["bytes_per_counted_kib"]
+        wb = wr * cal["WRITE_SIZE"]["bytes_per_counted_kib"]
+        wl[w] = {"fetch_kib_per_launch": round(f, 1), "write_kib_per_launch": round(wr, 1),
+                 "hbm_read_bytes": int(rd), "hbm_write_bytes": int(wb), "hbm_bytes_per_launch": int(rd + wb),
+                 "launches": n}
+    cmds = {}
+    for w in COUNTER_WORKLOADS:
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            name = f"{w}_{ctr.split('_')[0].lower()}"
+            cmds[name] = PMC_CMD.format(ctr=ctr, regex="decode_mfma", name=name, args=PMC_BENCH_ARGS.format(w=w))
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        name = "copy_" + ctr.split("_")[0].lower()
+        cmds[name] = PMC_CMD.format(ctr=ctr, regex="copyBuffer", name=name, args="--copy-calibration")
+    cmds["summary"] = f"python3 <repo>/bench.py --write-counters <out>"
+    res = {"kernel": "decode_mfma_kernel<4> (split-KV attention)", "kernel_source_sha256_16": kernel_source_hash(),
+           "calibration": cal, "workloads": wl, "commands": cmds}
+    with open(COUNTERS, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res["workloads"]), flush=True)
+
+
 def algorithmic(wl):
     """Algorithmic bytes and flops of one step and of one launch of the
     split-KV attention kernel."""
@@ -476,10 +534,16 @@ def main():
                     help="comma-separated batch sizes: only time the query / output projections at them")
     ap.add_argument("--l60-only", action="store_true", help="only time the 60-layer configuration")
     ap.add_argument("--sparse-only", action="store_true", help="only time the sparse top-k decode configurations")
+    ap.add_argument("--write-counters", default="", metavar="DIR",
+                    help="write profiles/decode_attention_counters.json from the rocprofv3 counter passes in DIR "
+                         "(the commands it records) and exit; needs no GPU")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM "
                          "byte counters of rocprofv3)")
     args = ap.parse_args()
+    if args.write_counters:
+        write_counters(args.write_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: the library and this benchmark run on one GPU; multi-GPU runs are not supported "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
