@@ -16,6 +16,13 @@ namespace {
 
 thread_local std::string g_err;
 
+// Limits every entry point shares: batch rows (B, T), work partitions and
+// pool row strides (elements).  Within them every size and offset below fits
+// its type.
+constexpr int32_t MAX_ROWS = 1 << 20;
+constexpr int32_t MAX_SPLITS = 1 << 20;
+constexpr int64_t MAX_ROW_STRIDE = (int64_t)1 << 24;
+
 mla_status fail(mla_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 mla_status fail(mla_status st, const char* fmt, ...) {
   char buf[512];
@@ -36,6 +43,14 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 int elt_size(const mla_dims* d) { return d->dtype == MLA_FP32 ? 4 : 2; }
 
+// x > 0 and finite, decided on the bits: the library is built with
+// -fno-honor-nans, under which a float comparison may treat a NaN as ordered.
+bool positive_finite(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  return (u >> 31) == 0 && u != 0 && ((u >> 23) & 0xff) != 0xff;
+}
+
 mla_status check_dims(const mla_dims* d) {
   if (!d) return fail(MLA_ERR_INVALID_ARG, "dims is NULL");
   if (d->dtype != MLA_BF16 && d->dtype != MLA_FP32) return fail(MLA_ERR_INVALID_ARG, "bad dtype %d", d->dtype);
@@ -46,21 +61,29 @@ mla_status check_dims(const mla_dims* d) {
   if (d->d_model < 64 || d->d_model % 64 != 0)
     return fail(MLA_ERR_UNSUPPORTED, "d_model=%d must be a positive multiple of 64", d->d_model);
   if (d->page_size < 1) return fail(MLA_ERR_INVALID_ARG, "page_size=%d must be >= 1", d->page_size);
-  if (!(d->softmax_scale > 0.f) || !(d->rope_base > 0.f))
-    return fail(MLA_ERR_INVALID_ARG, "softmax_scale and rope_base must be positive");
+  if (!positive_finite(d->softmax_scale) || !positive_finite(d->rope_base))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale and rope_base must be positive and finite");
   return MLA_OK;
 }
 
 mla_status check_pool(const mla_dims* d, const void* c_KV, const void* k_R, int64_t row_stride, int32_t num_pages) {
   if (!c_KV || !k_R) return fail(MLA_ERR_INVALID_ARG, "c_KV / k_R is NULL");
   if (!aligned16(c_KV) || !aligned16(k_R)) return fail(MLA_ERR_INVALID_ARG, "c_KV / k_R not 16-byte aligned");
-  if (row_stride < mla::D_C || (row_stride * elt_size(d)) % 16 != 0)
-    return fail(MLA_ERR_INVALID_ARG, "row_stride=%lld must be >= 512 and a multiple of 16 bytes",
+  if (row_stride < mla::D_C || row_stride > MAX_ROW_STRIDE || (row_stride * elt_size(d)) % 16 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "row_stride=%lld must be in [512, 2^24] and a multiple of 16 bytes",
                 (long long)row_stride);
   if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages=%d must be >= 1", num_pages);
   if ((int64_t)num_pages * d->page_size >= ((int64_t)1 << 31))
     return fail(MLA_ERR_UNSUPPORTED, "pool holds more than 2^31 rows");
   return MLA_OK;
+}
+
+int32_t default_splits();
+
+// n_splits as the calls take it: <= 0 selects the default; -1 when above the limit.
+int32_t resolve_splits(int32_t n_splits) {
+  if (n_splits <= 0) return default_splits();
+  return n_splits > MAX_SPLITS ? -1 : n_splits;
 }
 
 int32_t default_splits() {
@@ -85,7 +108,7 @@ static mla_status cache_append_impl(const mla_dims* dims, int32_t T, const void*
                                     void* workspace, size_t ws_bytes, void* stream) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (T < 0) return fail(MLA_ERR_INVALID_ARG, "T=%d < 0", T);
+  if (T < 0 || T > MAX_ROWS) return fail(MLA_ERR_INVALID_ARG, "T=%d out of range [0, 2^20]", T);
   if (T == 0) return ok();
   if (!h_t || !W_DKV || !W_KR || !pos || !page_table)
     return fail(MLA_ERR_INVALID_ARG, "null pointer among h_t, W_DKV, W_KR, pos, page_table");
@@ -114,7 +137,7 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t T, const void* h_t, co
 }
 
 size_t mla_cache_append_workspace_size(const mla_dims* dims, int32_t T) {
-  if (check_dims(dims) != MLA_OK || T < 1) return 0;
+  if (check_dims(dims) != MLA_OK || T < 1 || T > MAX_ROWS) return 0;
   return mla::append_workspace_bytes(*dims, T);
 }
 
@@ -128,8 +151,9 @@ mla_status mla_cache_append_ws(const mla_dims* dims, int32_t T, const void* h_t,
 }
 
 size_t mla_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t n_splits) {
-  if (check_dims(dims) != MLA_OK || B < 1) return 0;
-  if (n_splits <= 0) n_splits = default_splits();
+  if (check_dims(dims) != MLA_OK || B < 1 || B > MAX_ROWS) return 0;
+  n_splits = resolve_splits(n_splits);
+  if (n_splits < 0) return 0;
   return mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims)).total;
 }
 
@@ -157,7 +181,7 @@ static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, 
                               void* stream, bool merge_append_flags = false, int32_t* ext_flags = nullptr) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (B < 1 || B > MAX_ROWS) return fail(MLA_ERR_INVALID_ARG, "B=%d out of range [1, 2^20]", B);
   if (!q_C || !q_R || !pos_q || !W_UK || !W_UV || !page_table || !seq_lens || !out || !workspace)
     return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(q_C) || !aligned16(q_R) || !aligned16(W_UK) || !aligned16(W_UV) || !aligned16(out))
@@ -175,8 +199,9 @@ static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, 
     return fail(MLA_ERR_INVALID_ARG, "max_pages=%d out of range", max_pages);
   if ((int64_t)B * max_pages * dims->page_size >= ((int64_t)1 << 31))
     return fail(MLA_ERR_UNSUPPORTED, "B*max_pages*page_size >= 2^31 tokens");
-  if (n_splits <= 0) n_splits = default_splits();
-  if (n_splits > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d too large", n_splits);
+  const int32_t n_req = n_splits;
+  n_splits = resolve_splits(n_splits);
+  if (n_splits < 0) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d above 2^20", n_req);
   const mla::DecodeWs L = mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims), step != nullptr);
   if (ws_bytes < L.total)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
@@ -247,8 +272,9 @@ mla_status mla_decode_ex(const mla_dims* dims, int32_t B, const void* q_C, const
 }
 
 size_t mla_decode_step_workspace_size(const mla_dims* dims, int32_t B, int32_t n_splits) {
-  if (check_dims(dims) != MLA_OK || B < 1) return 0;
-  if (n_splits <= 0) n_splits = default_splits();
+  if (check_dims(dims) != MLA_OK || B < 1 || B > MAX_ROWS) return 0;
+  n_splits = resolve_splits(n_splits);
+  if (n_splits < 0) return 0;
   return mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims), true).total;
 }
 
@@ -325,7 +351,7 @@ OutputPlan output_plan(const mla_dims& d, int32_t B) {
 mla_status check_query_dims(const mla_dims* dims, int32_t B, int32_t d_cq) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (B < 1 || B > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "B=%d out of range", B);
+  if (B < 1 || B > MAX_ROWS) return fail(MLA_ERR_INVALID_ARG, "B=%d out of range [1, 2^20]", B);
   if (d_cq < 0 || d_cq > 65536 || d_cq % 128 != 0)
     return fail(MLA_ERR_UNSUPPORTED, "d_cq=%d must be 0 or a positive multiple of 128 up to 65536", d_cq);
   if (dims->dtype == MLA_BF16 && dims->d_model % 128 != 0)
@@ -514,8 +540,9 @@ static PrefillWs prefill_ws_layout(const mla_dims& d, int32_t T, int32_t max_pag
 }
 
 size_t mla_prefill_workspace_size(const mla_dims* dims, int32_t T, int32_t max_pages, int32_t n_splits) {
-  if (check_dims(dims) != MLA_OK || T < 1 || T > (1 << 20) || max_pages < 1) return 0;
-  if (n_splits <= 0) n_splits = default_splits();
+  if (check_dims(dims) != MLA_OK || T < 1 || T > MAX_ROWS || max_pages < 1) return 0;
+  n_splits = resolve_splits(n_splits);
+  if (n_splits < 0) return 0;
   return prefill_ws_layout(*dims, T, max_pages, n_splits).total;
 }
 
@@ -526,7 +553,7 @@ mla_status mla_prefill(const mla_dims* dims, int32_t T, const void* h, const voi
                        void* workspace, size_t ws_bytes, int32_t n_splits, void* stream) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (T < 1 || T > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "T=%d out of range", T);
+  if (T < 1 || T > MAX_ROWS) return fail(MLA_ERR_INVALID_ARG, "T=%d out of range [1, 2^20]", T);
   // every check of the decode that follows is made here too, before anything is launched
   if (!h || !W_DKV || !W_KR || !seq_id || !pos || !page_table || !workspace || !q_C || !q_R || !W_UK || !W_UV ||
       !out)
@@ -536,8 +563,9 @@ mla_status mla_prefill(const mla_dims* dims, int32_t T, const void* h, const voi
     return fail(MLA_ERR_INVALID_ARG, "h / weights / q_C / q_R / out not 16-byte aligned");
   if (num_seqs < 1 || max_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_seqs and max_pages must be >= 1");
   if (((uintptr_t)workspace & 255) != 0) return fail(MLA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-  if (n_splits <= 0) n_splits = default_splits();
-  if (n_splits > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d too large", n_splits);
+  const int32_t n_req = n_splits;
+  n_splits = resolve_splits(n_splits);
+  if (n_splits < 0) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d above 2^20", n_req);
   st = check_pool(dims, c_KV, k_R, row_stride, num_pages);
   if (st != MLA_OK) return st;
   if ((int64_t)T * max_pages * dims->page_size >= ((int64_t)1 << 31))
@@ -585,7 +613,8 @@ static LayerWs layer_ws_layout(const mla_dims& d, int32_t B, int32_t d_cq, int32
 
 size_t mla_decode_layer_workspace_size(const mla_dims* dims, int32_t B, int32_t d_cq, int32_t n_splits) {
   if (check_query_dims(dims, B, d_cq) != MLA_OK) return 0;
-  if (n_splits <= 0) n_splits = default_splits();
+  n_splits = resolve_splits(n_splits);
+  if (n_splits < 0) return 0;
   return layer_ws_layout(*dims, B, d_cq, n_splits).total;
 }
 
@@ -610,8 +639,9 @@ mla_status mla_decode_layer(const mla_dims* dims, int32_t B, int32_t d_cq, const
   if (max_pages < 1 || (int64_t)B * max_pages * dims->page_size >= ((int64_t)1 << 31))
     return fail(MLA_ERR_INVALID_ARG, "max_pages=%d out of range", max_pages);
   if (opts && opts->impl != 0 && opts->impl != 1) return fail(MLA_ERR_INVALID_ARG, "opts->impl=%d", opts->impl);
-  if (n_splits <= 0) n_splits = default_splits();
-  if (n_splits > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d too large", n_splits);
+  const int32_t n_req = n_splits;
+  n_splits = resolve_splits(n_splits);
+  if (n_splits < 0) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d above 2^20", n_req);
   const LayerWs L = layer_ws_layout(*dims, B, d_cq, n_splits);
   if (ws_bytes < L.total) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   char* ws = (char*)workspace;
@@ -644,8 +674,9 @@ mla_status check_indexer(int32_t H_I, int32_t d_I, int32_t top_k, const void* q_
   if (!q_I || !w_I || !k_I) return fail(MLA_ERR_INVALID_ARG, "q_I / w_I / k_I is NULL");
   if (!aligned16(q_I) || !aligned16(k_I) || ((uintptr_t)w_I & 3) != 0)
     return fail(MLA_ERR_INVALID_ARG, "q_I / k_I not 16-byte aligned or w_I not 4-byte aligned");
-  if (idx_row_stride < d_I || (idx_row_stride * 2) % 16 != 0)
-    return fail(MLA_ERR_INVALID_ARG, "idx_row_stride=%lld must be >= d_I and a multiple of 8", (long long)idx_row_stride);
+  if (idx_row_stride < d_I || idx_row_stride > MAX_ROW_STRIDE || idx_row_stride % 8 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "idx_row_stride=%lld must be in [d_I, 2^24] and a multiple of 8",
+                (long long)idx_row_stride);
   if (page_size < 16 || page_size % 16 != 0)
     return fail(MLA_ERR_UNSUPPORTED, "page_size=%d: the indexer needs a multiple of 16", page_size);
   return MLA_OK;
@@ -659,7 +690,8 @@ int32_t sparse_default_splits(int32_t B, int32_t top_k) {
 }  // namespace
 
 size_t mla_indexer_select_workspace_size(int32_t B, int32_t max_pages, int32_t page_size, int32_t top_k) {
-  if (B < 1 || max_pages < 1 || page_size < 1 || top_k < 1) return 0;
+  if (B < 1 || B > MAX_ROWS || max_pages < 1 || page_size < 1 || top_k < 1) return 0;
+  if ((int64_t)B * max_pages * page_size >= ((int64_t)1 << 31)) return 0;
   return mla::select_ws_layout(B, max_pages * page_size, top_k, false).total;
 }
 
@@ -668,7 +700,7 @@ mla_status mla_indexer_select(int32_t B, int32_t H_I, int32_t d_I, int32_t top_k
                               const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, float* scores,
                               int32_t* sel_tok, int32_t* sel_row, int32_t* err_flags, void* workspace,
                               size_t ws_bytes, void* stream) {
-  if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (B < 1 || B > MAX_ROWS) return fail(MLA_ERR_INVALID_ARG, "B=%d out of range [1, 2^20]", B);
   mla_status st = check_indexer(H_I, d_I, top_k, q_I, w_I, k_I, idx_row_stride, page_size);
   if (st != MLA_OK) return st;
   if (!page_table || !seq_lens || !scores || !sel_tok || !sel_row || !err_flags || !workspace)
@@ -690,7 +722,9 @@ mla_status mla_indexer_select(int32_t B, int32_t H_I, int32_t d_I, int32_t top_k
 
 size_t mla_sparse_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t max_pages, int32_t top_k,
                                         int32_t n_splits) {
-  if (check_dims(dims) != MLA_OK || B < 1 || max_pages < 1 || top_k < 1) return 0;
+  if (check_dims(dims) != MLA_OK || B < 1 || B > MAX_ROWS || max_pages < 1 || top_k < 1) return 0;
+  if ((int64_t)B * max_pages * dims->page_size >= ((int64_t)1 << 31)) return 0;
+  if (n_splits > MAX_SPLITS) return 0;
   if (n_splits <= 0) n_splits = sparse_default_splits(B, top_k);
   const mla::DecodeWs D = mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims));
   return D.total + mla::select_ws_layout(B, max_pages * dims->page_size, top_k, true).total;
@@ -708,7 +742,7 @@ mla_status mla_sparse_decode(const mla_dims* dims, int32_t B, const void* q_C, c
   if (dims->dtype != MLA_BF16 || (dims->n_h != 32 && dims->n_h != 64 && dims->n_h != 128) || dims->page_size < 32 ||
       dims->page_size % 32 != 0)
     return fail(MLA_ERR_UNSUPPORTED, "sparse decode needs bf16, n_h in {32, 64, 128} and page_size a multiple of 32");
-  if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (B < 1 || B > MAX_ROWS) return fail(MLA_ERR_INVALID_ARG, "B=%d out of range [1, 2^20]", B);
   st = check_indexer(H_I, d_I, top_k, q_I, w_I, k_I, idx_row_stride, dims->page_size);
   if (st != MLA_OK) return st;
   if (!q_C || !q_R || !pos_q || !W_UK || !W_UV || !page_table || !seq_lens || !out || !workspace)
@@ -722,8 +756,8 @@ mla_status mla_sparse_decode(const mla_dims* dims, int32_t B, const void* q_C, c
     return fail(MLA_ERR_INVALID_ARG, "max_pages=%d out of range", max_pages);
   if ((int64_t)B * top_k >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "B*top_k >= 2^31");
   if (opts && opts->impl != 0) return fail(MLA_ERR_INVALID_ARG, "opts->impl=%d (sparse decode has one kernel)", opts->impl);
+  if (n_splits > MAX_SPLITS) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d above 2^20", n_splits);
   if (n_splits <= 0) n_splits = sparse_default_splits(B, top_k);
-  if (n_splits > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "n_splits=%d too large", n_splits);
   const mla::DecodeWs D = mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims));
   const mla::SelectWs S = mla::select_ws_layout(B, max_pages * dims->page_size, top_k, true);
   if (ws_bytes < D.total + S.total)
@@ -830,7 +864,7 @@ mla_status mla_decode_step_noalloc(const mla_dims* dims, int32_t B, const void* 
                                    void* stream) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  if (B < 1 || B > MAX_ROWS) return fail(MLA_ERR_INVALID_ARG, "B=%d out of range [1, 2^20]", B);
   const int32_t n_splits = default_splits();
   const size_t need = mla::decode_ws_layout(B, dims->n_h, n_splits, elt_size(dims), true).total;
   if (need > NOALLOC_SCRATCH_BYTES)

@@ -602,7 +602,7 @@ __global__ void __launch_bounds__(SEL_NT) select_write_kernel(const float* __res
 
 SelectWs select_ws_layout(int32_t B, int32_t max_tokens, int32_t top_k, bool outputs) {
   SelectWs w;
-  w.nchunks = (max_tokens + SEL_CH - 1) / SEL_CH;
+  w.nchunks = (int32_t)(((int64_t)max_tokens + SEL_CH - 1) / SEL_CH);
   size_t off = 0;
   w.hist = off;    off += align256((size_t)B * SEL_BINS * 4);
   w.st = off;      off += align256((size_t)B * 16);
@@ -627,7 +627,7 @@ hipError_t launch_indexer_select(int32_t B, int32_t H_I, const void* q_I, const 
   int32_t* st = (int32_t*)(ws + L.st);
   int32_t* cnt = (int32_t*)(ws + L.cnt);
   select_clear_kernel<<<B, 256, 0, s>>>(hist);
-  const dim3 gi((max_tokens + IDX_TOK_WG - 1) / IDX_TOK_WG, B);
+  const dim3 gi((uint32_t)(((int64_t)max_tokens + IDX_TOK_WG - 1) / IDX_TOK_WG), B);
   const bf16* q = (const bf16*)q_I;
   const bf16* k = (const bf16*)k_I;
 #define MLA_INDEXER(HB)                                                                                       \

@@ -43,6 +43,11 @@
  *
  * Errors: host-side checks (null or misaligned pointers, unsupported dims,
  * bad sizes, small workspace) return a status without launching anything.
+ * Limits shared by every call: batch rows B or T <= 2^20, n_splits <= 2^20,
+ * row strides <= 2^24 elements, tokens addressed by one call (B * max_pages *
+ * page_size, and num_pages * page_size) < 2^31; softmax_scale and rope_base
+ * positive and finite.  The workspace-size functions return 0 outside these
+ * limits.
  * Values that live on the device (positions, sequence lengths, page ids) are
  * checked by the kernels: an out-of-range value is clamped so that no access
  * leaves its buffer, and a flag is raised in the workspace (decode) or in the
