@@ -33,17 +33,19 @@
 //    blocks) = K_tile . Q^T with v_mfma_f32_16x16x32_bf16.  The wave's query
 //    block (32 heads x 576 bf16) is split: latent dims 0..447 in 112 VGPRs,
 //    dims 448..575 (incl. the RoPE part) staged once per sequence in LDS.
-//  * Online softmax in the owner wave, in log2 units (q~ carries
-//    softmax_scale*log2(e)).  The running reference max only moves when a
-//    tile's max exceeds it by more than RESCALE_T (so p <= 2^RESCALE_T), which
-//    makes the O rescale rare; the accumulators are zeroed when a segment
-//    ends.  Row reductions use v_permlane16/32_swap.  P (bf16) and
-//    the rescale factors go to LDS.
-//  * P.V: wave w owns 512/NW latent columns for all heads (O^T blocks of 32
-//    latent columns x 32 heads, v_mfma_f32_32x32x16_bf16, 256 fp32
-//    accumulators kept in AGPRs).  Block dblk = 2g + p holds the columns of
-//    chunks 8g + p + {0, 2, 4, 6}.  V^T fragments are read from the staged
-//    tile with ds_read_b64_tr_b16; P^T fragments with ds_read_b128.
+//  * Online softmax in the wave that owns the heads, in log2 units (q~
+//    carries softmax_scale*log2(e)).  The running reference max only moves
+//    when a tile's max exceeds it by more than RESCALE_T (so p <=
+//    2^RESCALE_T), which makes the O rescale rare; the accumulators are
+//    zeroed when a segment ends.  Row reductions use v_permlane16/32_swap.
+//  * P.V: the same wave owns those 32 heads' O over all 512 latent columns
+//    (O^T blocks of 32 latent columns x 32 heads, v_mfma_f32_32x32x16_bf16,
+//    256 fp32 accumulators kept in AGPRs).  P never leaves the wave: one
+//    v_permlane16_swap per dword turns the score accumulators (bf16) into
+//    the P^T operand, so no wave waits for another between the scores and
+//    P.V, and the tile-top barrier is the only one per tile.  Block dblk =
+//    2g + p holds the columns of chunks 8g + p + {0, 2, 4, 6}; its V^T
+//    fragments are read from the staged tile with ds_read_b64_tr_b16.
 //  * At the end of each (sequence, range) segment the unnormalised O~ (bf16),
 //    the reference max m and the sum l (fp32) go to the segment's partial slot;
 //    O~ is transposed through the wave's staged-query LDS area so that every
@@ -57,7 +59,6 @@ constexpr int TT = DECODE_TT;           // cached rows per tile (32)
 constexpr int NINSTR = TT * 72 / 64;    // 36 copy instructions (blocks of 1 KB) per tile
 constexpr int TILEB = NINSTR * 1024;    // 36,864 bytes per tile buffer (36 windows of 1 KB)
 constexpr int PGOFF = TILEB;            // the tile's two page ids follow its windows
-constexpr int PSTR = 80;                // bytes per head row of P in LDS (32 bf16 + pad)
 constexpr float RESCALE_T = 24.0f;      // log2 headroom before the reference max moves
 constexpr int KS = D_K / 32;            // 18 K-steps of 32 for the score MFMA
 constexpr int KS_REG = 14;              // K-steps of the query block kept in VGPRs
@@ -246,15 +247,11 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
                    int32_t rows_stride) {
   constexpr int NH = 32 * NW;
   constexpr int IPW = NINSTR / NW;              // DMA instructions per wave (NW divides 36)
-  constexpr int DB = 16 / NW;                   // 32-wide latent blocks per wave in P.V
-  constexpr int PIECES = DB / 4;                // 128-column pieces of a wave's latent columns
+  constexpr int DB = 16;                        // 32-wide latent blocks of a wave's O (all 512 columns)
   __shared__ __attribute__((aligned(1024))) char kt0[TILEB + 4 * TT];
   __shared__ __attribute__((aligned(1024))) char kt1[TILEB + 4 * TT];
   __shared__ __attribute__((aligned(1024))) char kt2[TILEB + 4 * TT];
   __shared__ __attribute__((aligned(1024))) char ql[NH * QLB];   // query dims 448..575, swizzled
-  __shared__ __attribute__((aligned(16))) char pl[NH * PSTR];
-  __shared__ float alpha_l[NH];
-  __shared__ int resc_l[NW];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -295,8 +292,6 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
         v_off[p][hi] = 16 * (576 * rgb + 8 * (m ^ rgb) + ((p + 2 * y) ^ swz(m))) + 8 * (lane & 1);
       }
   }
-  // P^T fragment: head 32hb + (lane&31), tokens kc*16 + 8*(lane>>5)
-  const int p_off = (lane & 31) * PSTR + (lane >> 5) * 16;
 
   Cursor cur;
   const cint_t rec = (cint_t)split_rec + SPLIT_REC * split;
@@ -370,7 +365,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 
   // ---- state
   bf16x8 q[2][KS_REG];
-  f32x16 o[NW][DB];
+  f32x16 o[DB];
   // Softmax state of the lane's heads 32w + 16hb + (lane&15): the reference
   // max (the same in the four lanes that hold a head) and this lane's part of
   // the sum (its tokens only; the four parts are added when the segment ends).
@@ -415,11 +410,9 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
 
   // ---- prologue: tiles 0 and 1 in flight, page ids of tile 2 in flight
 #pragma unroll
-  for (int hb = 0; hb < NW; ++hb)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ACC_ZERO(o[hb][db][r]);
+    for (int r = 0; r < 16; ++r) ACC_ZERO(o[db][r]);
   m_ref[0] = m_ref[1] = -INFINITY;
   l_sum[0] = l_sum[1] = 0.f;
   // The query loads go first; the pages of the first two tiles come with the
@@ -553,83 +546,67 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
         }
       }
       any_resc = __builtin_amdgcn_readfirstlane(__any(any_resc) ? 1 : 0);
-      if (any_resc && lane < 16) {
-        alpha_l[32 * wave + lane] = alpha[0];
-        alpha_l[32 * wave + 16 + lane] = alpha[1];
-      }
     }
-    if (lane == 0) resc_l[wave] = any_resc;
+    // P in bf16, and the B fragments of P^T for the two 16-token chunks.
+    // Lane (g, c) = (lane>>4, lane&15) holds P of tokens 16tb + 4g + i for
+    // heads c (x[0]) and 16 + c (x[1]); the 32x32x16 B operand wants, in lane
+    // (g, c), head 16(g&1) + c and tokens 16tb + 8(g>>1) + 0..7.  Rows g and
+    // g^1 trade x[0] of the odd row for x[1] of the even row
+    // (v_permlane16_swap), after which (x[0], x[1]) is that fragment.
+    bf16x8 pf[2];
+    float sum[2] = {0.f, 0.f};
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float sum = 0.f;
-      const int head = 32 * wave + 16 * hb + (lane & 15);
+    for (int tb = 0; tb < 2; ++tb) {
+      bf16x4 x[2];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        bf16x4 pb;
+      for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = __builtin_amdgcn_exp2f(s[tb][hb][i] - m_ref[hb]);
-          pb[i] = (bf16)p;
-          sum += p;
+          x[hb][i] = (bf16)p;
+          sum[hb] += p;
         }
-        *(bf16x4*)(pl + head * PSTR + (16 * tb + 4 * (lane >> 4)) * 2) = pb;
-      }
-      l_sum[hb] = l_sum[hb] * alpha[hb] + sum;
+      const u32x2 x0 = __builtin_bit_cast(u32x2, x[0]), x1 = __builtin_bit_cast(u32x2, x[1]);
+      const auto w0 = __builtin_amdgcn_permlane16_swap(x0[0], x1[0], false, false);
+      const auto w1 = __builtin_amdgcn_permlane16_swap(x0[1], x1[1], false, false);
+      pf[tb] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w1[0], w0[1], w1[1]});
     }
-    // P, alpha visible to all waves.  Only LDS traffic is waited for: a plain
-    // __syncthreads would also wait for the tiles in flight.
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
-    __builtin_amdgcn_s_barrier();
+    l_sum[0] = l_sum[0] * alpha[0] + sum[0];
+    l_sum[1] = l_sum[1] * alpha[1] + sum[1];
 
-    // ---- rescale O where an owner moved its reference max (rare).  Only the
-    // heads of the owners that raised their flag are scaled: alpha_l holds
-    // this tile's factors for those owners alone (the others' are stale).
-    // (Four waves test one combined flag, fewer test one flag per owner: the
-    // forms the register allocator fits best.)
-    int resc = NW == 4 ? 0 : 1;
-    if (NW == 4) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) resc |= resc_l[w];
-    }
-    if (resc) {
-#pragma unroll
-      for (int hb = 0; hb < NW; ++hb) {
-        if (NW == 4 || resc_l[hb]) {
-          const float a = NW != 4 || resc_l[hb] ? alpha_l[32 * hb + (lane & 31)] : 1.f;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ACC_SCALE(o[hb][db][r], a);
-        }
-      }
-    }
-
-    // ---- O^T[d][head] += V^T[d][tok] P^T[tok][head], two 16-token chunks;
-    // both chunks' fragments are read before the first chunk's MFMAs issue
-    bf16x8 pf[2][NW], vf[2][DB];
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-      for (int hb = 0; hb < NW; ++hb)
-        pf[kc][hb] = *(const bf16x8*)(pl + 32 * hb * PSTR + p_off + kc * 32);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int dblk = DB * wave + db;
-        const int base = 1024 * (dblk >> 1) + 18432 * kc;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kt + base + v_off[dblk & 1][0]));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kt + base + v_off[dblk & 1][1]));
-        const bf16x4 lob = __builtin_bit_cast(bf16x4, lo), hib = __builtin_bit_cast(bf16x4, hi);
-        vf[kc][db][0] = lob[0]; vf[kc][db][1] = lob[1]; vf[kc][db][2] = lob[2]; vf[kc][db][3] = lob[3];
-        vf[kc][db][4] = hib[0]; vf[kc][db][5] = hib[1]; vf[kc][db][6] = hib[2]; vf[kc][db][7] = hib[3];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    // ---- rescale O where the reference max moved (rare): the lane's
+    // accumulators all belong to head lane&31 = 16((lane>>4)&1) + (lane&15)
+    if (any_resc) {
+      const float a = (lane & 16) ? alpha[1] : alpha[0];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int hb = 0; hb < NW; ++hb) ACC_MFMA(o[hb][db], vf[kc][db], pf[kc][hb]);
+        for (int r = 0; r < 16; ++r) ACC_SCALE(o[db][r], a);
+    }
+
+    // ---- O^T[d][head] += V^T[d][tok] P^T[tok][head] for the wave's 32 heads
+    // and all 512 latent columns: 2 chunks x 16 blocks, V^T fragments read
+    // from the staged tile VR steps ahead of their MFMA.
+    constexpr int VR = 4;
+    constexpr int NSTEP = 2 * DB;
+    bf16x8 vf[VR];
+    auto load_v = [&](int step) __attribute__((always_inline)) {
+      const int kc = step / DB, dblk = step % DB;
+      const int base = 1024 * (dblk >> 1) + 18432 * kc;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kt + base + v_off[dblk & 1][0]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kt + base + v_off[dblk & 1][1]));
+      const bf16x4 lob = __builtin_bit_cast(bf16x4, lo), hib = __builtin_bit_cast(bf16x4, hi);
+      bf16x8& v = vf[step % VR];
+      v[0] = lob[0]; v[1] = lob[1]; v[2] = lob[2]; v[3] = lob[3];
+      v[4] = hib[0]; v[5] = hib[1]; v[6] = hib[2]; v[7] = hib[3];
+    };
+#pragma unroll
+    for (int st = 0; st < VR - 1; ++st) load_v(st);
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      if (st + VR - 1 < NSTEP) load_v(st + VR - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      ACC_MFMA(o[st % DB], vf[st % VR], pf[st / DB]);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -647,10 +624,9 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       const int wh = ln & 31;                                   // head row written by this lane
       char* const wrow = stg + wh * 256 + (ln >> 5) * 8;
       const int rh = ln >> 4, rc = ln & 15;                     // head (mod 4) and chunk read
+      {
 #pragma unroll
-      for (int hb = 0; hb < NW; ++hb) {
-#pragma unroll
-        for (int pc = 0; pc < PIECES; ++pc) {
+        for (int pc = 0; pc < DB / 4; ++pc) {
 #pragma unroll
           for (int dq = 0; dq < 4; ++dq) {
             const int db = 4 * pc + dq;
@@ -660,10 +636,10 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
               // latent column 8*(8g + p + 2*r4) + 4*(lane>>5) + r%4: chunk
               // 8*(dq>>1) + (dq&1) + 2*r4 of this 128-column piece, half lane>>5
               float v0, v1, v2, v3;
-              ACC_READ(v0, o[hb][db][4 * r4]);
-              ACC_READ(v1, o[hb][db][4 * r4 + 1]);
-              ACC_READ(v2, o[hb][db][4 * r4 + 2]);
-              ACC_READ(v3, o[hb][db][4 * r4 + 3]);
+              ACC_READ(v0, o[db][4 * r4]);
+              ACC_READ(v1, o[db][4 * r4 + 1]);
+              ACC_READ(v2, o[db][4 * r4 + 2]);
+              ACC_READ(v3, o[db][4 * r4 + 3]);
               bf16x4 v;
               v[0] = (bf16)v0;
               v[1] = (bf16)v1;
@@ -677,7 +653,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
           for (int k = 0; k < 8; ++k) {
             const int h = 4 * k + rh;
             const bf16x8 v = *(const bf16x8*)(stg + h * 256 + ((rc ^ (h & 15)) << 4));
-            bf16* dst = part_o + (slot * NH + 32 * hb + h) * D_C + (D_C / NW) * wave + 128 * pc + 8 * rc;
+            bf16* dst = part_o + (slot * NH + 32 * wave + h) * D_C + 128 * pc + 8 * rc;
             *(bf16x8*)dst = v;
           }
         }
@@ -695,11 +671,9 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       l_sum[0] = l_sum[1] = 0.f;
       // the next segment accumulates from zero
 #pragma unroll
-      for (int hb = 0; hb < NW; ++hb)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) ACC_ZERO(o[hb][db][r]);
+        for (int r = 0; r < 16; ++r) ACC_ZERO(o[db][r]);
       // the next segment's query, loaded and waited for here (once per
       // segment) so that no query load is in flight during a later tile
       if (t_n1.n > 0) {
