@@ -72,29 +72,48 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i's
-// chunk lands at LDS byte lds_base + 16*i.  Issued through asm so that the
-// compiler's wait-count pass does not see an LDS write in flight: with one
-// visible it drains every LDS wait to zero, which would serialise the
-// fragment reads below.  The instruction has no result register; its
-// completion is awaited explicitly (vmcnt(0) + barrier before the tile is
-// read), and the memory clobber keeps LDS accesses on their side of it.
-// m0 (which holds the LDS base) is saved and restored around the copy, with
-// the one wait state required between an m0 write and an LDS-DMA load.
+// HBM -> LDS copies (global_load_lds).  m0 holds the LDS base of a copy; the
+// instruction reads it when it leaves the wave's memory queue, so an m0 write
+// right behind a copy waits for that.  m0 is therefore written before each
+// copy and not restored after it (declared clobbered: the compiler sets it
+// again where it needs it), with the one wait state required between an m0
+// write and an LDS-DMA load.  Issued through asm so that the compiler's
+// wait-count pass does not see an LDS write in flight: with one visible it
+// drains every LDS wait to zero, which would serialise the fragment reads
+// below.  The instructions have no result register; their completion is
+// awaited explicitly (vmcnt(0) + barrier before the tile is read), and the
+// memory clobber keeps LDS accesses on their side of them.
+//
+// 16 bytes per lane: lane i's chunk lands at LDS byte lds_base + 16*i.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  uint32_t m0_save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(m0_save)
-               : "v"(gptr), "s"(lds_base)
-               : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_base)
+               : "memory", "m0");
 }
-// The same for 4 bytes per active lane (lane i -> lds_base + 4*i).
+// 4 bytes per active lane (lane i -> lds_base + 4*i).
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
-  uint32_t m0_save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(m0_save)
-               : "v"(gptr), "s"(lds_base)
-               : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(gptr), "s"(lds_base)
+               : "memory", "m0");
+}
+// dma16 of line j of a row group: the copy reads gptr + 128*j (j < 8: the
+// offset is the instruction's immediate) or gptr (j = 8), so one address
+// register pair serves all nine lines.  The immediate offset is added to the
+// LDS address as well, so m0 is set that much lower.
+__device__ __forceinline__ void dma16_line(const char* gptr, int j, uint32_t lds_base) {
+#define MLA_DMA_LINE(OFF)                                                                                 \
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:" #OFF : : "v"(gptr), \
+               "s"(lds_base - (OFF))                                                                     \
+               : "memory", "m0")
+  switch (j) {
+    case 1: MLA_DMA_LINE(128); break;
+    case 2: MLA_DMA_LINE(256); break;
+    case 3: MLA_DMA_LINE(384); break;
+    case 4: MLA_DMA_LINE(512); break;
+    case 5: MLA_DMA_LINE(640); break;
+    case 6: MLA_DMA_LINE(768); break;
+    case 7: MLA_DMA_LINE(896); break;
+    default: MLA_DMA_LINE(0); break;
+  }
+#undef MLA_DMA_LINE
 }
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(lds_void*)p;
@@ -349,17 +368,18 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
                                : resolve_row(td, 8 * g + m, pg0, pg1);
     return row * stride_b + 16 * ((ln & 7) ^ swz(m));
   };
-  auto dma_one = [&](char* kt, int I, int64_t off) __attribute__((always_inline)) {
+  auto dma_one = [&](char* kt, int I, const char* pc, const char* pk) __attribute__((always_inline)) {
     const int gi = I / 9, j = I % 9, g = wave + NW * gi;
-    const char* src = j < 8 ? (const char*)c_KV + off + 128 * j : (const char*)k_R + off;
-    dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(kt) + (9 * g + j) * 1024));
+    dma16_line(j < 8 ? pc : pk, j, __builtin_amdgcn_readfirstlane(lds_addr(kt) + (9 * g + j) * 1024));
   };
   auto issue_dma = [&](char* kt, const TileDesc& td, int32_t pg0, int32_t pg1) __attribute__((always_inline)) {
 #pragma unroll
     for (int gi = 0; gi < 4 / NW; ++gi) {
       const int64_t off = dma_src(td, gi, pg0, pg1, kt + PGOFF);
+      const char* pc = (const char*)c_KV + off;
+      const char* pk = (const char*)k_R + off;
 #pragma unroll
-      for (int j = 0; j < 9; ++j) dma_one(kt, 9 * gi + j, off);
+      for (int j = 0; j < 9; ++j) dma_one(kt, 9 * gi + j, pc, pk);
     }
   };
 
@@ -461,11 +481,16 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
     // t_n2's copy instructions are spread over the score K-steps below, so
     // that the four waves do not queue them all at once
     const bool copy = t_n2.n > 0;
-    int64_t doff[4 / NW];
+    const char* dpc[4 / NW];
+    const char* dpk[4 / NW];
     {
       const int2 pg = *(const int2*)(kt_issue + PGOFF);
 #pragma unroll
-      for (int gi = 0; gi < 4 / NW; ++gi) doff[gi] = copy ? dma_src(t_n2, gi, pg.x, pg.y, kt_issue + PGOFF) : 0;
+      for (int gi = 0; gi < 4 / NW; ++gi) {
+        const int64_t off = copy ? dma_src(t_n2, gi, pg.x, pg.y, kt_issue + PGOFF) : 0;
+        dpc[gi] = (const char*)c_KV + off;
+        dpk[gi] = (const char*)k_R + off;
+      }
     }
 
     // ---- scores S^T[token][head] for this wave's 32 heads (2 x 2 blocks of 16x16)
@@ -503,7 +528,7 @@ decode_mfma_kernel(const bf16* __restrict__ qabs, const bf16* __restrict__ c_KV,
       }
       if (copy) {
 #pragma unroll
-        for (int I = ks * IPW / KS; I < (ks + 1) * IPW / KS; ++I) dma_one(kt_issue, I, doff[I / 9]);
+        for (int I = ks * IPW / KS; I < (ks + 1) * IPW / KS; ++I) dma_one(kt_issue, I, dpc[I / 9], dpk[I / 9]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
