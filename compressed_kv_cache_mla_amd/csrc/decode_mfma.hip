@@ -84,7 +84,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // awaited explicitly (vmcnt(0) + barrier before the tile is read), and the
 // memory clobber keeps LDS accesses on their side of them.
 //
+// m0 is a register the compiler reserves, and clang warns that a clobber of
+// it is not preserved for the compiler; nothing the compiler emits in this
+// file reads m0 (tests/test_isa_m0.py checks the built code for that), so
+// the warning is silenced for these three helpers.
+//
 // 16 bytes per lane: lane i's chunk lands at LDS byte lds_base + 16*i.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_base)
                : "memory", "m0");
@@ -115,6 +122,7 @@ __device__ __forceinline__ void dma16_line(const char* gptr, int j, uint32_t lds
   }
 #undef MLA_DMA_LINE
 }
+#pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(lds_void*)p;
 }
