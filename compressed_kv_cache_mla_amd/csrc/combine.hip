@@ -160,6 +160,7 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
   merge_step_flags(merge_flags, ext_flags);
   __shared__ __attribute__((aligned(16))) char ol[CS * D_C * 2];
   __shared__ int empty_l[CS];
+  __shared__ __attribute__((aligned(16))) float red[CS == 16 ? 16 * 64 * 8 : 4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.x;
@@ -174,18 +175,23 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
 #pragma unroll
     for (int ks = 0; ks < D_C / 32; ++ks) wpre[ks] = *(const bf16x8*)(wr + 32 * ks);
   }
-  for (int bb = wave; bb < CS; bb += 16) {
+  // Few sequences in the block (CS = 16 only): WPS waves share a sequence,
+  // each merging every WPS-th slot, and their sums are added in LDS in a
+  // fixed order; otherwise one wave merges a whole sequence.
+  const int WPS = CS == 16 && nb <= 8 ? (nb <= 1 ? 16 : nb <= 2 ? 8 : nb <= 4 ? 4 : 2) : 1;
+  if (WPS > 1) {
+    const int bb = wave / WPS, pp = wave % WPS;
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int empty = 1;
     if (bb < nb) {
       const int b = b0 + bb;
       const int64_t sb = prefix[b], n = prefix[b + 1] - sb;
-      if (n <= 0 && lse && lane == 0) lse[(int64_t)b * n_h + h] = -INFINITY;
+      if (n <= 0 && lse && lane == 0 && pp == 0) lse[(int64_t)b * n_h + h] = -INFINITY;
       if (n > 0) {
         empty = 0;
         const int64_t w0 = split_of(sb, N, G), w1 = split_of(sb + n - 1, N, G);
         const int cnt = (int)(w1 - w0 + 1);
-        const float* ml = part_ml + ((w0 + b) * n_h + h) * 2;   // slot w0 + b + i at ml + 2*n_h*i
+        const float* ml = part_ml + ((w0 + b) * n_h + h) * 2;
         const int64_t mstride = (int64_t)2 * n_h;
         float mx = -INFINITY;
         for (int i = lane; i < cnt; i += 64) mx = fmaxf(mx, ml[i * mstride]);
@@ -194,21 +200,21 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
         for (int i = lane; i < cnt; i += 64) L += exp2f(ml[i * mstride] - mx) * ml[i * mstride + 1];
         L = wave_sum64(L);
         const float invL = 1.f / L;
-        if (lse && lane == 0) lse[(int64_t)b * n_h + h] = (mx + log2f(L)) * 0.69314718055994531f;
-        const bf16* po = part_o + ((w0 + b) * n_h + h) * D_C + 8 * lane;   // slot i at po + n_h*D_C*i
+        if (lse && lane == 0 && pp == 0) lse[(int64_t)b * n_h + h] = (mx + log2f(L)) * 0.69314718055994531f;
+        const bf16* po = part_o + ((w0 + b) * n_h + h) * D_C + 8 * lane;
         const int64_t sstride = (int64_t)n_h * D_C;
         for (int i0 = 0; i0 < cnt; i0 += 64) {
           const int m = min(64, cnt - i0);
           const float wl = lane < m ? exp2f(ml[(i0 + lane) * mstride] - mx) * invL : 0.f;
-          for (int i = 0; i < m; i += CB) {
+          for (int i = pp; i < m; i += WPS * CB) {
             bf16x8 v[CB];
 #pragma unroll
             for (int u = 0; u < CB; ++u)
-              if (i + u < m) v[u] = *(const bf16x8*)(po + sstride * (i0 + i + u));
+              if (i + u * WPS < m) v[u] = *(const bf16x8*)(po + sstride * (i0 + i + u * WPS));
 #pragma unroll
             for (int u = 0; u < CB; ++u)
-              if (i + u < m) {
-                const float wg = __shfl(wl, i + u);
+              if (i + u * WPS < m) {
+                const float wg = __shfl(wl, i + u * WPS);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) a[k] = fmaf(wg, (float)v[u][k], a[k]);
               }
@@ -216,11 +222,77 @@ __global__ void __launch_bounds__(1024) combine_mfma_kernel(int32_t B, int32_t n
         }
       }
     }
-    bf16x8 r;
+    float4* rw = (float4*)(red + (wave * 64 + lane) * 8);
+    rw[0] = float4{a[0], a[1], a[2], a[3]};
+    rw[1] = float4{a[4], a[5], a[6], a[7]};
+    __syncthreads();
+    {
+      const int sq = wave;   // sequence column written by this wave
+      float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (sq < nb) {
+        for (int q = 0; q < WPS; ++q) {
+          const float4* rr = (const float4*)(red + ((sq * WPS + q) * 64 + lane) * 8);
+          const float4 x0 = rr[0], x1 = rr[1];
+          t[0] += x0.x; t[1] += x0.y; t[2] += x0.z; t[3] += x0.w;
+          t[4] += x1.x; t[5] += x1.y; t[6] += x1.z; t[7] += x1.w;
+        }
+      }
+      bf16x8 r;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) r[k] = (bf16)a[k];
-    *(bf16x8*)(ol + bb * 1024 + ((lane ^ (bb & 15)) << 4)) = r;
-    if (lane == 0) empty_l[bb] = empty;
+      for (int k = 0; k < 8; ++k) r[k] = (bf16)t[k];
+      *(bf16x8*)(ol + sq * 1024 + ((lane ^ (sq & 15)) << 4)) = r;
+      if (lane == 0 && pp == 0 && bb < CS) empty_l[bb] = empty;
+      if (lane == 0 && sq >= nb) empty_l[sq] = 1;
+    }
+  } else {
+    for (int bb = wave; bb < CS; bb += 16) {
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      int empty = 1;
+      if (bb < nb) {
+        const int b = b0 + bb;
+        const int64_t sb = prefix[b], n = prefix[b + 1] - sb;
+        if (n <= 0 && lse && lane == 0) lse[(int64_t)b * n_h + h] = -INFINITY;
+        if (n > 0) {
+          empty = 0;
+          const int64_t w0 = split_of(sb, N, G), w1 = split_of(sb + n - 1, N, G);
+          const int cnt = (int)(w1 - w0 + 1);
+          const float* ml = part_ml + ((w0 + b) * n_h + h) * 2;   // slot w0 + b + i at ml + 2*n_h*i
+          const int64_t mstride = (int64_t)2 * n_h;
+          float mx = -INFINITY;
+          for (int i = lane; i < cnt; i += 64) mx = fmaxf(mx, ml[i * mstride]);
+          mx = wave_max64(mx);
+          float L = 0.f;
+          for (int i = lane; i < cnt; i += 64) L += exp2f(ml[i * mstride] - mx) * ml[i * mstride + 1];
+          L = wave_sum64(L);
+          const float invL = 1.f / L;
+          if (lse && lane == 0) lse[(int64_t)b * n_h + h] = (mx + log2f(L)) * 0.69314718055994531f;
+          const bf16* po = part_o + ((w0 + b) * n_h + h) * D_C + 8 * lane;   // slot i at po + n_h*D_C*i
+          const int64_t sstride = (int64_t)n_h * D_C;
+          for (int i0 = 0; i0 < cnt; i0 += 64) {
+            const int m = min(64, cnt - i0);
+            const float wl = lane < m ? exp2f(ml[(i0 + lane) * mstride] - mx) * invL : 0.f;
+            for (int i = 0; i < m; i += CB) {
+              bf16x8 v[CB];
+  #pragma unroll
+              for (int u = 0; u < CB; ++u)
+                if (i + u < m) v[u] = *(const bf16x8*)(po + sstride * (i0 + i + u));
+  #pragma unroll
+              for (int u = 0; u < CB; ++u)
+                if (i + u < m) {
+                  const float wg = __shfl(wl, i + u);
+  #pragma unroll
+                  for (int k = 0; k < 8; ++k) a[k] = fmaf(wg, (float)v[u][k], a[k]);
+                }
+            }
+          }
+        }
+      }
+      bf16x8 r;
+  #pragma unroll
+      for (int k = 0; k < 8; ++k) r[k] = (bf16)a[k];
+      *(bf16x8*)(ol + bb * 1024 + ((lane ^ (bb & 15)) << 4)) = r;
+      if (lane == 0) empty_l[bb] = empty;
+    }
   }
   __syncthreads();
   if (wave >= D_H / 16) return;

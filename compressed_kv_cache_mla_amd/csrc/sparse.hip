@@ -158,39 +158,19 @@ __device__ void pick_digit(const int32_t* bins, bool from_global, int32_t* st_b,
   }
 }
 
-// Clears every sequence's global histogram before the first pass.
-__global__ void __launch_bounds__(256) select_clear_kernel(int32_t* __restrict__ hist) {
-  int4* h = (int4*)(hist + (int64_t)blockIdx.x * SEL_BINS);
-  for (int i = threadIdx.x; i < SEL_BINS / 4; i += 256) h[i] = int4{0, 0, 0, 0};
-}
-
-// Picks pass PASS's digit of sequence blockIdx.x from its global histogram
-// (filled by the previous kernel), then clears that histogram for the next
-// pass.  Pass 0 also records sequences that keep every token.
-template <int PASS>
-__global__ void __launch_bounds__(256) select_pick_kernel(const int32_t* __restrict__ seq_lens, int32_t max_tokens,
-                                                          int32_t top_k, int32_t* __restrict__ hist,
-                                                          int32_t* __restrict__ st) {
-  __shared__ int32_t part[256];
-  const int32_t b = blockIdx.x;
-  const int32_t n = clamp_len(seq_lens[b], max_tokens);
-  if (n <= top_k) {
-    if (PASS == 0 && threadIdx.x == 0) {
-      st[4 * b + 0] = 0;
-      st[4 * b + 1] = 0;
-      st[4 * b + 2] = 1;
-    }
-    return;
+// Clears every sequence's three global histograms (one per radix pass)
+// before the first pass.
+__global__ void __launch_bounds__(256) select_clear_kernel(int32_t* __restrict__ hist, int32_t B) {
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    int4* h = (int4*)(hist + ((int64_t)pass * B + blockIdx.x) * SEL_BINS);
+    for (int i = threadIdx.x; i < SEL_BINS / 4; i += 256) h[i] = int4{0, 0, 0, 0};
   }
-  int32_t* hb = hist + (int64_t)b * SEL_BINS;
-  pick_digit<PASS, 256>(hb, true, st + 4 * b, top_k, part);
-  __syncthreads();
-  for (int i = threadIdx.x; i < SEL_BINS; i += 256) hb[i] = 0;
 }
 
 // Relevance scores of one 1024-token range of one sequence (blockIdx.y), and
 // the histogram of the first radix digit of its scores (added to the
-// sequence's global histogram; select_pick_kernel<0> reads it).
+// sequence's pass-0 global histogram, which select_hist_kernel<1> reads).
 template <int HB>
 __global__ void __launch_bounds__(256) indexer_kernel(const bf16* __restrict__ q_I, const float* __restrict__ w_I,
                                                       const bf16* __restrict__ k_I, int64_t idx_stride,
@@ -314,22 +294,39 @@ __global__ void __launch_bounds__(256) indexer_kernel(const bf16* __restrict__ q
 }
 
 // Radix pass PASS (1 or 2) over one SEL_CH-token chunk of one sequence.
-// local (a single chunk per sequence): the workgroup picks the digit from its
-// own histogram; otherwise it adds its histogram to the sequence's global
-// one and select_pick_kernel<PASS> follows.
+// The digit of the pass before comes from that pass's global histogram,
+// picked by every workgroup of the sequence (they all find the same); with a
+// single chunk per sequence (local) pass 2 instead starts from the state
+// pass 1 left.  local: the workgroup then picks this pass's digit from its
+// own histogram and stores the resulting state; otherwise it adds its
+// histogram to the sequence's global one of this pass (the next kernel picks
+// from it), and chunk 0 stores the state before this pass.
+// State planes (st, {key bits fixed, ties still to take, every token kept}
+// per sequence): 0 after pass 0, 1 after pass 1, 2 final.  Sequences that
+// keep every token get {0, 0, 1} in plane 2 here.
 template <int PASS>
 __global__ void __launch_bounds__(SEL_NT) select_hist_kernel(const float* __restrict__ scores, int32_t max_tokens,
                                                           const int32_t* __restrict__ seq_lens, int32_t top_k,
-                                                          int32_t* __restrict__ hist, int32_t* __restrict__ st,
-                                                          bool local) {
+                                                          int32_t* __restrict__ hist, int32_t B,
+                                                          int32_t* __restrict__ st, bool local) {
   using D = Digit<PASS>;
   __shared__ int32_t h[SEL_BINS];
   __shared__ int32_t part[SEL_NT];
+  __shared__ int32_t st_l[4];
   const int32_t b = blockIdx.y;
   const int tid = threadIdx.x;
   const int32_t n = clamp_len(seq_lens[b], max_tokens);
-  if (n <= top_k) return;   // every token kept
-  const uint32_t fixed = (uint32_t)st[4 * b];
+  if (n <= top_k) {   // every token kept
+    if (PASS == 1 && blockIdx.x == 0 && tid < 3) st[(2 * B + b) * 4 + tid] = tid == 2 ? 1 : 0;
+    return;
+  }
+  if (tid < 3) st_l[tid] = PASS == 1 || !local ? (PASS == 1 ? 0 : st[b * 4 + tid]) : st[(B + b) * 4 + tid];
+  __syncthreads();
+  if (PASS == 1 || !local) {
+    pick_digit<PASS - 1, SEL_NT>(hist + ((int64_t)(PASS - 1) * B + b) * SEL_BINS, true, st_l, top_k, part);
+    __syncthreads();
+  }
+  const uint32_t fixed = (uint32_t)st_l[0];
   for (int i = tid; i < SEL_BINS; i += SEL_NT) h[i] = 0;
   __syncthreads();
   const int32_t c0 = blockIdx.x * SEL_CH, c1 = min(c0 + SEL_CH, n);
@@ -356,11 +353,14 @@ __global__ void __launch_bounds__(SEL_NT) select_hist_kernel(const float* __rest
   }
   __syncthreads();
   if (local) {
-    pick_digit<PASS, SEL_NT>(h, false, st + 4 * b, top_k, part);
+    pick_digit<PASS, SEL_NT>(h, false, st_l, top_k, part);
+    __syncthreads();
+    if (tid < 3) st[((PASS == 1 ? 1 : 2) * B + b) * 4 + tid] = st_l[tid];
   } else {
-    int32_t* hb = hist + (int64_t)b * SEL_BINS;
+    int32_t* hb = hist + ((int64_t)PASS * B + b) * SEL_BINS;
     for (int i = tid; i < SEL_BINS; i += SEL_NT)
       if (h[i]) atomicAdd(&hb[i], h[i]);
+    if (blockIdx.x == 0 && tid < 3) st[((PASS - 1) * B + b) * 4 + tid] = st_l[tid];
   }
 }
 
@@ -388,16 +388,29 @@ __device__ __forceinline__ int32_t block_excl_sum(int32_t v, int32_t* wsum, int3
 }
 
 // Kept tokens of one chunk: {key > T, key == T}, or {all, 0}.
+// Several chunks per sequence only: the last digit is first picked from the
+// pass-2 global histogram (by every workgroup of the sequence), and chunk 0
+// stores the final state (plane 2) for select_write_kernel.
 __global__ void __launch_bounds__(SEL_NT) select_count_kernel(const float* __restrict__ scores, int32_t max_tokens,
-                                                           const int32_t* __restrict__ seq_lens,
-                                                           const int32_t* __restrict__ st, int32_t* __restrict__ cnt,
+                                                           const int32_t* __restrict__ seq_lens, int32_t top_k,
+                                                           const int32_t* __restrict__ hist, int32_t B,
+                                                           int32_t* __restrict__ st, int32_t* __restrict__ cnt,
                                                            int32_t nchunks) {
   __shared__ int32_t wsum[2][SEL_NT / 64];
+  __shared__ int32_t part[SEL_NT];
+  __shared__ int32_t st_l[4];
   const int32_t b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t n = clamp_len(seq_lens[b], max_tokens);
-  const bool all = st[4 * b + 2] != 0;
-  const uint32_t T = (uint32_t)st[4 * b];
+  const bool all = n <= top_k;
+  if (!all) {
+    if (tid < 3) st_l[tid] = st[(B + b) * 4 + tid];
+    __syncthreads();
+    pick_digit<2, SEL_NT>(hist + ((int64_t)2 * B + b) * SEL_BINS, true, st_l, top_k, part);
+    __syncthreads();
+    if (blockIdx.x == 0 && tid < 3) st[(2 * B + b) * 4 + tid] = st_l[tid];
+  }
+  const uint32_t T = all ? 0u : (uint32_t)st_l[0];
   const int32_t c0 = blockIdx.x * SEL_CH, c1 = min(c0 + SEL_CH, n);
   int32_t gt = 0, eq = 0;
   const float* sb = scores + (int64_t)b * max_tokens;
@@ -610,8 +623,8 @@ SelectWs select_ws_layout(int32_t B, int32_t max_tokens, int32_t top_k, bool out
   SelectWs w;
   w.nchunks = (int32_t)(((int64_t)max_tokens + SEL_CH - 1) / SEL_CH);
   size_t off = 0;
-  w.hist = off;    off += align256((size_t)B * SEL_BINS * 4);
-  w.st = off;      off += align256((size_t)B * 16);
+  w.hist = off;    off += align256((size_t)3 * B * SEL_BINS * 4);   // one histogram per radix pass
+  w.st = off;      off += align256((size_t)3 * B * 16);             // one state per pass
   w.cnt = off;     off += align256((size_t)B * w.nchunks * 8);
   w.scores = w.sel_tok = w.sel_row = 0;
   if (outputs) {
@@ -632,7 +645,7 @@ hipError_t launch_indexer_select(int32_t B, int32_t H_I, const void* q_I, const 
   int32_t* hist = (int32_t*)(ws + L.hist);
   int32_t* st = (int32_t*)(ws + L.st);
   int32_t* cnt = (int32_t*)(ws + L.cnt);
-  select_clear_kernel<<<B, 256, 0, s>>>(hist);
+  select_clear_kernel<<<B, 256, 0, s>>>(hist, B);
   const dim3 gi((uint32_t)(((int64_t)max_tokens + IDX_TOK_WG - 1) / IDX_TOK_WG), B);
   const bf16* q = (const bf16*)q_I;
   const bf16* k = (const bf16*)k_I;
@@ -648,17 +661,13 @@ hipError_t launch_indexer_select(int32_t B, int32_t H_I, const void* q_I, const 
 #undef MLA_INDEXER
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  select_pick_kernel<0><<<B, 256, 0, s>>>(seq_lens, max_tokens, top_k, hist, st);
   const dim3 gs(L.nchunks, B);
   const bool local = L.nchunks == 1;   // one workgroup per sequence picks its own digits
-  select_hist_kernel<1><<<gs, SEL_NT, 0, s>>>(scores, max_tokens, seq_lens, top_k, hist, st, local);
-  if (!local) select_pick_kernel<1><<<B, 256, 0, s>>>(seq_lens, max_tokens, top_k, hist, st);
-  select_hist_kernel<2><<<gs, SEL_NT, 0, s>>>(scores, max_tokens, seq_lens, top_k, hist, st, local);
-  if (!local) {
-    select_pick_kernel<2><<<B, 256, 0, s>>>(seq_lens, max_tokens, top_k, hist, st);
-    select_count_kernel<<<gs, SEL_NT, 0, s>>>(scores, max_tokens, seq_lens, st, cnt, L.nchunks);
-  }
-  select_write_kernel<<<gs, SEL_NT, 0, s>>>(scores, max_tokens, seq_lens, top_k, st, cnt, L.nchunks, page_table,
+  select_hist_kernel<1><<<gs, SEL_NT, 0, s>>>(scores, max_tokens, seq_lens, top_k, hist, B, st, local);
+  select_hist_kernel<2><<<gs, SEL_NT, 0, s>>>(scores, max_tokens, seq_lens, top_k, hist, B, st, local);
+  if (!local)
+    select_count_kernel<<<gs, SEL_NT, 0, s>>>(scores, max_tokens, seq_lens, top_k, hist, B, st, cnt, L.nchunks);
+  select_write_kernel<<<gs, SEL_NT, 0, s>>>(scores, max_tokens, seq_lens, top_k, st + 2 * B * 4, cnt, L.nchunks, page_table,
                                             max_pages, page_size, num_pages, sel_tok, sel_row, flags);
   return hipGetLastError();
 }
