@@ -263,6 +263,23 @@ def test_bf16_page_permutation_is_bitwise_invariant():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("B,n_h", [(1, 128), (2, 128), (3, 128), (5, 128), (8, 128), (20, 64)])
+def test_bf16_few_sequences_many_splits(B, n_h):
+    """Blocks of the combine holding at most 8 sequences, where several waves
+    share one sequence's slots (16, 8, 4 or 2 per sequence; B = 20 at 64 heads
+    leaves 4 in its second block), with slot counts above one 64-slot chunk
+    and a ragged last chunk; sequence 1 holds only the query token."""
+    cfg = W.scaled(W.CONFIGS["b64_ragged"], name=f"few_b{B}_h{n_h}", B=B, n_h=n_h, d_model=512,
+                   lens=(2000, 9000), seed=5200 + B)
+    _say(f"case {cfg.name}")
+    if B >= 3:
+        base = cfg.context_lengths
+        cfg.context_lengths = lambda: np.where(np.arange(B) == 1, 0, base())  # noqa: E731
+    for n_splits in (97, 300, 1000):
+        wl = W.Workload(cfg, n_splits=n_splits)
+        _check_decode(wl, range(B))
+
+
 def test_bf16_deterministic_and_split_invariant():
     cfg = W.scaled(W.CONFIGS["b64_ragged"], name="splits", d_model=256, B=4, lens=(500, 3000), seed=6)
     _say("case determinism / splits")
