@@ -8,6 +8,9 @@ attention over the latent cache, combine, W^UV epilogue).  Inputs are
 resident in HBM before timing starts.  To keep the 256 MB Infinity Cache from
 serving repeated reads, steps rotate over several independent copies of the
 workload (own weights, queries and cache) whose total size exceeds it.
+Before its warm-up steps each measurement runs the same calls back to back,
+untimed, for --settle seconds (default 0.5), so that the GPU, idle during
+the workload's set-up, has reached its steady clocks when timing starts.
 
 Prints one JSON line.  The headline workload is batch 64 at 8K context
 (b64_l8192); `value` is its decode tokens/s (B sequences per step);
@@ -55,7 +58,7 @@ def kernel_source_hash() -> str:
 COUNTER_WORKLOADS = ("b64_l8192", "b32_l4096", "b64_ragged", "b4_l131072")
 PMC_CMD = ("cd /tmp && timeout -s KILL 120 rocprofv3 --pmc {ctr} --kernel-include-regex {regex} --output-format csv "
            "-d <out>/{name} -o run -- python3 <repo>/bench.py {args}")
-PMC_BENCH_ARGS = "--no-cpu-baseline --no-extras --no-l60 --configs '' --workload {w} --steps 3 --warmup 1"
+PMC_BENCH_ARGS = "--no-cpu-baseline --no-extras --no-l60 --configs '' --workload {w} --steps 3 --warmup 1 --settle 0"
 
 
 def write_counters(out_dir: str):
@@ -147,6 +150,30 @@ def measured_copy_gbps(torch) -> float:
     return 2 * n / (best * 1e-3) / 1e9
 
 
+SETTLE_S = 0.5   # default; --settle
+
+
+def settle(torch, fn, seconds: float) -> int:
+    """Run fn(i) (one whole call of what is about to be timed) back to back
+    for about `seconds` of wall time, before the warm-up and the timed calls.
+    An MI355X coming from idle (workload set-up leaves it idle for seconds)
+    takes some tens of milliseconds of load to reach its steady clocks: at
+    B = 64, L = 8192 the first 50 steps after 6 warm-up steps averaged 224 us,
+    later blocks of 50 fell to 194 us after about 400 steps, with or without
+    events recorded inside them.  Untimed, like the warm-up; the timed region
+    still holds exactly the requested steps.  Returns the calls made."""
+    t0 = time.perf_counter()
+    n = 0
+    while seconds > 0:
+        for _ in range(16):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return n
+
+
 def measure_projections(torch, mla, B: int, n_h: int = 128, d_model: int = 5120, d_cq: int = 1536, reps: int = 20):
     """The weight-streaming projections around the attention at batch B
     (DeepSeek-V2 sizes; d_cq = 1536, a choice: the pages give no query rank):
@@ -180,6 +207,7 @@ def measure_projections(torch, mla, B: int, n_h: int = 128, d_model: int = 5120,
             ("query_project", lambda x: mla.query_project(dims, x["h"], x["W_DQ"], x["W_UQ"], x["W_QR"], q_C, q_R, wq),
              q_bytes),
             ("output_project", lambda x: mla.output_project(dims, x["o"], x["W_O"], u, wo), o_bytes)):
+        settle(torch, lambda i: fn(sets[i % 3]), SETTLE_S)
         for i in range(6):
             fn(sets[i % 3])
         torch.cuda.synchronize()
@@ -221,6 +249,7 @@ def measure_layer(torch, mla, W, name: str, d_cq: int = 1536, reps: int = 20, co
                              wl.pos_q, wl.c_KV, wl.k_R, wl.row_stride, wl.num_pages, wl.page_table, wl.seq_lens, u,
                              wl.lse, ws)
         runs.append(call)
+    settle(torch, lambda i: runs[i % copies](), SETTLE_S)
     for i in range(4):
         runs[i % copies]()
     torch.cuda.synchronize()
@@ -276,6 +305,8 @@ def measure_prefill(torch, mla, B: int, L: int, T: int, n_h: int = 128, d_model:
     def call():
         mla.prefill(dims, c_h, W_DKV, W_KR, q_C, q_R, c_seq, c_pos, W_UK, W_UV, pool[:, :512], pool[:, 512:], 576,
                     num_pages, pt, out, workspace=ws)
+
+    settle(torch, lambda i: call(), SETTLE_S)
     for _ in range(3):
         call()
     torch.cuda.synchronize()
@@ -400,6 +431,7 @@ def measure_sparse(torch, mla, W, name: str, top_k: int, H_I: int = 64, reps: in
                           wl.num_pages, wl.page_table, wl.seq_lens, ix.q_I, ix.w_I, ix.pool, ix.row_stride, top_k,
                           wl.out, wl.lse, workspace=wss[i % copies], ev_start=ev[0], ev_stop=ev[1])
 
+    settle(torch, run, SETTLE_S)
     for i in range(3):
         run(i)
     torch.cuda.synchronize()
@@ -484,6 +516,7 @@ def measure_l60(torch, mla, W, steps: int, warmup: int, n_splits: int = 0):
     with torch.cuda.graph(g):
         for wl in layers:
             wl.step()
+    settle(torch, lambda i: g.replay(), SETTLE_S)
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -511,10 +544,14 @@ def measure_l60(torch, mla, W, steps: int, warmup: int, n_splits: int = 0):
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed back-to-back calls before each warm-up, so that the GPU runs at its "
+                         "steady clocks (0 = none)")
     ap.add_argument("--workload", default="b64_l8192",
                     help="headline workload (default: batch 64, 8K context, the shape the target is stated on)")
     ap.add_argument("--configs", default="b32_l4096,b64_ragged,b4_l131072",
@@ -541,6 +578,7 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy three times (reference for the HBM "
                          "byte counters of rocprofv3)")
     args = ap.parse_args()
+    SETTLE_S = args.settle
     if args.write_counters:
         write_counters(args.write_counters)
         return
@@ -604,6 +642,7 @@ def main():
             else:
                 wl.step(ev_start=evs[0], ev_stop=evs[1], impl=args.impl)
 
+        settled = settle(torch, step, args.settle)
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
@@ -628,6 +667,7 @@ def main():
         dist = {"step_us_p10_p50_p90": [round(float(x), 2) for x in np.percentile(step_us, [10, 50, 90])],
                 "kernel_us_p10_p50_p90": [round(float(x), 2) for x in np.percentile(kern_us, [10, 50, 90])]}
         del wls
+        dist["settle_steps"] = settled
         return (first, alg, copies, t_start.elapsed_time(t_stop) / steps, sum(kern_us) / len(kern_us), wall,
                 dist)
 
@@ -652,7 +692,7 @@ def main():
     torch.cuda.empty_cache()
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle_s": args.settle, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if cfg.dtype == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "B": B, "context_tokens_per_seq": int(cfg.lens) if not isinstance(
             cfg.lens, (tuple, list)) else list(cfg.lens), "cached_tokens": alg["N"], "n_h": cfg.n_h, "d_h": 128,
