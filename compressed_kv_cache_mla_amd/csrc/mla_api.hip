@@ -173,12 +173,22 @@ struct StepAppendIn {
   void* o_packed;   // optional: the combine also writes out as the output projection's packed bf16 activations
 };
 
+// The decode layer's query path fused with the absorption: q^C = W^UQ c^Q is
+// formed by the absorption launch from the packed c^Q (rows padded to a
+// multiple of 64) and the packed W^UQ; q_C is then not read.
+struct FusedQuery {
+  const void* cQ_packed;
+  const void* W_UQ_packed;
+  int32_t d_cq;
+};
+
 static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
                               const void* W_UK, const void* W_UV, const void* c_KV, const void* k_R,
                               int64_t row_stride, int32_t num_pages, const int32_t* page_table, int32_t max_pages,
                               const int32_t* seq_lens, float* out, float* lse, void* workspace, size_t ws_bytes,
                               int32_t n_splits, const mla_decode_opts* opts, const StepAppendIn* step,
-                              void* stream, bool merge_append_flags = false, int32_t* ext_flags = nullptr) {
+                              void* stream, bool merge_append_flags = false, int32_t* ext_flags = nullptr,
+                              const FusedQuery* fq = nullptr) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (B < 1 || B > MAX_ROWS) return fail(MLA_ERR_INVALID_ARG, "B=%d out of range [1, 2^20]", B);
@@ -235,7 +245,9 @@ static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, 
                              (mla::bf16*)c_KV, (mla::bf16*)k_R, row_stride, mla::rope_table(dims->rope_base),
                              flags + 1};
     e = mla::launch_step_prep(*dims, B, step->h_new, step->W_DKV, step->W_KR, q_C, q_R, pos_q, W_UK, qabs, pa,
-                              (float*)(ws + L.app_part), (int32_t*)(ws + L.app_cnt), dst, s);
+                              (float*)(ws + L.app_part), (int32_t*)(ws + L.app_cnt), dst, s, fq == nullptr);
+    if (e == hipSuccess && fq)
+      e = mla::launch_absorb_fused(*dims, B, fq->d_cq, fq->cQ_packed, fq->W_UQ_packed, q_R, pos_q, W_UK, qabs, s);
   } else {
     if (step)
       e = mla::launch_append(*dims, B, step->h_new, step->W_DKV, step->W_KR, nullptr, pos_q, page_table, B,
@@ -404,9 +416,11 @@ size_t mla_query_project_workspace_size(const mla_dims* dims, int32_t B, int32_t
 // counters: the split-K tile counters of the two products (SPLITK_COUNTER_BYTES
 // of zeros); the public entry point passes the block at offset 0 of its
 // workspace, the whole layer a block at a fixed offset of its own.
+// first_only (low-rank, bf16, packed c^Q): only c^Q and q^R are formed; c^Q
+// stays packed in the workspace for the fused absorption.
 static mla_status query_project_impl(const mla_dims* dims, int32_t B, int32_t d_cq, const void* h, const void* W_DQ,
                                      const void* W_UQ, const void* W_QR, void* q_C, void* q_R, void* workspace,
-                                     size_t ws_bytes, void* stream, char* counters) {
+                                     size_t ws_bytes, void* stream, char* counters, bool first_only = false) {
   mla_status st = check_query_dims(dims, B, d_cq);
   if (st != MLA_OK) return st;
   if (!h || !W_UQ || !W_QR || !q_C || !q_R || !workspace)
@@ -442,7 +456,7 @@ static mla_status query_project_impl(const mla_dims* dims, int32_t B, int32_t d_
   g.S = p.S1;
   g.part = (float*)(ws + p.off_part);
   if (e == hipSuccess) e = mla::launch_gemm(g, o, f32, f32, f32, s);
-  if (e == hipSuccess && p.lowrank) {
+  if (e == hipSuccess && p.lowrank && !first_only) {
     mla::GemmArgs g2 = gemm_args(c_Q, d_cq, B, d_cq, counters ? counters : ws);
     mla::GemmOut o2{};
     gemm_segments(g2, o2, {{W_UQ, nq, q_C, nq}});
@@ -648,15 +662,23 @@ mla_status mla_decode_layer(const mla_dims* dims, int32_t B, int32_t d_cq, const
   // the projections' split-K counters sit at fixed offsets of the step's
   // layout (the rest of the workspace moves with B)
   const mla::DecodeWs D = mla::decode_ws_layout(B, dims->n_h, n_splits, (int)elt_size(dims), true);
+  // bf16 with a low-rank query: q^C = W^UQ c^Q is formed inside the
+  // absorption launch from the packed c^Q the first product leaves in the
+  // query workspace, so the W^UQ product has no launch of its own
+  const QueryPlan qp = query_plan(*dims, B, d_cq);
+  const bool fuse = d_cq > 0 && qp.packed && mla::step_prep_supported(*dims, B) &&
+                    mla::absorb_fused_supported(*dims, B, d_cq);
+  const FusedQuery fq{ws + L.q + qp.off_cq, W_UQ, d_cq};
   st = query_project_impl(dims, B, d_cq, h, W_DQ, W_UQ, W_QR, ws + L.qc, ws + L.qr, ws + L.q, L.qc - L.q, stream,
-                          ws + D.q_cnt);
+                          ws + D.q_cnt, fuse);
   // the step's combine also leaves o packed (bf16) where the output
   // projection reads it, which saves that projection's pack launch
   const OutputPlan op = output_plan(*dims, B);
   const StepAppendIn in{h, W_DKV, W_KR, op.packed ? ws + L.out + op.off_o : nullptr};
   if (st == MLA_OK)
     st = decode_impl(dims, B, ws + L.qc, ws + L.qr, pos_q, W_UK, W_UV, c_KV, k_R, row_stride, num_pages, page_table,
-                     max_pages, seq_lens, (float*)(ws + L.o), lse, workspace, L.q, n_splits, opts, &in, stream);
+                     max_pages, seq_lens, (float*)(ws + L.o), lse, workspace, L.q, n_splits, opts, &in, stream, false,
+                     nullptr, fuse ? &fq : nullptr);
   if (st == MLA_OK)
     st = output_project_impl(dims, B, (const float*)(ws + L.o), W_O, u, ws + L.out, L.total - L.out, stream,
                              op.packed, ws + D.o_cnt);

@@ -302,15 +302,25 @@ hipError_t launch_prefill_queries(int32_t T, const int32_t* seq_id, const int32_
 // launch_plan is not called).
 hipError_t launch_absorb(const mla_dims& d, int32_t B, const void* q_C, const void* q_R, const int32_t* pos_q,
                          const void* W_UK, void* qabs, const PlanArgs& pa, hipStream_t s);
+// The decode layer's q^C = W^UQ c^Q and its absorption in one launch (bf16;
+// c^Q and W^UQ in the packed layout of the projection kernels, c^Q with its
+// rows padded to a multiple of 64).  The plan is not run here.
+inline bool absorb_fused_supported(const mla_dims& d, int32_t B, int32_t d_cq) {
+  return d.dtype == MLA_BF16 && B >= 1 && d_cq >= 32 && d_cq % 32 == 0;
+}
+hipError_t launch_absorb_fused(const mla_dims& d, int32_t B, int32_t d_cq, const void* cQ_packed,
+                               const void* W_UQ_packed, const void* q_R, const int32_t* pos_q, const void* W_UK,
+                               void* qabs, hipStream_t s);
 // Decode step, first launch: the split-K append of each sequence's newest
 // token (finished in the same launch), the query absorption and the plan, as
 // one grid (bf16, d_model a multiple of 1024; step_prep_supported()).
 struct AppendDst;
 bool step_prep_supported(const mla_dims& d, int32_t B);
+// absorb = false: append and plan only (the absorption runs elsewhere).
 hipError_t launch_step_prep(const mla_dims& d, int32_t B, const void* h_new, const void* W_DKV, const void* W_KR,
                             const void* q_C, const void* q_R, const int32_t* pos_q, const void* W_UK, void* qabs,
                             const PlanArgs& pa, float* app_part, int32_t* app_cnt, const AppendDst& dst,
-                            hipStream_t s);
+                            hipStream_t s, bool absorb = true);
 hipError_t launch_decode_simple(const mla_dims& d, int32_t B, const void* qabs, const void* c_KV,
                                 const void* k_R, int64_t row_stride, int32_t num_pages,
                                 const int32_t* page_table, int32_t max_pages, const int32_t* prefix,

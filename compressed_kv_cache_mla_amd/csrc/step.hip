@@ -10,6 +10,9 @@
 // None of the three reads what another writes, so one launch replaces three
 // (append, append finish, absorb + plan) and their latency chains overlap.
 // The attention kernel reads the new rows after this launch has completed.
+// In the decode layer with a low-rank bf16 query the absorption is left out
+// of this launch (absorb = false): absorb_fused_kernel (absorb.hip) forms
+// q^C = W^UQ c^Q and absorbs it in a launch of its own.
 #include "absorb_mfma.h"
 #include "append_splitk.h"
 
@@ -78,7 +81,7 @@ bool step_prep_supported(const mla_dims& d, int32_t B) {
 hipError_t launch_step_prep(const mla_dims& d, int32_t B, const void* h_new, const void* W_DKV, const void* W_KR,
                             const void* q_C, const void* q_R, const int32_t* pos_q, const void* W_UK, void* qabs,
                             const PlanArgs& pa, float* app_part, int32_t* app_cnt, const AppendDst& dst,
-                            hipStream_t s) {
+                            hipStream_t s, bool absorb) {
   StepPrepArgs a;
   a.pa = pa;
   a.h_new = (const bf16*)h_new;
@@ -98,7 +101,7 @@ hipError_t launch_step_prep(const mla_dims& d, int32_t B, const void* h_new, con
   a.qscale = d.softmax_scale * LOG2E;
   a.B = B;
   a.n_h = d.n_h;
-  const int64_t n_abs = (int64_t)4 * d.n_h * ((B + 63) / 64);
+  const int64_t n_abs = absorb ? (int64_t)4 * d.n_h * ((B + 63) / 64) : 0;
   const int64_t grid = 1 + (int64_t)a.n_app + n_abs;
   // Above 32 sequences each workgroup also requests 12 KB of LDS that it
   // does not use, so that at most three share a CU (4 x 44 KB exceeds the

@@ -374,7 +374,13 @@ mla_status mla_prefill(const mla_dims* dims, int32_t T, const void* h, const voi
  * (mla_query_project), the decode step (mla_decode_step: append of the token's
  * latent row, absorption, attention over the cache, combine + W^UV) and the
  * output projection (mla_output_project), on the same stream and with the
- * same results as those three calls.
+ * same results as those three calls, except in one case.  With bf16, a
+ * low-rank query (d_cq > 0), more than 8 sequences and d_model a multiple of
+ * 1024, q^C = W^UQ c^Q is formed inside the absorption launch and never stored
+ * ("DeepSeek-V2：在“大力出奇迹”的AI军备竞赛中，四两拨千斤" (liang.world), ch.2 §2:
+ * the query's low-rank compression c^Q, absorbed with W^UK).  Its fp32 sums
+ * then run in another order before the bf16 rounding of q^C, so u and lse
+ * agree with the three calls to within that rounding, not bit for bit.
  *   h            [B, d_model]     dtype   device  state of each sequence's new token
  *   W_DKV, W_KR  row-major, as for mla_cache_append
  *   W_DQ, W_UQ, W_QR   packed, as for mla_query_project (W_DQ NULL iff d_cq == 0)

@@ -1,11 +1,16 @@
 """GPU parity of the whole decode layer (mla_decode_layer): query projection,
 decode step and output projection from the new tokens' states h to u.
 
-Checked two ways: bit for bit against the three entry points called one after
-the other (mla_query_project, mla_decode_step, mla_output_project), and
-against the fp64 oracle chained the same way -- oracle.query_project_lowrank,
-the absorbed attention over the oracle's own cache rows, oracle.output_project
--- on sampled sequences, within the bf16 bound.
+Checked two ways: against the three entry points called one after the other
+(mla_query_project, mla_decode_step, mla_output_project), and against the
+fp64 oracle chained the same way -- oracle.query_project_lowrank, the absorbed
+attention over the oracle's own cache rows, oracle.output_project -- on
+sampled sequences, within the bf16 bound, with the cache rows the layer
+appended held to the oracle's down-projection.  Against the parts the layer is
+bit for bit the same except where it forms q^C = W^UQ c^Q inside the
+absorption launch (bf16, a low-rank query, more than 8 sequences): there
+q^C's fp32 sums run in another order before their bf16 rounding, and u is held
+to the parts within a bound far below the oracle's.
 """
 import numpy as np
 import pytest
@@ -14,7 +19,7 @@ import torch
 import oracle
 import seeded_inputs as si
 import workloads as W
-from cases import oracle_cache, rel_err
+from cases import gpu_cache_rows, oracle_cache, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +38,10 @@ def _proj_weights(seed, n_h, d_model, d_cq, device, dtype=torch.bfloat16):
 @pytest.mark.parametrize("B,d_model,d_cq,lens,dtype", [(5, 1024, 512, (40, 700), torch.bfloat16),
                                                     (40, 1024, 0, (20, 300), torch.bfloat16),
                                                     (1, 1024, 256, (1, 90), torch.bfloat16),
-                                                    (3, 1024, 256, (10, 200), torch.float32)])
+                                                    (3, 1024, 256, (10, 200), torch.float32),
+                                                    (20, 1024, 512, (30, 400), torch.bfloat16),
+                                                    (64, 1024, 256, (20, 300), torch.bfloat16),
+                                                    (70, 2048, 384, (10, 200), torch.bfloat16)])
 def test_decode_layer_equals_its_parts_and_the_oracle(B, d_model, d_cq, lens, dtype):
     import compressed_kv_cache_mla_amd as mla
     n_h_cfg = 16 if dtype == torch.float32 else 128
@@ -54,6 +62,9 @@ def test_decode_layer_equals_its_parts_and_the_oracle(B, d_model, d_cq, lens, dt
                          ws, n_splits=37)
         torch.cuda.synchronize()
         assert mla.read_error_flags(ws) == 0
+    sampled = sorted({0, B - 1, B // 2})
+    # the rows the layer appended (the parts below write them again)
+    new_rows = {b: gpu_cache_rows(wl, b, [int(wl.prefix[b + 1] - wl.prefix[b]) - 1])[0] for b in sampled}
     # the three parts, one after the other, on workspaces of their own
     q_C = torch.empty((B, n_h, 128), dtype=dtype, device="cuda")
     q_R = torch.empty((B, n_h, 64), dtype=dtype, device="cuda")
@@ -67,13 +78,20 @@ def test_decode_layer_equals_its_parts_and_the_oracle(B, d_model, d_cq, lens, dt
     u2 = torch.empty_like(u)
     mla.output_project(dims, out, Pp["W_O"], u2, mla.output_project_workspace(dims, B))
     torch.cuda.synchronize()
-    assert torch.equal(u, u2) and torch.equal(lse, lse2)
+    fused = dtype == torch.bfloat16 and d_cq > 0 and B > 8
+    if fused:
+        assert rel_err(u.double().cpu().numpy(), u2.double().cpu().numpy()) <= 2e-3
+        assert float((lse - lse2).abs().max()) <= 1e-3 * max(1.0, float(lse2.abs().max()))
+    else:
+        assert torch.equal(u, u2) and torch.equal(lse, lse2)
     # the oracle, chained
     f = {k: (None if v is None else v.double().cpu().numpy()) for k, v in P.items()}
     got = u.double().cpu().numpy()
-    for b in sorted({0, B - 1, B // 2}):
+    for b in sampled:
         d = wl.oracle_inputs(b)
         c, kR = oracle_cache(wl, d)
+        e_row = rel_err(new_rows[b], np.concatenate([c[-1], kR[-1]]))
+        assert e_row <= (1e-2 if dtype == torch.bfloat16 else 1e-5), f"sequence {b}: appended row rel err {e_row:.3e}"
         h_b = d["h"][d["n"] - 1]
         if d_cq:
             qc, qr = oracle.query_project_lowrank(h_b, f["W_DQ"], f["W_UQ"], f["W_QR"], n_h)
