@@ -30,8 +30,12 @@
 //    and the number r of ties at T to keep are known.  A count pass (several
 //    chunks only) and a write pass then list, in token order, every token
 //    with key > T and the first r tokens with key == T, with their pool rows
-//    (page-table lookups) for the gather attention.  Integer work only: the
-//    result is exact and deterministic.
+//    (page-table lookups) for the gather attention.  When every sequence fits
+//    one chunk, select_local_kernel does passes 1 and 2, the picks and the
+//    listing in one launch, a workgroup per sequence with its scores in LDS.
+//    Integer work only: the result is exact and deterministic.
+#include <type_traits>
+
 #include "mla_common.h"
 
 namespace mla {
@@ -617,6 +621,100 @@ __global__ void __launch_bounds__(SEL_NT) select_write_kernel(const float* __res
   }
 }
 
+// Every sequence within one SEL_CH chunk: the radix passes after the
+// indexer's, the final threshold and the listing, in one workgroup per
+// sequence with the sequence's scores held in LDS (instead of
+// select_hist_kernel<1>, <2> and select_write_kernel, three launches).  The
+// pass-0 digit is picked from the indexer's histogram; passes 1 and 2
+// histogram the keys that match the bits fixed so far (LDS atomics) and pick
+// their digit; then each thread takes a contiguous run of tokens, and two
+// block scans of its counts above T and at T give, for every token in order,
+// its position in the list: the tokens above T before it plus the ties at T
+// before it, at most r of them.  The same list as the three-launch path.
+__global__ void __launch_bounds__(SEL_NT) select_local_kernel(const float* __restrict__ scores, int32_t max_tokens,
+                                                           const int32_t* __restrict__ seq_lens, int32_t top_k,
+                                                           const int32_t* __restrict__ hist, int32_t B,
+                                                           int32_t* __restrict__ st,
+                                                           const int32_t* __restrict__ page_table, int32_t max_pages,
+                                                           int32_t page_size, int32_t num_pages,
+                                                           int32_t* __restrict__ sel_tok, int32_t* __restrict__ sel_row,
+                                                           int32_t* __restrict__ flags) {
+  __shared__ __attribute__((aligned(16))) float sc[SEL_CH];
+  __shared__ int32_t h[SEL_BINS];
+  __shared__ int32_t part[SEL_NT];
+  __shared__ int32_t wsum[2][SEL_NT / 64];
+  __shared__ int32_t st_l[4];
+  const int32_t b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t n = clamp_len(seq_lens[b], max_tokens);
+  const bool all = n <= top_k;
+  if (!all) {
+    const float* sb = scores + (int64_t)b * max_tokens;
+    for (int32_t t = 4 * tid; t < n; t += 4 * SEL_NT) {
+      const float4 v = *(const float4*)(sb + t);
+      const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (t + e < n) sc[t + e] = x[e];
+    }
+    if (tid < 3) st_l[tid] = 0;
+    __syncthreads();
+    pick_digit<0, SEL_NT>(hist + (int64_t)b * SEL_BINS, true, st_l, top_k, part);
+    __syncthreads();
+    auto pass = [&](auto P) __attribute__((always_inline)) {
+      using D = Digit<decltype(P)::value>;
+      for (int i = tid; i < SEL_BINS; i += SEL_NT) h[i] = 0;
+      __syncthreads();
+      const uint32_t fixed = (uint32_t)st_l[0];
+      for (int32_t t = tid; t < n; t += SEL_NT) {
+        const uint32_t key = score_key(sc[t]);
+        if ((key & D::HIMASK) == fixed) atomicAdd(&h[(key >> D::SHIFT) & D::BMASK], 1);
+      }
+      __syncthreads();
+      pick_digit<decltype(P)::value, SEL_NT>(h, false, st_l, top_k, part);
+      __syncthreads();
+    };
+    pass(std::integral_constant<int, 1>{});
+    pass(std::integral_constant<int, 2>{});
+  }
+  const uint32_t T = all ? 0u : (uint32_t)st_l[0];
+  const int32_t rem = all ? 0 : st_l[1];
+  if (tid < 3) st[(2 * B + b) * 4 + tid] = all ? (tid == 2 ? 1 : 0) : (tid == 2 ? 0 : (int32_t)(tid ? rem : T));
+  const int32_t per = (n + SEL_NT - 1) / SEL_NT;
+  const int32_t t0 = min(n, tid * per), t1 = min(n, t0 + per);
+  int32_t g = 0, e = 0;
+  for (int32_t t = t0; t < t1; ++t) {
+    const uint32_t key = all ? 0u : score_key(sc[t]);
+    g += all || key > T;
+    e += !all && key == T;
+  }
+  int32_t tot;
+  int32_t er = block_excl_sum(e, wsum[0], tot);
+  int32_t gr = block_excl_sum(g, wsum[1], tot);
+  const int32_t* pt = page_table + (int64_t)b * max_pages;
+  for (int32_t t = t0; t < t1; ++t) {
+    const uint32_t key = all ? 0u : score_key(sc[t]);
+    int32_t pos = -1;
+    if (all || key > T) {
+      pos = gr + min(er, rem);
+      ++gr;
+    } else if (key == T) {
+      if (er < rem) pos = gr + er;
+      ++er;
+    }
+    if (pos >= 0 && pos < top_k) {   // always below top_k when the passes agree; guards the writes
+      const int32_t p = t / page_size;
+      int32_t pg = pt[p];
+      if (pg < 0 || pg >= num_pages) {
+        atomicOr(flags, MLA_FLAG_BAD_PAGE);
+        pg = pg < 0 ? 0 : num_pages - 1;
+      }
+      sel_tok[(int64_t)b * top_k + pos] = t;
+      sel_row[(int64_t)b * top_k + pos] = pg * page_size + (t - p * page_size);
+    }
+  }
+}
+
 }  // namespace
 
 SelectWs select_ws_layout(int32_t B, int32_t max_tokens, int32_t top_k, bool outputs) {
@@ -662,7 +760,12 @@ hipError_t launch_indexer_select(int32_t B, int32_t H_I, const void* q_I, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 gs(L.nchunks, B);
-  const bool local = L.nchunks == 1;   // one workgroup per sequence picks its own digits
+  if (L.nchunks == 1) {   // one workgroup per sequence does the whole selection
+    select_local_kernel<<<B, SEL_NT, 0, s>>>(scores, max_tokens, seq_lens, top_k, hist, B, st, page_table, max_pages,
+                                             page_size, num_pages, sel_tok, sel_row, flags);
+    return hipGetLastError();
+  }
+  const bool local = false;
   select_hist_kernel<1><<<gs, SEL_NT, 0, s>>>(scores, max_tokens, seq_lens, top_k, hist, B, st, local);
   select_hist_kernel<2><<<gs, SEL_NT, 0, s>>>(scores, max_tokens, seq_lens, top_k, hist, B, st, local);
   if (!local)

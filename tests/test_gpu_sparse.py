@@ -97,6 +97,19 @@ def test_select_massive_ties():
         assert np.array_equal(sel_tok[b, :min(n, 1000)], oracle.topk_select(ref, 1000))
 
 
+@pytest.mark.parametrize("lens,B,top_k,exact", [((20000, 60000), 3, 3000, True),
+                                                 ((262200, 300000), 2, 2048, False)])
+def test_select_long_sequences(lens, B, top_k, exact):
+    """Sequences past one selection chunk: each radix pass spread over the
+    chunks of a sequence, with the count pass placing each chunk's kept
+    tokens (the shorter workloads select in one workgroup per sequence)."""
+    cfg = W.scaled(W.CONFIGS["b64_ragged"], name=f"sp_long_{lens[0]}", B=B, lens=lens, cache_mode="direct",
+                   seed=4104 + B)
+    wl = W.Workload(cfg)
+    idx = W.IndexerInputs(wl, H_I=64, exact=exact)
+    _check_selection(wl, idx, top_k, exact=exact)
+
+
 def _sparse(wl, idx, top_k, n_splits=0):
     B = wl.cfg.B
     sel = torch.full((B, top_k), -1, dtype=torch.int32, device=wl.device)
