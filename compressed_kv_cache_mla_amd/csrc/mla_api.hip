@@ -238,6 +238,8 @@ static mla_status decode_impl(const mla_dims* dims, int32_t B, const void* q_C, 
   pa.max_pages = max_pages;
   pa.page_size = dims->page_size;
   if (opts && opts->impl != 0 && opts->impl != 1) return fail(MLA_ERR_INVALID_ARG, "opts->impl=%d", opts->impl);
+  if (fq && !(step && mla::step_prep_supported(*dims, B) && mla::absorb_fused_supported(*dims, B, fq->d_cq)))
+    return fail(MLA_ERR_UNSUPPORTED, "the fused query absorption needs the one-launch step (bf16, d_model %% 1024 == 0)");
   hipError_t e = hipSuccess;
   if (step && mla::step_prep_supported(*dims, B)) {
     // append (split-K, finished in the same launch), absorption and plan in one launch
