@@ -126,7 +126,10 @@ __global__ void __launch_bounds__(256) absorb_fused_kernel(int32_t B, int32_t n_
   __shared__ __attribute__((aligned(16))) bf16 qcl[32 * D_H];   // q^C of the 32 sequences, [b][d]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.x;
+  // heads h and h^1 (which share the 128-byte lines of the q~ layout) are 8
+  // workgroups apart, on one XCD
+  const int h = (n_h & 15) ? (int)blockIdx.x
+                           : (int)((blockIdx.x & ~15u) | ((blockIdx.x & 7) << 1) | ((blockIdx.x >> 3) & 1));
   const int b0 = blockIdx.y * 32;
   const int nb = min(32, B - b0);
   // 1. W^UK_h -> LDS: 128 copy instructions of 1 KB, 32 per quarter
@@ -217,19 +220,9 @@ __global__ void __launch_bounds__(256) absorb_fused_kernel(int32_t B, int32_t n_
       }
       a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], a, 0, 0, 0);
     }
-    // lane -> sequence (lane & 31), latent rows (r/4)*8 + 4*(lane>>5) + r%4 of the wave's 32 columns
     const int bb = lane & 31;
-    if (bb < nb) {
-      bf16* qb = qabs + (int64_t)(b0 + bb) * n_h * D_K;
-      const int d0 = 128 * cq + 32 * wave + 4 * (lane >> 5);
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (bf16)(a[4 * r4 + i] * qscale);
-        *(bf16x4*)(qb + qabs_offset(n_h, true, h, d0 + 8 * r4)) = o;
-      }
-    }
+    store_qabs_block(a, qscale, bb < nb ? qabs + (int64_t)(b0 + bb) * n_h * D_K : nullptr, n_h, h,
+                     128 * cq + 32 * wave, lane);
   }
   // RoPE half: 32 sequences x 32 pairs
 #pragma unroll

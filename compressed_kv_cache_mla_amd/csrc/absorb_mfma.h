@@ -23,6 +23,51 @@ namespace mla {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
+// Stores one wave's 32-column x 32-sequence block of q~, scaled and rounded
+// to bf16.  The accumulator is in the C layout of v_mfma_f32_32x32x16_bf16
+// (lane -> sequence lane & 31, latent rows (r/4)*8 + 4*(lane>>5) + r%4), so
+// each lane holds four runs of 4 rows.  v_permlane32_swap trades row runs
+// between the half-waves until half k holds rows 16p + 8k .. 16p + 8k + 7 for
+// p = 0, 1; one 16-byte store per p then gives each sequence 32 contiguous
+// bytes of its 64-byte run of the q~ layout per store instruction, where
+// 8-byte stores gave 16.  Every lane of the wave takes part in the swaps;
+// qb is null for lanes whose sequence is past the batch.
+__device__ __forceinline__ void store_qabs_block(const f32x16& acc, float qscale, bf16* qb, int32_t n_h, int h,
+                                                 int dbase, int lane) {
+  unsigned int w[8];
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      bf16x2 v;
+      v[0] = (bf16)(acc[4 * r4 + 2 * i] * qscale);
+      v[1] = (bf16)(acc[4 * r4 + 2 * i + 1] * qscale);
+      w[2 * r4 + i] = __builtin_bit_cast(unsigned int, v);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      // lanes 32..63 of the first operand trade with lanes 0..31 of the second
+      const auto x = __builtin_amdgcn_permlane32_swap(w[4 * p + i], w[4 * p + 2 + i], false, false);
+      w[4 * p + i] = x[0];
+      w[4 * p + 2 + i] = x[1];
+    }
+  }
+  if (qb != nullptr) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      u32x4 o;
+      o[0] = w[4 * p];
+      o[1] = w[4 * p + 1];
+      o[2] = w[4 * p + 2];
+      o[3] = w[4 * p + 3];
+      *(u32x4*)(qb + qabs_offset(n_h, true, h, dbase + 16 * p + 8 * (lane >> 5))) = o;
+    }
+  }
+}
+
 __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32_t B, int32_t n_h,
                                                   const bf16* __restrict__ q_C, const bf16* __restrict__ q_R,
                                                   const int32_t* __restrict__ pos_q, const bf16* __restrict__ W_UK,
@@ -30,7 +75,14 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32
                                                   char* wl) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = bx >> 2, cq = bx & 3;
+  // bx -> (head, quarter): quarter = bits 0-1, head bit 1 = bit 2, head bit 0
+  // = bit 3, head >> 2 = bits 4 and up.  Heads h and h^1 share the 128-byte
+  // lines of the q~ layout; with this order their workgroups for one quarter
+  // are 8 apart in the grid, so on the same XCD (workgroups are dealt to the
+  // 8 XCDs in turn) and their halves of each line meet in one L2.
+  int h = bx >> 2;
+  const int cq = bx & 3;
+  if ((n_h & 3) == 0) h = ((bx >> 4) << 2) | (((bx >> 2) & 1) << 1) | ((bx >> 3) & 1);
   // W^UK_h[:, 128cq .. 128cq+127] -> LDS (2048 chunks of 16 B; 8 copy instructions per wave)
   const char* wsrc = (const char*)(W_UK + (int64_t)h * D_H * D_C) + 256 * cq;
 #pragma unroll
@@ -81,20 +133,8 @@ __device__ __forceinline__ void absorb_mfma_block(int bx, int by, int nby, int32
   // C layout: lane -> sequence (lane & 31) of the block, latent rows (r/4)*8 + 4*(lane>>5) + r%4
   auto store_block = [&](const f32x16& acc, int b0, int nb, int nblk) {
     const int bb = 32 * nblk + (lane & 31);
-    if (bb < nb) {
-      // 4 consecutive latent dims (a multiple of 4 first) stay consecutive in the q~ layout
-      bf16* qb = qabs + (int64_t)(b0 + bb) * n_h * D_K;
-      const int d0 = 128 * cq + 32 * wave + 4 * (lane >> 5);
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 o;
-        o[0] = (bf16)(acc[4 * r4 + 0] * qscale);
-        o[1] = (bf16)(acc[4 * r4 + 1] * qscale);
-        o[2] = (bf16)(acc[4 * r4 + 2] * qscale);
-        o[3] = (bf16)(acc[4 * r4 + 3] * qscale);
-        *(bf16x4*)(qb + qabs_offset(n_h, true, h, d0 + 8 * r4)) = o;
-      }
-    }
+    store_qabs_block(acc, qscale, bb < nb ? qabs + (int64_t)(b0 + bb) * n_h * D_K : nullptr, n_h, h,
+                     128 * cq + 32 * wave, lane);
   };
   // RoPE half (32 pairs per sequence), shared by the 4 column-quarter
   // workgroups of the head (pairs 512q .. 512q+511 of a 64-sequence block,
