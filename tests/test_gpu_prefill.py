@@ -169,11 +169,14 @@ def test_prefill_deepseek_sizes_sampled():
     c.check()
 
 
-def test_prefill_long_chunk_shares_the_absorption_weights():
-    """512 new tokens after a 300-token prior (n_h = 128): the absorption then
-    lets each W^UK block serve several 64-token blocks; every token checked."""
-    _say("case prefill 512-token chunk")
-    c = Chunk(81, 128, 1024, torch.bfloat16, [300], [512], 64)
+@pytest.mark.parametrize("prior,chunk", [([300], [512]), ([300, 20], [400, 50])])
+def test_prefill_long_chunk_shares_the_absorption_weights(prior, chunk):
+    """512 (or 450, in two sequences) new tokens after a short prior (n_h =
+    128): the absorption then lets each W^UK block serve several 64-token
+    blocks, and the combine merges 64 queries per workgroup (450: a last
+    block of 2); every token checked."""
+    _say(f"case prefill long chunk {prior} {chunk}")
+    c = Chunk(81, 128, 1024, torch.bfloat16, prior, chunk, 64)
     c.run()
     assert c.mla.read_error_flags(c.ws) == 0
     c.check()
