@@ -262,6 +262,101 @@ __global__ void __launch_bounds__(256) append_splitk_kernel(int32_t T_rows, int3
   append_splitk_block<false, MT>(blockIdx.x, blockIdx.y, blockIdx.z, T_rows, d_model, h, W_DKV, W_KR, part, red);
 }
 
+// Wide form of the chunk sums for long row batches (T >= APPEND_WIDE_MIN_T,
+// prefill chunks): workgroup (64 output columns, chunk kc, 64 rows), 4 waves
+// over quarters of the chunk.  Per K-step a wave loads 4 activation and 4
+// weight fragments and runs 16 MFMAs, so each activation fragment serves 4
+// column tiles where append_splitk_kernel's 16-column workgroups load it once
+// per tile (activation traffic / 4).  Each wave's sums are those of
+// append_splitk_block (same fragments, same K-steps in the same order, A =
+// activations, B = weights), and the waves are added as (w0 + w1) + (w2 +
+// w3), so the chunk sums and the rows append_finish_kernel stores from them
+// are bitwise those of the 16-column form, and of the decode step's append.
+__global__ void __launch_bounds__(256) append_wide_kernel(int32_t T_rows, int32_t d_model, const bf16* __restrict__ h,
+                                                          const bf16* __restrict__ W_DKV,
+                                                          const bf16* __restrict__ W_KR, float* __restrict__ part) {
+  constexpr int MT = 4, NT = AW_NT, ROWS = 16 * MT, COLS = 16 * NT, LD = COLS + 1, KB = 2;
+  __shared__ float red[2][ROWS * LD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n0 = blockIdx.x * COLS, kc = blockIdx.y, m0 = blockIdx.z * ROWS;
+  const int K = d_model, kchunk = K / SK_SPLIT, kw = kchunk / 4, nks = kw / 32;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int64_t kbase = (int64_t)kc * kchunk + wave * kw;   // this wave's first k
+  // columns n0 .. n0+63 lie in one weight (D_C is a multiple of 64)
+  const bf16* W = n0 < D_C ? W_DKV + (int64_t)n0 * K : W_KR + (int64_t)(n0 - D_C) * K;
+  const bf16* wp = W + (int64_t)r16 * K + kbase + kq;   // tile c at + 16 c K
+  const bf16* xp[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)   // rows past T repeat row T-1
+    xp[t] = h + (int64_t)min(m0 + 16 * t + r16, T_rows - 1) * d_model + kbase + kq;
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int c = 0; c < NT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b0 = 0; b0 < nks; b0 += KB) {
+    bf16x8 wv[NT][KB], xv[MT][KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+      if (b0 + i < nks) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) wv[c][i] = *(const bf16x8*)(wp + (int64_t)16 * c * K + 32 * (b0 + i));
+#pragma unroll
+        for (int t = 0; t < MT; ++t) xv[t][i] = *(const bf16x8*)(xp[t] + 32 * (b0 + i));
+      }
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+      if (b0 + i < nks) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int c = 0; c < NT; ++c)
+            acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[t][i], wv[c][i], acc[t][c], 0, 0, 0);
+      }
+  }
+  // C layout: lane holds column 16c + lane%16, rows 16t + 4*(lane/16) + i
+  auto slot = [&](int buf, int t, int c, int i) -> float& {
+    return red[buf][(16 * t + 4 * (lane >> 4) + i) * LD + 16 * c + r16];
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) slot(buf, t, c, i) = acc[t][c][i];
+  };
+  auto add = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][c][i] = acc[t][c][i] + slot(buf, t, c, i);
+  };
+  if (wave == 1) put(0);
+  if (wave == 3) put(1);
+  __syncthreads();
+  if (wave == 0) add(0);   // w0 + w1
+  if (wave == 2) add(1);   // w2 + w3
+  __syncthreads();
+  if (wave == 2) put(1);
+  __syncthreads();
+  if (wave == 0) {
+    add(1);                // (w0 + w1) + (w2 + w3)
+    put(0);
+  }
+  __syncthreads();
+  // part[kc][m][576]: 64 columns of 4 rows per pass
+  const int col = tid & 63;
+#pragma unroll
+  for (int j = 0; j < ROWS / 4; ++j) {
+    const int r = 4 * j + (tid >> 6);
+    const int m = m0 + r;
+    if (m < T_rows) part[((int64_t)kc * T_rows + m) * D_K + n0 + col] = red[0][r * LD + col];
+  }
+}
+
 __global__ void __launch_bounds__(256) append_finish_kernel(int32_t T_rows, int32_t d_model,
                                                             const float* __restrict__ part, AppendDst a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -284,7 +379,10 @@ hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void
   if (ws && need > 0 && ws_bytes >= need) {
     const int rows = 16 * append_mt(T);
     dim3 g1(D_K / 16, SK_SPLIT, (T + rows - 1) / rows);
-    if (append_mt(T) == 4)
+    if (T >= APPEND_WIDE_MIN_T)
+      append_wide_kernel<<<dim3(D_K / (16 * AW_NT), SK_SPLIT, (T + 63) / 64), 256, 0, s>>>(
+          T, d.d_model, (const bf16*)h, (const bf16*)W_DKV, (const bf16*)W_KR, (float*)ws);
+    else if (append_mt(T) == 4)
       append_splitk_kernel<4><<<g1, 256, 0, s>>>(T, d.d_model, (const bf16*)h, (const bf16*)W_DKV,
                                                 (const bf16*)W_KR, (float*)ws);
     else

@@ -26,6 +26,11 @@ constexpr int SK_RED_FLOATS = GK_RED_FLOATS;
 // Token rows per workgroup: 32 (MT = 2) up to 32 tokens, 64 (MT = 4) above,
 // so that a 33..64-token batch reads the weights once.
 inline int append_mt(int32_t T) { return T > 32 ? 4 : 2; }
+// From this many rows the two-launch append computes its chunk sums in 64 x 64
+// tiles (append_wide_kernel, append.hip), 16-column tiles below.
+constexpr int APPEND_WIDE_MIN_T = 256;
+constexpr int AW_NT = 4;   // 16-column tiles per workgroup of the wide form
+static_assert(D_C % (16 * AW_NT) == 0 && D_K % (16 * AW_NT) == 0, "wide append tiles");
 // K-steps per load batch for MT row tiles (the 64-row form keeps its loads
 // within the fused step's register budget).
 __host__ __device__ constexpr int append_kb(int MT) { return MT == 4 ? 2 : GK_KB; }

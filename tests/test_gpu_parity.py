@@ -206,7 +206,7 @@ def test_bf16_rising_scores_rescale_vs_oracle(n_h):
     _check_decode_modes(wl, [cfg.B - 1], [("reconstruct", [0, n_h - 1])])
 
 
-@pytest.mark.parametrize("d_model,B", [(1024, 7), (1024, 20), (1024, 40), (512, 7)])
+@pytest.mark.parametrize("d_model,B", [(1024, 7), (1024, 20), (1024, 40), (512, 7), (1024, 300)])
 def test_decode_step_equals_append_then_decode(d_model, B):
     # mla_decode_step (one launch for append + absorption + plan when d_model is
     # a multiple of 1024, separate launches otherwise) against the same inputs
