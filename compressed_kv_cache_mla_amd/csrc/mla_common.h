@@ -285,7 +285,8 @@ namespace mla {
 // no workspace path for these sizes) a batch of up to APPEND_WS_MAX_T rows
 // (bf16) runs split over d_model in two launches; otherwise one kernel does
 // it.  The split path measured faster from 128 to 1024 rows (33 against 53 us
-// at 512, 61 against 109 us at 1024 on DeepSeek-V2 sizes).
+// at 512, 61 against 109 us at 1024 on DeepSeek-V2 sizes, with 16-column
+// chunk-sum tiles; the 64 x 64 tiles used from 256 rows bring 512 rows to 25).
 constexpr int APPEND_WS_MAX_T = 1024;
 size_t append_workspace_bytes(const mla_dims& d, int32_t T);
 hipError_t launch_append(const mla_dims& d, int32_t T, const void* h, const void* W_DKV, const void* W_KR,
